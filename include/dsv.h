@@ -1,0 +1,151 @@
+/*
+ * dsv.h — C ABI of the DSV dynamic-sparsity attention hot path on MI355X (gfx950).
+ *
+ * The operations follow the technical summaries of
+ *   "DSV: Exploiting Dynamic Sparsity to Accelerate Large-Scale Video DiT Training"
+ *   (gist.science/{zh,pt,fr,ko}/paper/2502.07590):
+ *   - zh §2.1 "Two-Stage Training Algorithm" / pt §2A / fr §2A / ko §2가: per-head low-rank
+ *     factors approximate QK^T and are used to estimate the critical KV pairs; full attention
+ *     is then computed on the critical pairs only.
+ *   - zh §2.2 "Efficient Kernels" / pt §2B / fr §2B / ko §2나: the low-rank MatMul and the
+ *     top-k are fused so the S x S score matrix is never stored (memory O(S^2) -> O(S*k));
+ *     spatio-temporally adjacent queries are grouped and share one list of critical KV indices.
+ *
+ * Conventions shared by every entry point
+ *   Token grid: a sample is a latent video of T x Hh x W tokens, flattened row-major,
+ *     token n = (t*Hh + y)*W + x, S = T*Hh*W.
+ *   Query groups: gt x gh x gw blocks of adjacent tokens (gt | T, gh | Hh, gw | W).
+ *     G = gt*gh*gw queries per group, NG = S/G groups per (batch, head). Group index
+ *     g = (a*(Hh/gh) + b)*(W/gw) + c for block (a,b,c); its members are enumerated
+ *     row-major over (dt,dy,dx). Groups never cross samples.
+ *   Tensors Q, K, V, O, dO, dQ, dK, dV: [B][H][S][d] contiguous. LSE: [B][H][S] fp32.
+ *     Q_lr, K_lr: [B][H][S][r] contiguous, same storage dtype as Q.
+ *   idx (critical-KV lists), packed int32, no padding:
+ *     row of (b,h,g) starts at NG*(b*sum_h k_h + sum_{h'<h} k_h') + g*k_h and holds k_h
+ *     strictly ascending key indices in [0,S). Total length B*NG*sum_h k_h.
+ *   k_per_head: HOST array of H int32, 1 <= k_h <= S (k_h = S is dense attention).
+ *   Scale: softmax(scale * q.k), no causal mask; the LSE is natural-log and includes the scale.
+ *
+ * Ownership and concurrency
+ *   The caller owns every buffer. Every pointer except k_per_head and the problem
+ *   descriptor is a device pointer. The library allocates nothing and keeps no state:
+ *   calls are re-entrant and thread-safe. `stream` is a hipStream_t (NULL = legacy default
+ *   stream). Calls are asynchronous: inputs must stay unchanged, and outputs unread, until
+ *   the stream has passed the call. Outputs are overwritten, never accumulated.
+ *
+ * Errors
+ *   Arguments are validated before anything is enqueued. On a non-OK status nothing has been
+ *   enqueued and the outputs are untouched. DSV_ERR_HIP reports a failed launch; device faults
+ *   surface at the caller's next synchronisation. dsv_last_error() returns a thread-local
+ *   message describing the last non-OK status.
+ */
+#ifndef DSV_H_
+#define DSV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DSV_FP32 = 0, DSV_BF16 = 1 } dsv_dtype;
+
+/* How the per-query low-rank scores of a group are combined into one group score.
+ * SUM: sigma[g][m] = sum_{n in g} Q_lr[n].K_lr[m] (MEAN ranks identically). MAX is not
+ * implemented and returns DSV_ERR_UNSUPPORTED. */
+typedef enum { DSV_GROUP_SUM = 0, DSV_GROUP_MAX = 1 } dsv_reduce;
+
+typedef enum {
+  DSV_OK = 0,
+  DSV_ERR_NULL = 1,        /* a required pointer is NULL */
+  DSV_ERR_SHAPE = 2,       /* non-positive size, group extents do not divide the grid, ... */
+  DSV_ERR_K = 3,           /* some k_h outside [1, S] */
+  DSV_ERR_DTYPE = 4,       /* dtype not one of dsv_dtype */
+  DSV_ERR_ALIGN = 5,       /* a device pointer is not 16-byte aligned */
+  DSV_ERR_WORKSPACE = 6,   /* ws_bytes < dsv_workspace_bytes(...) */
+  DSV_ERR_UNSUPPORTED = 7, /* a valid but unimplemented case (head_dim, rank, G, reduce) */
+  DSV_ERR_HIP = 8          /* the HIP runtime reported an error at launch */
+} dsv_status;
+
+typedef enum { DSV_OP_TOPK = 0, DSV_OP_FWD = 1, DSV_OP_BWD = 2 } dsv_op;
+
+typedef struct {
+  int32_t batch, heads;          /* B, H */
+  int32_t frames, height, width; /* T, Hh, W */
+  int32_t head_dim, rank;        /* d in {64,128}; r in {16,32,48,64} */
+  int32_t gt, gh, gw;            /* group extents; G = gt*gh*gw must be 16, 32, 48 or 64 */
+  int32_t dtype;                 /* dsv_dtype of Q,K,V,O,dO,Q_lr,K_lr */
+} dsv_problem;
+
+/* Bytes of device workspace `op` needs for this problem (0 today for every op; the argument
+ * pair ws/ws_bytes is kept so that later versions can use scratch without an ABI change).
+ * Returns (size_t)-1 if the problem is invalid. */
+size_t dsv_workspace_bytes(int op, const dsv_problem* p, const int32_t* k_per_head);
+
+/* Total int32 elements of the packed idx array: B * NG * sum_h k_h (0 if invalid). */
+int64_t dsv_idx_elems(const dsv_problem* p, const int32_t* k_per_head);
+
+/* Element offset of row (b,h,g) inside the packed idx array (-1 if out of range). */
+int64_t dsv_idx_row_offset(const dsv_problem* p, const int32_t* k_per_head, int32_t b,
+                           int32_t h, int32_t g);
+
+/* Critical-KV estimation: fused low-rank group scoring + exact per-group top-k.
+ * (DSV summaries: zh §2.1 and §2.2, pt §2A-§2B, fr §2A-§2B, ko §2가-§2나.)
+ *   q_lr, k_lr : [B][H][S][r] device, dtype p->dtype.
+ *   k_per_head : host [H].
+ *   reduce     : DSV_GROUP_SUM.
+ *   idx        : device int32, dsv_idx_elems() elements, written.
+ * For every (b,h,g): sigma[m] = (sum_{n in g} q_lr[n]) . k_lr[m] evaluated in fp32 (equal to
+ * summing the per-query scores, by linearity); the row holds the k_h keys with the largest
+ * sigma, equal scores ranked by lower key index, written in ascending key order.
+ * Exactness: the scores, hence idx, are exact when Q_lr and K_lr hold integers with
+ * G*max|q| < 2^16 and G*r*max|q|*max|k| < 2^24 (the bf16 path splits the group sum into two
+ * bf16 terms; outside this domain the group sum is rounded to 16 significant bits). The S x S
+ * and NG x S score matrices are never stored. */
+int dsv_lowrank_topk(const dsv_problem* p, const void* q_lr, const void* k_lr,
+                     const int32_t* k_per_head, int reduce, int32_t* idx, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* Query-grouped sparse attention, forward.
+ * (DSV summaries: zh §2.1 "sparse computation" bullet and §2.2 "Query Grouping".)
+ *   q,k,v : [B][H][S][d] device, dtype p->dtype.   idx, k_per_head: as above.
+ *   o     : [B][H][S][d] device, dtype p->dtype (written).
+ *   lse   : [B][H][S] fp32 device (written): log sum_m exp(scale*q.k_m) over the row's keys.
+ * For query n in group g: O[n] = sum_{m in idx(g)} softmax_m(scale*q_n.k_m) v_m, computed with
+ * fp32 accumulation (bf16 MFMA operands on the bf16 path). */
+int dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, const void* v,
+                        const int32_t* idx, const int32_t* k_per_head, float scale, void* o,
+                        float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Query-grouped sparse attention, backward (idx is a constant: no gradient flows to the
+ * low-rank factors).
+ *   o, d_o : [B][H][S][d] device, dtype p->dtype (o is the forward output).
+ *   lse    : forward LSE.
+ *   dq,dk,dv : [B][H][S][d] fp32 device (written; dk/dv are cleared by the call, then every
+ *              key receives the sum over all groups that selected it).
+ * With P = exp(scale*q.k - LSE), Delta_n = dO_n.O_n, dS = P*(dO.v - Delta):
+ *   dQ_n = scale*sum_m dS[n,m] k_m,  dK_m = scale*sum_n dS[n,m] q_n,  dV_m = sum_n P[n,m] dO_n.
+ * dK/dV are summed with fp32 atomics: their low bits depend on the summation order. */
+int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,
+                        const void* o, const void* d_o, const float* lse, const int32_t* idx,
+                        const int32_t* k_per_head, float scale, float* dq, float* dk, float* dv,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Validation only: returns the status the corresponding call would return for these
+ * arguments before enqueueing anything (no HIP call is made). Pointers are checked for NULL
+ * and 16-byte alignment; pass any non-NULL aligned values to check shapes alone. */
+int dsv_validate(int op, const dsv_problem* p, const int32_t* k_per_head, int reduce,
+                 const void* const* ptrs, int n_ptrs, size_t ws_bytes);
+
+const char* dsv_status_string(int status);
+const char* dsv_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* dsv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSV_H_ */
