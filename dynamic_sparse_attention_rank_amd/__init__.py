@@ -1,0 +1,248 @@
+"""Python binding of libdsv.so, the DSV hot path for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+PyTorch supplies device memory and the current HIP stream. The names mirror the C ABI in
+include/dsv.h: `lowrank_topk`, `sparse_attn_fwd`, `sparse_attn_bwd`.
+
+Import fails loudly if the library has not been built (`build()` or
+`python -m dynamic_sparse_attention_rank_amd._build`): there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import List, Optional, Sequence, Tuple
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libdsv.so")
+
+DSV_FP32, DSV_BF16 = 0, 1
+DSV_GROUP_SUM, DSV_GROUP_MAX = 0, 1
+DSV_OP_TOPK, DSV_OP_FWD, DSV_OP_BWD = 0, 1, 2
+STATUS = {0: "DSV_OK", 1: "DSV_ERR_NULL", 2: "DSV_ERR_SHAPE", 3: "DSV_ERR_K",
+          4: "DSV_ERR_DTYPE", 5: "DSV_ERR_ALIGN", 6: "DSV_ERR_WORKSPACE",
+          7: "DSV_ERR_UNSUPPORTED", 8: "DSV_ERR_HIP"}
+EXPORTED = ("dsv_workspace_bytes", "dsv_idx_elems", "dsv_idx_row_offset", "dsv_lowrank_topk",
+            "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd", "dsv_validate", "dsv_status_string",
+            "dsv_last_error", "dsv_version")
+
+
+class DsvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("batch", "heads", "frames", "height", "width", "head_dim", "rank",
+                 "gt", "gh", "gw", "dtype")]
+
+    @property
+    def seq(self) -> int:
+        return self.frames * self.height * self.width
+
+    @property
+    def group_size(self) -> int:
+        return self.gt * self.gh * self.gw
+
+    @property
+    def n_groups(self) -> int:
+        return self.seq // self.group_size
+
+
+def problem(batch, heads, frames, height, width, head_dim, rank, group, dtype) -> Problem:
+    gt, gh, gw = group
+    dt = {"fp32": DSV_FP32, "bf16": DSV_BF16}.get(dtype, dtype)
+    return Problem(batch, heads, frames, height, width, head_dim, rank, gt, gh, gw, dt)
+
+
+def problem_for(cfg) -> Problem:
+    """Problem descriptor of a `synth` workload."""
+    return problem(cfg.batch, cfg.heads, cfg.frames, cfg.height, cfg.width, cfg.head_dim,
+                   cfg.rank, cfg.group, cfg.dtype)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m dynamic_sparse_attention_rank_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(Problem)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        vp, sz, f = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+        L.dsv_workspace_bytes.argtypes = [ctypes.c_int, P, i32p]
+        L.dsv_workspace_bytes.restype = sz
+        L.dsv_idx_elems.argtypes = [P, i32p]
+        L.dsv_idx_elems.restype = ctypes.c_int64
+        L.dsv_idx_row_offset.argtypes = [P, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+        L.dsv_idx_row_offset.restype = ctypes.c_int64
+        L.dsv_lowrank_topk.argtypes = [P, vp, vp, i32p, ctypes.c_int, vp, vp, sz, vp]
+        L.dsv_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, i32p, f, vp, vp, vp, sz, vp]
+        L.dsv_sparse_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32p, f, vp, vp, vp,
+                                          vp, sz, vp]
+        L.dsv_validate.argtypes = [ctypes.c_int, P, i32p, ctypes.c_int,
+                                   ctypes.POINTER(vp), ctypes.c_int, sz]
+        L.dsv_status_string.restype = ctypes.c_char_p
+        L.dsv_status_string.argtypes = [ctypes.c_int]
+        L.dsv_last_error.restype = ctypes.c_char_p
+        L.dsv_version.restype = ctypes.c_char_p
+        for fn in ("dsv_lowrank_topk", "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd",
+                   "dsv_validate"):
+            getattr(L, fn).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _kph(k_per_head: Sequence[int]):
+    arr = (ctypes.c_int32 * len(k_per_head))(*[int(x) for x in k_per_head])
+    return arr
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DsvError(status, lib().dsv_last_error().decode())
+
+
+def last_error() -> str:
+    return lib().dsv_last_error().decode()
+
+
+def version() -> str:
+    return lib().dsv_version().decode()
+
+
+def idx_elems(p: Problem, k_per_head: Sequence[int]) -> int:
+    return int(lib().dsv_idx_elems(ctypes.byref(p), _kph(k_per_head)))
+
+
+def idx_row_offset(p: Problem, k_per_head: Sequence[int], b: int, h: int, g: int) -> int:
+    return int(lib().dsv_idx_row_offset(ctypes.byref(p), _kph(k_per_head), b, h, g))
+
+
+def workspace_bytes(op: int, p: Problem, k_per_head: Sequence[int]) -> int:
+    return int(lib().dsv_workspace_bytes(op, ctypes.byref(p), _kph(k_per_head)))
+
+
+def validate(op: int, p: Problem, k_per_head: Sequence[int], ptrs: Sequence[int],
+             reduce: int = DSV_GROUP_SUM, ws_bytes: int = 0) -> int:
+    """Status the call would return for these arguments (no HIP call is made)."""
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return int(lib().dsv_validate(op, ctypes.byref(p), _kph(k_per_head), reduce, arr,
+                                  len(ptrs), ws_bytes))
+
+
+# ----------------------------------------------------------------------------- torch layer
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(stream) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _dev(t, name, dtype=None, shape=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _storage_dtype(p: Problem):
+    torch = _torch()
+    return torch.float32 if p.dtype == DSV_FP32 else torch.bfloat16
+
+
+def lowrank_topk(p: Problem, q_lr, k_lr, k_per_head: Sequence[int], idx=None,
+                 reduce: int = DSV_GROUP_SUM, stream=None):
+    """Critical-KV index lists (packed int32, see include/dsv.h) for Q_lr, K_lr [B,H,S,r]."""
+    torch = _torch()
+    dt = _storage_dtype(p)
+    shp = (p.batch, p.heads, p.seq, p.rank)
+    qp = _dev(q_lr, "q_lr", dt, shp)
+    kp = _dev(k_lr, "k_lr", dt, shp)
+    n = idx_elems(p, k_per_head)
+    if idx is None:
+        idx = torch.zeros(max(n, 1), dtype=torch.int32, device=q_lr.device)
+    ip = _dev(idx, "idx", torch.int32)
+    if idx.numel() < n:
+        raise ValueError("idx is too small")
+    _check(lib().dsv_lowrank_topk(ctypes.byref(p), qp, kp, _kph(k_per_head), reduce, ip,
+                                  None, 0, _stream_ptr(stream)))
+    return idx
+
+
+def sparse_attn_fwd(p: Problem, q, k, v, idx, k_per_head: Sequence[int],
+                    scale: Optional[float] = None, o=None, lse=None, stream=None):
+    """(O, LSE) of the query-grouped sparse attention forward."""
+    torch = _torch()
+    dt = _storage_dtype(p)
+    shp = (p.batch, p.heads, p.seq, p.head_dim)
+    if scale is None:
+        scale = 1.0 / math.sqrt(p.head_dim)
+    ptr = [_dev(q, "q", dt, shp), _dev(k, "k", dt, shp), _dev(v, "v", dt, shp),
+           _dev(idx, "idx", torch.int32)]
+    if idx.numel() < idx_elems(p, k_per_head):
+        raise ValueError("idx is too small")
+    if o is None:
+        o = torch.empty(shp, dtype=dt, device=q.device)
+    if lse is None:
+        lse = torch.empty(shp[:3], dtype=torch.float32, device=q.device)
+    op = _dev(o, "o", dt, shp)
+    lp = _dev(lse, "lse", torch.float32, shp[:3])
+    _check(lib().dsv_sparse_attn_fwd(ctypes.byref(p), ptr[0], ptr[1], ptr[2], ptr[3],
+                                     _kph(k_per_head), float(scale), op, lp, None, 0,
+                                     _stream_ptr(stream)))
+    return o, lse
+
+
+def sparse_attn_bwd(p: Problem, q, k, v, o, d_o, lse, idx, k_per_head: Sequence[int],
+                    scale: Optional[float] = None, dq=None, dk=None, dv=None, stream=None):
+    """(dQ, dK, dV) in fp32 for the query-grouped sparse attention."""
+    torch = _torch()
+    dt = _storage_dtype(p)
+    shp = (p.batch, p.heads, p.seq, p.head_dim)
+    if scale is None:
+        scale = 1.0 / math.sqrt(p.head_dim)
+    ptr = [_dev(q, "q", dt, shp), _dev(k, "k", dt, shp), _dev(v, "v", dt, shp),
+           _dev(o, "o", dt, shp), _dev(d_o, "d_o", dt, shp),
+           _dev(lse, "lse", torch.float32, shp[:3]), _dev(idx, "idx", torch.int32)]
+    if idx.numel() < idx_elems(p, k_per_head):
+        raise ValueError("idx is too small")
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty(shp, dtype=torch.float32, device=q.device)
+        _dev(t, name, torch.float32, shp)
+        outs.append(t)
+    _check(lib().dsv_sparse_attn_bwd(ctypes.byref(p), *ptr[:6], ptr[6], _kph(k_per_head),
+                                     float(scale), outs[0].data_ptr(), outs[1].data_ptr(),
+                                     outs[2].data_ptr(), None, 0, _stream_ptr(stream)))
+    return tuple(outs)
+
+
+def idx_rows(idx, p: Problem, k_per_head: Sequence[int], b: int, h: int):
+    """View of the (b, h) block of a packed idx tensor as [NG, k_h]."""
+    off = idx_row_offset(p, k_per_head, b, h, 0)
+    kh = int(k_per_head[h])
+    return idx[off:off + p.n_groups * kh].view(p.n_groups, kh)
+
+
+def build(verbose: bool = False) -> str:
+    from . import _build
+    return _build.build(verbose=verbose)

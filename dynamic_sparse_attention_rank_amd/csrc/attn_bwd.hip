@@ -1,0 +1,437 @@
+// attn_bwd.hip — query-grouped sparse attention, backward (dQ, dK, dV) with the index lists
+// held constant.
+//
+// The DSV summaries (gist.science/{zh,pt,fr,ko}/paper/2502.07590) report sparse *training*
+// throughput (zh §4 / pt §4: up to 3.02x over full attention), which needs the backward of
+// the sparse attention of zh §2.1; the pages do not describe it. This is the standard softmax
+// attention gradient restricted to each group's selected keys:
+//     P = exp(scale q.k - LSE), Delta_n = dO_n . O_n, dS = P * (dO.v - Delta)
+//     dQ_n = scale sum_m dS[n,m] k_m     (owned by the group: written once)
+//     dK_m = scale sum_n dS[n,m] q_n     (summed over every group that selected m)
+//     dV_m = sum_n P[n,m] dO_n           (idem)
+//
+// bf16 path (gfx950 MFMA), one wave per group, keys in chunks of 32:
+//   * S = Q K^T and dP = dO V^T are computed with Q / dO as the A operand (registers) and K / V
+//     rows gathered straight into B operands. A lane then holds one key and 4 queries per
+//     16x16 tile, which is exactly the A operand of dV = P^T dO and dK = dS^T Q: no transpose
+//     of P or dS is needed there. Their B operands (dO and Q with queries contiguous per lane)
+//     are built once per group in LDS.
+//   * dQ^T += K^T dS^T needs dS with queries in lanes: dS goes through a 4 KB LDS tile; K rows
+//     are re-gathered one full row per 16 lanes and transposed in registers (v_perm_b32).
+//   * dK/dV contributions are added with fp32 atomics, 16 consecutive features per 16 lanes;
+//     dK/dV are cleared by a fill kernel on the same stream first.
+// fp32 path: plain fp32 FMA (one lane per query, then one lane per feature for dK/dV); it
+// exists for fp32 inputs and is not tuned.
+#include <math.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "dsv_internal.h"
+
+namespace dsv {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, int& h, int& g) {
+  const int per_head = geo.B * geo.NG;
+  const int slot = unit / per_head;
+  const int rem = unit - slot * per_head;
+  h = geo.order[slot];
+  b = rem / geo.NG;
+  g = rem - b * geo.NG;
+}
+
+__global__ void fill_zero(float4* __restrict__ p, long long n4) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// LDS layout of the transposed operands: for feature block db (16 features) and k-step m
+// (32 queries), lane (lg, li) reads 8 queries (lg, e), e = 0..7 <-> query
+// 16*(2m + e/4) + 4*lg + (e%4), of feature 16*db + li. Stored as [db][m][lane][8] bf16 so that
+// the read is one conflict-free 16-byte access per lane.
+template <int D, int QBP>
+struct BwdLds {
+  static constexpr int NDB = D / 16;
+  static constexpr int NM = QBP / 2;
+  uint16_t qt[NDB * NM * 64 * 8];
+  uint16_t dot[NDB * NM * 64 * 8];
+  uint16_t ds[64 * 40];   // dS tile [query][key], 32 keys + 8 pad per row
+  float lse2[64] __attribute__((aligned(16)));    // LSE * log2(e) per group member
+  float delta[64] __attribute__((aligned(16)));   // Delta per group member
+};
+
+template <int D, int QB>
+__global__ __launch_bounds__(64) void attn_bwd_bf16(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
+    const int32_t* __restrict__ idx, float scale, float* __restrict__ dq,
+    float* __restrict__ dk, float* __restrict__ dv, Geom geo) {
+  constexpr int QBP = (QB + 1) & ~1;   // query blocks padded to whole 32-query k-steps
+  constexpr int NM = QBP / 2;
+  constexpr int KS = D / 32;
+  constexpr int NDB = D / 16;
+  constexpr int DPL = D / 16;
+  using L = BwdLds<D, QBP>;
+  __shared__ __attribute__((aligned(16))) L lds;
+
+  const int lane = threadIdx.x;
+  const int lg = lane >> 4;
+  const int li = lane & 15;
+  int b, h, g;
+  decode_unit(geo, blockIdx.x, b, h, g);
+  const int kh = geo.k[h];
+  const long long bh = (long long)b * geo.H + h;
+  const long long base = bh * geo.S * D;
+  const uint16_t* Q = q + base;
+  const uint16_t* K = k + base;
+  const uint16_t* V = v + base;
+  const int32_t* row = idx + geo.row_offset(b, h, g);
+  const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
+  const int G = geo.G;
+
+  // ---- per-group set-up: A operands of S and dP, LSE, Delta, transposed B operands in LDS
+  int tok[QB];
+  u32x4 qa[QB][KS], doa[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    tok[qb] = gg.token(g, qb * 16 + li);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qa[qb][ks] = ld16(Q + (long long)tok[qb] * D + ks * 32 + 8 * lg);
+      doa[qb][ks] = ld16(d_o + base + (long long)tok[qb] * D + ks * 32 + 8 * lg);
+    }
+  }
+  // Delta_n = dO_n . O_n: lane (lg, li) covers features 32ks + 8lg .. of member 16qb + li
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 ov = ld16(o + base + (long long)tok[qb] * D + ks * 32 + 8 * lg);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = fmaf(bf16_lo(doa[qb][ks][w]), bf16_lo(ov[w]), acc);
+        acc = fmaf(bf16_hi(doa[qb][ks][w]), bf16_hi(ov[w]), acc);
+      }
+    }
+    acc = wave_xor_sum(acc, 16);
+    acc = wave_xor_sum(acc, 32);
+    if (lg == 0) {
+      lds.delta[qb * 16 + li] = acc;
+      lds.lse2[qb * 16 + li] = lse[bh * geo.S + tok[qb]] * kLog2e;
+    }
+  }
+  if (QB < QBP && lg == 0) {   // padded members: no contribution (P = 0 through lse2 = +inf)
+    lds.delta[QB * 16 + li] = 0.f;
+    lds.lse2[QB * 16 + li] = INFINITY;
+  }
+  // transposed operands: entry (db, m, lane', e) = X[member(m, lane', e)][16 db + li']
+  for (int i = lane; i < NDB * NM * 64; i += 64) {
+    const int ln = i & 63;
+    const int m = (i >> 6) % NM;
+    const int db = (i >> 6) / NM;
+    const int llg = ln >> 4, lli = ln & 15;
+    uint16_t tq[8], td[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int mem = 16 * (2 * m + e / 4) + 4 * llg + (e & 3);
+      tq[e] = 0;
+      td[e] = 0;
+      if (mem < G) {
+        const int n = gg.token(g, mem);
+        tq[e] = Q[(long long)n * D + 16 * db + lli];
+        td[e] = d_o[base + (long long)n * D + 16 * db + lli];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      lds.qt[i * 8 + e] = tq[e];
+      lds.dot[i * 8 + e] = td[e];
+    }
+  }
+  __syncthreads();
+
+  floatx4 dqacc[QB][DPL];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int f = 0; f < DPL; ++f) dqacc[qb][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+  const float c2 = scale * kLog2e;
+  float* dK = dk + base;
+  float* dV = dv + base;
+
+  u32x4 kb_n[2][KS], vb_n[2][KS];   // natural K / V rows (B operands) of the current chunk
+  auto load_nat = [&](int cb) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = clamp_key(row[min(cb + 16 * kb + li, kh - 1)], geo.S);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kb_n[kb][ks] = ld16(K + (long long)key * D + ks * 32 + 8 * lg);
+        vb_n[kb][ks] = ld16(V + (long long)key * D + ks * 32 + 8 * lg);
+      }
+    }
+  };
+  load_nat(0);
+
+  for (int cb = 0; cb < kh; cb += 32) {
+    // K rows for the dQ operand: keys 8lg + e of the chunk, features DPL*li ..
+    int tkey[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tkey[e] = clamp_key(row[min(cb + 8 * lg + e, kh - 1)], geo.S);
+    // keys whose dK/dV rows this lane updates: 16kb + 4lg + j
+    int akey[2][4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) akey[kb][j] = clamp_key(row[min(cb + 16 * kb + 4 * lg + j, kh - 1)], geo.S);
+
+    // ---- S = Q K^T, dP = dO V^T ; lane: key 16kb + li, members 16qb + 4lg + j
+    u32x4 pa[2][NM], dsa[2][NM];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const bool kvalid = cb + 16 * kb + li < kh;
+      float pv[QBP][4], dsv_[QBP][4];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        floatx4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          s = mfma_bf16(qa[qb][ks], kb_n[kb][ks], s);
+          dp = mfma_bf16(doa[qb][ks], vb_n[kb][ks], dp);
+        }
+        // LSE / Delta of the members this tile gives the lane: 16qb + 4lg + j
+        const floatx4 l2 = *reinterpret_cast<const floatx4*>(&lds.lse2[qb * 16 + 4 * lg]);
+        const floatx4 dl = *reinterpret_cast<const floatx4*>(&lds.delta[qb * 16 + 4 * lg]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = kvalid ? exp2f(s[j] * c2 - l2[j]) : 0.f;
+          pv[qb][j] = p;
+          dsv_[qb][j] = p * (dp[j] - dl[j]);
+        }
+      }
+#pragma unroll
+      for (int qb = QB; qb < QBP; ++qb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[qb][j] = dsv_[qb][j] = 0.f;
+      // A operands of P^T dO / dS^T Q: element e <-> member 16(2m + e/4) + 4lg + e%4
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        pa[kb][m][0] = pack_bf16(pv[2 * m][0], pv[2 * m][1]);
+        pa[kb][m][1] = pack_bf16(pv[2 * m][2], pv[2 * m][3]);
+        pa[kb][m][2] = pack_bf16(pv[2 * m + 1][0], pv[2 * m + 1][1]);
+        pa[kb][m][3] = pack_bf16(pv[2 * m + 1][2], pv[2 * m + 1][3]);
+        dsa[kb][m][0] = pack_bf16(dsv_[2 * m][0], dsv_[2 * m][1]);
+        dsa[kb][m][1] = pack_bf16(dsv_[2 * m][2], dsv_[2 * m][3]);
+        dsa[kb][m][2] = pack_bf16(dsv_[2 * m + 1][0], dsv_[2 * m + 1][1]);
+        dsa[kb][m][3] = pack_bf16(dsv_[2 * m + 1][2], dsv_[2 * m + 1][3]);
+      }
+      // dS tile -> LDS as [member][key]
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t w = pack_bf16(dsv_[qb][j], 0.f);
+          lds.ds[(qb * 16 + 4 * lg + j) * 40 + 16 * kb + li] = (uint16_t)(w & 0xffffu);
+        }
+    }
+    // the natural K/V registers are free again: request the next chunk's rows now
+    if (cb + 32 < kh) load_nat(cb + 32);
+
+    // ---- dV = P^T dO, dK = scale dS^T Q ; lane: feature 16db + li, keys 16kb + 4lg + j
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bool avalid[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) avalid[j] = cb + 16 * kb + 4 * lg + j < kh;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        floatx4 accv = {0.f, 0.f, 0.f, 0.f}, acck = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const int off = ((db * NM + m) * 64 + lane) * 8;
+          const u32x4 bdo = *reinterpret_cast<const u32x4*>(&lds.dot[off]);
+          const u32x4 bq = *reinterpret_cast<const u32x4*>(&lds.qt[off]);
+          accv = mfma_bf16(pa[kb][m], bdo, accv);
+          acck = mfma_bf16(dsa[kb][m], bq, acck);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (avalid[j]) {
+            const long long a = (long long)akey[kb][j] * D + 16 * db + li;
+            unsafeAtomicAdd(dV + a, accv[j]);
+            unsafeAtomicAdd(dK + a, acck[j] * scale);
+          }
+        }
+      }
+    }
+
+    // ---- dQ^T += K^T dS^T ; K transposed in registers, dS^T from the LDS tile
+    u32x4 vA[DPL];
+    {
+      if constexpr (D == 128) {
+        u32x4 raw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) raw[e] = ld16(K + (long long)tkey[e] * D + DPL * li);
+        transpose8x8_b16(raw, vA);
+      } else {
+        u32x2 raw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) raw[e] = ld8(K + (long long)tkey[e] * D + DPL * li);
+        transpose8x4_b16(raw, vA);
+      }
+    }
+    __syncthreads();   // dS tile complete (single-wave workgroup: orders the LDS writes)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      // B operand: member 16qb + li, keys 8lg + e (e = 0..7), zero past the row end
+      u32x4 bds = *reinterpret_cast<const u32x4*>(&lds.ds[(qb * 16 + li) * 40 + 8 * lg]);
+#pragma unroll
+      for (int f = 0; f < DPL; ++f) dqacc[qb][f] = mfma_bf16(vA[f], bds, dqacc[qb][f]);
+    }
+    __syncthreads();   // the next chunk overwrites the tile
+  }
+
+  // ---- store dQ (fp32): lane holds member 16qb + li, features DPL*(4lg + j) + f
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float* drow = dq + base + (long long)tok[qb] * D;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int f4 = 0; f4 < DPL / 4; ++f4) {
+        float4 w = make_float4(dqacc[qb][4 * f4][j] * scale, dqacc[qb][4 * f4 + 1][j] * scale,
+                               dqacc[qb][4 * f4 + 2][j] * scale, dqacc[qb][4 * f4 + 3][j] * scale);
+        *reinterpret_cast<float4*>(drow + DPL * (4 * lg + j) + 4 * f4) = w;
+      }
+    }
+  }
+}
+
+// fp32 inputs: lane = group member for P/dS/dQ, then lane = feature for dK/dV.
+template <int D>
+__global__ __launch_bounds__(64) void attn_bwd_f32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ o, const float* __restrict__ d_o, const float* __restrict__ lse,
+    const int32_t* __restrict__ idx, float scale, float* __restrict__ dq,
+    float* __restrict__ dk, float* __restrict__ dv, Geom geo) {
+  constexpr int CH = 16;   // keys per chunk
+  extern __shared__ float smem[];
+  const int G = geo.G;
+  float* sq = smem;                 // [G][D]
+  float* sdo = sq + G * D;          // [G][D]
+  float* sp = sdo + G * D;          // [G][CH]
+  float* sds = sp + G * CH;         // [G][CH]
+  const int lane = threadIdx.x;
+  int b, h, g;
+  decode_unit(geo, blockIdx.x, b, h, g);
+  const int kh = geo.k[h];
+  const long long bh = (long long)b * geo.H + h;
+  const long long base = bh * geo.S * D;
+  const int32_t* row = idx + geo.row_offset(b, h, g);
+  const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
+  for (int i = lane; i < G * D; i += 64) {
+    const int mem = i / D, c = i - mem * D;
+    const long long n = gg.token(g, mem);
+    sq[i] = q[base + n * D + c];
+    sdo[i] = d_o[base + n * D + c];
+  }
+  __syncthreads();
+  const bool member = lane < G;
+  const int n = member ? gg.token(g, lane) : 0;
+  float delta = 0.f, l = 0.f;
+  if (member) {
+    for (int c = 0; c < D; ++c) delta = fmaf(sdo[lane * D + c], o[base + (long long)n * D + c], delta);
+    l = lse[bh * geo.S + n];
+  }
+  float dqa[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) dqa[c] = 0.f;
+  for (int cb = 0; cb < kh; cb += CH) {
+    const int nk = min(CH, kh - cb);
+    if (member) {
+      for (int t = 0; t < nk; ++t) {
+        const long long kr = base + (long long)clamp_key(row[cb + t], geo.S) * D;
+        float s = 0.f, dp = 0.f;
+        for (int c = 0; c < D; ++c) {
+          s = fmaf(sq[lane * D + c], k[kr + c], s);
+          dp = fmaf(sdo[lane * D + c], v[kr + c], dp);
+        }
+        const float p = expf(s * scale - l);
+        const float ds = p * (dp - delta);
+        sp[lane * CH + t] = p;
+        sds[lane * CH + t] = ds;
+#pragma unroll
+        for (int c = 0; c < D; ++c) dqa[c] = fmaf(ds * scale, k[kr + c], dqa[c]);
+      }
+    }
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+      const long long kr = base + (long long)clamp_key(row[cb + t], geo.S) * D;
+      for (int c = lane; c < D; c += 64) {
+        float av = 0.f, ak = 0.f;
+        for (int mem = 0; mem < G; ++mem) {
+          av = fmaf(sp[mem * CH + t], sdo[mem * D + c], av);
+          ak = fmaf(sds[mem * CH + t], sq[mem * D + c], ak);
+        }
+        unsafeAtomicAdd(dv + kr + c, av);
+        unsafeAtomicAdd(dk + kr + c, ak * scale);
+      }
+    }
+    __syncthreads();
+  }
+  if (member) {
+#pragma unroll
+    for (int c = 0; c < D; ++c) dq[base + (long long)n * D + c] = dqa[c];
+  }
+}
+
+}  // namespace
+
+int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v, const void* o,
+                    const void* d_o, const float* lse, const int32_t* idx, float scale, float* dq,
+                    float* dk, float* dv, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const long long n4 = (long long)geo.B * geo.H * geo.S * geo.d / 4;
+  const int fill_blocks = (int)std::min<long long>((n4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_zero, dim3(fill_blocks), dim3(256), 0, st, (float4*)dk, n4);
+  hipLaunchKernelGGL(fill_zero, dim3(fill_blocks), dim3(256), 0, st, (float4*)dv, n4);
+  const dim3 grid(geo.B * geo.H * geo.NG);
+  const dim3 block(64);
+  if (geo.dtype == DSV_FP32) {
+    const size_t shm = (size_t)geo.G * (2 * geo.d + 2 * 16) * sizeof(float);
+#define DSV_BWD32(DD)                                                                         \
+  if (geo.d == DD) {                                                                          \
+    if (shm > 65536)                                                                          \
+      (void)hipFuncSetAttribute((const void*)attn_bwd_f32<DD>,                                \
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);        \
+    hipLaunchKernelGGL((attn_bwd_f32<DD>), grid, block, shm, st, (const float*)q,             \
+                       (const float*)k, (const float*)v, (const float*)o, (const float*)d_o,  \
+                       lse, idx, scale, dq, dk, dv, geo);                                     \
+    return (int)hipGetLastError();                                                            \
+  }
+    DSV_BWD32(64)
+    DSV_BWD32(128)
+#undef DSV_BWD32
+    return (int)hipErrorInvalidValue;
+  }
+  const int QBn = geo.G / 16;
+#define DSV_BWD16(DD, QQ)                                                                       \
+  if (geo.d == DD && QBn == QQ) {                                                               \
+    hipLaunchKernelGGL((attn_bwd_bf16<DD, QQ>), grid, block, 0, st, (const uint16_t*)q,         \
+                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,              \
+                       (const uint16_t*)d_o, lse, idx, scale, dq, dk, dv, geo);                 \
+    return (int)hipGetLastError();                                                              \
+  }
+  DSV_BWD16(64, 1) DSV_BWD16(64, 2) DSV_BWD16(64, 3) DSV_BWD16(64, 4)
+  DSV_BWD16(128, 1) DSV_BWD16(128, 2) DSV_BWD16(128, 3) DSV_BWD16(128, 4)
+#undef DSV_BWD16
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace dsv

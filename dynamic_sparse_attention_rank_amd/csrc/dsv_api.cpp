@@ -1,0 +1,211 @@
+// dsv_api.cpp — the C ABI: argument validation (no HIP calls) and dispatch to the launchers.
+//
+// Every check runs before anything is enqueued, so a non-OK status leaves the stream and the
+// outputs untouched.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <numeric>
+
+#include "dsv_internal.h"
+
+namespace dsv {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+static int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int validate_problem(const dsv_problem* p, const int32_t* kph, Geom* geo) {
+  if (!p) return fail(DSV_ERR_NULL, "problem descriptor is NULL");
+  if (!kph) return fail(DSV_ERR_NULL, "k_per_head is NULL");
+  const int vals[] = {p->batch, p->heads, p->frames, p->height, p->width,
+                      p->head_dim, p->rank, p->gt, p->gh, p->gw};
+  for (int v : vals)
+    if (v <= 0) return fail(DSV_ERR_SHAPE, "every size in the problem must be positive");
+  if (p->dtype != DSV_FP32 && p->dtype != DSV_BF16)
+    return fail(DSV_ERR_DTYPE, "dtype %d is not DSV_FP32 or DSV_BF16", p->dtype);
+  if (p->frames % p->gt || p->height % p->gh || p->width % p->gw)
+    return fail(DSV_ERR_SHAPE, "group %dx%dx%d does not divide the %dx%dx%d token grid", p->gt,
+                p->gh, p->gw, p->frames, p->height, p->width);
+  const long long S = (long long)p->frames * p->height * p->width;
+  if (S > (1LL << 24))
+    return fail(DSV_ERR_UNSUPPORTED, "S = %lld tokens exceeds 2^24", S);
+  if (p->heads > kMaxHeads)
+    return fail(DSV_ERR_UNSUPPORTED, "heads = %d exceeds %d", p->heads, kMaxHeads);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(DSV_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", p->head_dim);
+  if (p->rank % 16 || p->rank > 64)
+    return fail(DSV_ERR_UNSUPPORTED, "rank %d (supported: 16, 32, 48, 64)", p->rank);
+  const int G = p->gt * p->gh * p->gw;
+  if (G % 16 || G > 64)
+    return fail(DSV_ERR_UNSUPPORTED, "group size %d (supported: 16, 32, 48, 64)", G);
+  long long ksum = 0;
+  for (int h = 0; h < p->heads; ++h) {
+    if (kph[h] < 1 || kph[h] > S)
+      return fail(DSV_ERR_K, "k_per_head[%d] = %d is outside [1, %lld]", h, kph[h], S);
+    ksum += kph[h];
+  }
+  if (geo) {
+    Geom& g = *geo;
+    memset(&g, 0, sizeof(g));
+    g.B = p->batch; g.H = p->heads; g.T = p->frames; g.Hh = p->height; g.W = p->width;
+    g.S = (int)S; g.d = p->head_dim; g.r = p->rank; g.gt = p->gt; g.gh = p->gh; g.gw = p->gw;
+    g.G = G; g.NG = (int)(S / G); g.nbh = p->height / p->gh; g.nbw = p->width / p->gw;
+    g.dtype = p->dtype;
+    g.ksum = ksum;
+    long long acc = 0;
+    for (int h = 0; h < p->heads; ++h) {
+      g.k[h] = kph[h];
+      g.pre[h] = acc;
+      acc += kph[h];
+    }
+    int ord[kMaxHeads];
+    std::iota(ord, ord + p->heads, 0);
+    std::stable_sort(ord, ord + p->heads, [&](int a, int b) { return kph[a] > kph[b]; });
+    for (int h = 0; h < p->heads; ++h) g.order[h] = ord[h];
+  }
+  return DSV_OK;
+}
+
+static int check_ptr(const void* ptr, const char* name, size_t align) {
+  if (!ptr) return fail(DSV_ERR_NULL, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(ptr) % align)
+    return fail(DSV_ERR_ALIGN, "%s is not %zu-byte aligned", name, align);
+  return DSV_OK;
+}
+
+}  // namespace dsv
+
+using namespace dsv;
+
+extern "C" {
+
+const char* dsv_version(void) { return "0.1.0"; }
+
+const char* dsv_status_string(int s) {
+  switch (s) {
+    case DSV_OK: return "DSV_OK";
+    case DSV_ERR_NULL: return "DSV_ERR_NULL";
+    case DSV_ERR_SHAPE: return "DSV_ERR_SHAPE";
+    case DSV_ERR_K: return "DSV_ERR_K";
+    case DSV_ERR_DTYPE: return "DSV_ERR_DTYPE";
+    case DSV_ERR_ALIGN: return "DSV_ERR_ALIGN";
+    case DSV_ERR_WORKSPACE: return "DSV_ERR_WORKSPACE";
+    case DSV_ERR_UNSUPPORTED: return "DSV_ERR_UNSUPPORTED";
+    case DSV_ERR_HIP: return "DSV_ERR_HIP";
+    default: return "DSV_ERR_UNKNOWN";
+  }
+}
+
+const char* dsv_last_error(void) { return g_err; }
+
+size_t dsv_workspace_bytes(int op, const dsv_problem* p, const int32_t* k_per_head) {
+  if (op < DSV_OP_TOPK || op > DSV_OP_BWD) return (size_t)-1;
+  if (validate_problem(p, k_per_head, nullptr) != DSV_OK) return (size_t)-1;
+  return 0;
+}
+
+int64_t dsv_idx_elems(const dsv_problem* p, const int32_t* k_per_head) {
+  Geom g;
+  if (validate_problem(p, k_per_head, &g) != DSV_OK) return 0;
+  return (int64_t)g.B * g.NG * g.ksum;
+}
+
+int64_t dsv_idx_row_offset(const dsv_problem* p, const int32_t* k_per_head, int32_t b, int32_t h,
+                           int32_t g) {
+  Geom geo;
+  if (validate_problem(p, k_per_head, &geo) != DSV_OK) return -1;
+  if (b < 0 || b >= geo.B || h < 0 || h >= geo.H || g < 0 || g >= geo.NG) return -1;
+  return geo.row_offset(b, h, g);
+}
+
+int dsv_validate(int op, const dsv_problem* p, const int32_t* k_per_head, int reduce,
+                 const void* const* ptrs, int n_ptrs, size_t ws_bytes) {
+  Geom geo;
+  int st = validate_problem(p, k_per_head, &geo);
+  if (st != DSV_OK) return st;
+  static const char* topk_names[] = {"q_lr", "k_lr", "idx"};
+  static const size_t topk_align[] = {16, 16, 4};
+  static const char* fwd_names[] = {"q", "k", "v", "idx", "o", "lse"};
+  static const size_t fwd_align[] = {16, 16, 16, 4, 16, 4};
+  static const char* bwd_names[] = {"q", "k", "v", "o", "d_o", "lse", "idx", "dq", "dk", "dv"};
+  static const size_t bwd_align[] = {16, 16, 16, 16, 16, 4, 4, 16, 16, 16};
+  const char* const* names;
+  const size_t* aligns;
+  int n;
+  switch (op) {
+    case DSV_OP_TOPK:
+      if (reduce == DSV_GROUP_MAX)
+        return fail(DSV_ERR_UNSUPPORTED, "DSV_GROUP_MAX is not implemented");
+      if (reduce != DSV_GROUP_SUM) return fail(DSV_ERR_UNSUPPORTED, "unknown reduce %d", reduce);
+      names = topk_names; aligns = topk_align; n = 3; break;
+    case DSV_OP_FWD: names = fwd_names; aligns = fwd_align; n = 6; break;
+    case DSV_OP_BWD: names = bwd_names; aligns = bwd_align; n = 10; break;
+    default: return fail(DSV_ERR_UNSUPPORTED, "unknown op %d", op);
+  }
+  if (!ptrs || n_ptrs != n) return fail(DSV_ERR_NULL, "op %d expects %d pointers", op, n);
+  for (int i = 0; i < n; ++i)
+    if ((st = check_ptr(ptrs[i], names[i], aligns[i])) != DSV_OK) return st;
+  (void)ws_bytes;  // every op needs 0 bytes of workspace
+  return DSV_OK;
+}
+
+int dsv_lowrank_topk(const dsv_problem* p, const void* q_lr, const void* k_lr,
+                     const int32_t* k_per_head, int reduce, int32_t* idx, void* ws,
+                     size_t ws_bytes, void* stream) {
+  (void)ws;
+  const void* ptrs[] = {q_lr, k_lr, idx};
+  int st = dsv_validate(DSV_OP_TOPK, p, k_per_head, reduce, ptrs, 3, ws_bytes);
+  if (st != DSV_OK) return st;
+  Geom geo;
+  validate_problem(p, k_per_head, &geo);
+  int e = launch_topk(geo, q_lr, k_lr, idx, stream);
+  if (e) return fail(DSV_ERR_HIP, "top-k launch failed (hipError %d)", e);
+  return DSV_OK;
+}
+
+int dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, const void* v,
+                        const int32_t* idx, const int32_t* k_per_head, float scale, void* o,
+                        float* lse, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  const void* ptrs[] = {q, k, v, idx, o, lse};
+  int st = dsv_validate(DSV_OP_FWD, p, k_per_head, DSV_GROUP_SUM, ptrs, 6, ws_bytes);
+  if (st != DSV_OK) return st;
+  Geom geo;
+  validate_problem(p, k_per_head, &geo);
+  int e = launch_attn_fwd(geo, q, k, v, idx, scale, o, lse, stream);
+  if (e) return fail(DSV_ERR_HIP, "forward launch failed (hipError %d)", e);
+  return DSV_OK;
+}
+
+int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,
+                        const void* o, const void* d_o, const float* lse, const int32_t* idx,
+                        const int32_t* k_per_head, float scale, float* dq, float* dk, float* dv,
+                        void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  const void* ptrs[] = {q, k, v, o, d_o, lse, idx, dq, dk, dv};
+  int st = dsv_validate(DSV_OP_BWD, p, k_per_head, DSV_GROUP_SUM, ptrs, 10, ws_bytes);
+  if (st != DSV_OK) return st;
+  Geom geo;
+  validate_problem(p, k_per_head, &geo);
+  int e = launch_attn_bwd(geo, q, k, v, o, d_o, lse, idx, scale, dq, dk, dv, stream);
+  if (e) return fail(DSV_ERR_HIP, "backward launch failed (hipError %d)", e);
+  return DSV_OK;
+}
+
+}  // extern "C"

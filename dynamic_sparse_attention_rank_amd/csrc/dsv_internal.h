@@ -1,0 +1,46 @@
+// dsv_internal.h — host-side geometry shared by the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dsv.h"
+
+#if defined(__HIP__) || defined(__HIPCC__)
+#define DSV_HD __host__ __device__
+#else
+#define DSV_HD
+#endif
+
+namespace dsv {
+
+constexpr int kMaxHeads = 128;
+
+// Everything a kernel needs to locate its work, passed by value as a kernel argument.
+struct Geom {
+  int B, H, T, Hh, W, S, d, r, gt, gh, gw, G, NG, nbh, nbw;
+  int dtype;
+  long long ksum;            // sum_h k_h
+  int k[kMaxHeads];          // k_h
+  long long pre[kMaxHeads];  // sum_{h'<h} k_h'
+  int order[kMaxHeads];      // heads by decreasing k (stable): heavy heads are launched first
+
+  // Start of row (b, h, g) in the packed idx array.
+  DSV_HD inline long long row_offset(int b, int h, int g) const {
+    return (long long)NG * ((long long)b * ksum + pre[h]) + (long long)g * k[h];
+  }
+};
+
+// Validation (HIP-free). Fills `geo` when the problem is valid.
+int validate_problem(const dsv_problem* p, const int32_t* k_per_head, Geom* geo);
+void set_error(const char* fmt, ...);
+
+// Kernel launchers (one per translation unit). Return 0 or a hipError_t value.
+int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int32_t* idx, void* stream);
+int launch_attn_fwd(const Geom& geo, const void* q, const void* k, const void* v,
+                    const int32_t* idx, float scale, void* o, float* lse, void* stream);
+int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v, const void* o,
+                    const void* d_o, const float* lse, const int32_t* idx, float scale, float* dq,
+                    float* dk, float* dv, void* stream);
+
+}  // namespace dsv

@@ -113,6 +113,8 @@ def gathered_backward(q, k, v, do, members, rows, scale, groups=None):
         dp = dog @ vg.T
         ds = p * (dp - delta)
         dq[mem] = scale * (ds @ kg)
-        np.add.at(dk, sel, scale * (ds.T @ qg))
-        np.add.at(dv, sel, p.T @ dog)
+        # rows are strictly ascending, so `sel` has no repeats and += adds each key once
+        assert np.all(np.diff(sel) > 0)
+        dk[sel] += scale * (ds.T @ qg)
+        dv[sel] += p.T @ dog
     return dq, dk, dv

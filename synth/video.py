@@ -45,8 +45,14 @@ def _blur_axis(x: torch.Tensor, dim: int, taps: List[float]) -> torch.Tensor:
     n = x.shape[dim]
     if n == 1:
         return x
-    # reflect index map, valid while r < n (true for every workload grid)
-    idx = [abs(i) if i < 0 else (2 * (n - 1) - i if i >= n else i) for i in range(-r, n + r)]
+    # reflect index map (x[-1] = x[1]), folded repeatedly for grids shorter than the taps
+    period = 2 * (n - 1)
+
+    def fold(i):
+        j = i % period
+        return period - j if j >= n else j
+
+    idx = [fold(i) for i in range(-r, n + r)]
     idx_t = torch.tensor(idx, device=x.device)
     xp = x.index_select(dim, idx_t)
     out = torch.zeros_like(x)

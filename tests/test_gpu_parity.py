@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path through the C ABI against the oracle, element by element.
+
+Bars: idx bit-exact; O, dQ, dK, dV within max-abs-err 1e-3 (fp32 path) / 2e-2 (bf16 path);
+LSE within the same bar. Sizes are chosen so the oracle finishes in seconds while spanning
+several tiles and a ragged tail."""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_sparse_attention_rank_amd as dsv
+from oracle import attention as oatt
+from parity_util import (TOL, characterise_all_rows, f64, gpu_inputs, gpu_rows, maxerr,
+                         members, oracle_bwd, oracle_fwd, oracle_rows, run_bwd, run_fwd,
+                         run_topk, say, workload)
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------------------------- top-k
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_topk_bit_exact_full_config(name):
+    cfg = workload(name)
+    say(f"[topk] {name}")
+    x = gpu_inputs(cfg, backward=False)
+    idx = run_topk(cfg, x)
+    torch.cuda.synchronize()
+    mem = members(cfg)
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            ref = oracle_rows(cfg, x, b, h, mem)
+            got = gpu_rows(cfg, x, idx, b, h)
+            assert np.array_equal(got, ref), (b, h, np.argwhere(got != ref)[:5])
+
+
+TOPK_CASES = [
+    # (label, overrides, k_per_head)
+    ("k1", dict(heads=2, frames=4, height=8, width=8, group=(2, 2, 4), rank=32), [1, 1]),
+    ("kS", dict(heads=2, frames=2, height=8, width=8, group=(2, 2, 4), rank=32), [128, 128]),
+    ("ragged-k", dict(heads=3, frames=4, height=8, width=12, group=(2, 2, 4), rank=32),
+     [7, 45, 100]),
+    ("G32-r48", dict(heads=2, frames=4, height=8, width=16, group=(2, 4, 4), rank=48), [33, 60]),
+    ("G48-r64", dict(heads=2, frames=3, height=8, width=16, group=(3, 4, 4), rank=64), [50, 9]),
+    ("NG36", dict(heads=2, frames=4, height=12, width=12, group=(2, 2, 4), rank=16), [71, 200]),
+    ("fp32-r32", dict(heads=2, frames=4, height=8, width=8, group=(2, 2, 4), rank=32,
+                      dtype="fp32"), [19, 64]),
+    ("fp32-r48", dict(heads=1, frames=4, height=8, width=8, group=(1, 4, 4), rank=48,
+                      dtype="fp32"), [100]),
+]
+
+
+@pytest.mark.parametrize("label,over,ks", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_topk_edge_cases_bit_exact(label, over, ks):
+    cfg = workload("small", **over)
+    say(f"[topk-edge] {label}")
+    x = gpu_inputs(cfg, backward=False, k_per_head=ks)
+    idx = run_topk(cfg, x)
+    torch.cuda.synchronize()
+    for h in range(cfg.heads):
+        assert np.array_equal(gpu_rows(cfg, x, idx, 0, h), oracle_rows(cfg, x, 0, h)), h
+
+
+def test_topk_all_ties_takes_lowest_indices():
+    cfg = workload("small", heads=1, frames=4, height=8, width=8, group=(2, 2, 4), rank=32)
+    x = gpu_inputs(cfg, backward=False, k_per_head=[37])
+    x["q_lr"].zero_()
+    idx = run_topk(cfg, x)
+    rows = gpu_rows(cfg, x, idx, 0, 0)
+    assert np.array_equal(rows, np.tile(np.arange(37), (rows.shape[0], 1)))
+
+
+def test_topk_repeatable_bitwise():
+    cfg = workload("small", heads=4)
+    x = gpu_inputs(cfg, backward=False)
+    a = run_topk(cfg, x).clone()
+    b = run_topk(cfg, x)
+    assert torch.equal(a, b)
+    assert characterise_all_rows(cfg, x, b, 0, 3) == 0
+
+
+# ------------------------------------------------------------------------------- forward
+def _fwd_check(cfg, x, idx, heads=None, groups=None):
+    o, lse = run_fwd(cfg, x, idx)
+    torch.cuda.synchronize()
+    tol = TOL[cfg.dtype]
+    mem = members(cfg)
+    worst = 0.0
+    for b in range(cfg.batch):
+        for h in (range(cfg.heads) if heads is None else heads):
+            rows = gpu_rows(cfg, x, idx, b, h)
+            ro, rl = oracle_fwd(cfg, x, rows, b, h, groups=groups, mem=mem)
+            eo = maxerr(f64(o[b, h]), ro)
+            el = maxerr(f64(lse[b, h]), rl)
+            worst = max(worst, eo, el)
+            assert eo <= tol and el <= tol, (b, h, eo, el)
+    say(f"   worst max-abs-err {worst:.3e} (bar {tol})")
+    return o, lse
+
+
+def test_fwd_tiny_fp32_vs_dense_oracle():
+    cfg = workload("tiny")
+    say("[fwd] tiny fp32")
+    x = gpu_inputs(cfg, backward=False)
+    idx = run_topk(cfg, x)
+    o, lse = run_fwd(cfg, x, idx)
+    torch.cuda.synchronize()
+    mem = members(cfg)
+    for h in range(cfg.heads):
+        rows = gpu_rows(cfg, x, idx, 0, h)
+        ro, rl, _ = oatt.dense_masked_forward(f64(x["q"][0, h]), f64(x["k"][0, h]),
+                                              f64(x["v"][0, h]), mem, rows, x["scale"])
+        assert maxerr(f64(o[0, h]), ro) <= 1e-3
+        assert maxerr(f64(lse[0, h]), rl) <= 1e-3
+
+
+def test_fwd_small_bf16_all_groups():
+    cfg = workload("small")
+    say("[fwd] small bf16")
+    x = gpu_inputs(cfg, backward=False)
+    idx = run_topk(cfg, x)
+    _fwd_check(cfg, x, idx)
+
+
+FWD_CASES = [
+    ("bf16-d128-G64", dict(heads=2, frames=4, height=16, width=16, head_dim=128, rank=32),
+     [300, 77]),
+    ("bf16-d64-G16", dict(heads=2, frames=4, height=16, width=16, group=(2, 2, 4)), [1, 45]),
+    ("bf16-d128-G32", dict(heads=2, frames=4, height=8, width=16, group=(2, 4, 4),
+                           head_dim=128, rank=32), [33, 512]),
+    ("bf16-d64-G48-kS", dict(heads=1, frames=3, height=8, width=16, group=(3, 4, 4)), [384]),
+    ("fp32-d128-G64", dict(heads=2, frames=4, height=8, width=8, head_dim=128, rank=32,
+                           dtype="fp32"), [17, 256]),
+    ("fp32-d64-G16-k1", dict(heads=1, frames=4, height=8, width=8, group=(2, 2, 4),
+                             dtype="fp32"), [1]),
+]
+
+
+@pytest.mark.parametrize("label,over,ks", FWD_CASES, ids=[c[0] for c in FWD_CASES])
+def test_fwd_edge_cases(label, over, ks):
+    cfg = workload("small", **over)
+    say(f"[fwd-edge] {label}")
+    x = gpu_inputs(cfg, backward=False, k_per_head=ks)
+    idx = run_topk(cfg, x)
+    o, lse = _fwd_check(cfg, x, idx)
+    if ks[0] == 1:   # one key: O is that key's V row (stored dtype)
+        rows = gpu_rows(cfg, x, idx, 0, 0)
+        mem = members(cfg)
+        for g in range(rows.shape[0]):
+            ref = f64(x["v"][0, 0, rows[g, 0]])
+            assert np.max(np.abs(f64(o[0, 0, mem[g]]) - ref)) <= TOL[cfg.dtype]
+
+
+def test_fwd_repeatable_bitwise():
+    cfg = workload("small", heads=4)
+    x = gpu_inputs(cfg, backward=False)
+    idx = run_topk(cfg, x)
+    o1, l1 = run_fwd(cfg, x, idx)
+    o1, l1 = o1.clone(), l1.clone()
+    o2, l2 = run_fwd(cfg, x, idx)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------------------ backward
+def _bwd_check(cfg, x, idx, heads=None):
+    o, lse = run_fwd(cfg, x, idx)
+    dq, dk, dv = run_bwd(cfg, x, idx, o, lse)
+    torch.cuda.synchronize()
+    tol = TOL[cfg.dtype]
+    worst = 0.0
+    mem = members(cfg)
+    for b in range(cfg.batch):
+        for h in (range(cfg.heads) if heads is None else heads):
+            rows = gpu_rows(cfg, x, idx, b, h)
+            rq, rk, rv = oracle_bwd(cfg, x, rows, b, h, mem=mem)
+            e = (maxerr(f64(dq[b, h]), rq), maxerr(f64(dk[b, h]), rk), maxerr(f64(dv[b, h]), rv))
+            worst = max(worst, *e)
+            assert max(e) <= tol, (b, h, e)
+            # unselected keys receive exactly zero
+            unsel = np.setdiff1d(np.arange(cfg.seq), np.unique(rows))
+            if unsel.size:
+                assert not dk[b, h, unsel].any() and not dv[b, h, unsel].any()
+    say(f"   worst max-abs-err {worst:.3e} (bar {tol})")
+    return dq, dk, dv
+
+
+def test_bwd_tiny_shape_fp32():
+    cfg = workload("tiny")
+    say("[bwd] tiny fp32")
+    x = gpu_inputs(cfg, backward=True)
+    idx = run_topk(cfg, x)
+    _bwd_check(cfg, x, idx)
+
+
+def test_bwd_small_bf16_all_heads():
+    cfg = workload("small")
+    say("[bwd] small bf16")
+    x = gpu_inputs(cfg, backward=True)
+    idx = run_topk(cfg, x)
+    dq, dk, dv = _bwd_check(cfg, x, idx)
+    # sum rules per (b, h): sum_m dV_m = sum_n dO_n, sum_m dK_m = 0
+    s_dv = dv.double().sum(dim=2)
+    s_do = x["do"].double().sum(dim=2)
+    assert float((s_dv - s_do).abs().max()) < 0.5
+    assert float(dk.double().sum(dim=2).abs().max()) < 0.5
+
+
+BWD_CASES = [
+    ("bf16-d128-G64", dict(heads=2, frames=4, height=16, width=16, head_dim=128, rank=32),
+     [300, 77]),
+    ("bf16-d64-G16", dict(heads=2, frames=4, height=16, width=16, group=(2, 2, 4)), [1, 45]),
+    ("bf16-d128-G48", dict(heads=1, frames=3, height=8, width=16, group=(3, 4, 4),
+                           head_dim=128, rank=32), [100]),
+    ("bf16-d64-G32-kS", dict(heads=1, frames=2, height=8, width=16, group=(2, 4, 4)), [256]),
+    ("fp32-d128-G64", dict(heads=2, frames=4, height=8, width=8, head_dim=128, rank=32,
+                           dtype="fp32"), [17, 256]),
+    ("fp32-d64-G32-k1", dict(heads=1, frames=4, height=8, width=8, group=(2, 4, 4),
+                             dtype="fp32"), [1]),
+]
+
+
+@pytest.mark.parametrize("label,over,ks", BWD_CASES, ids=[c[0] for c in BWD_CASES])
+def test_bwd_edge_cases(label, over, ks):
+    cfg = workload("small", **over)
+    say(f"[bwd-edge] {label}")
+    x = gpu_inputs(cfg, backward=True, k_per_head=ks)
+    idx = run_topk(cfg, x)
+    dq, dk, dv = _bwd_check(cfg, x, idx)
+    if ks[0] == 1:   # a single key per group: dQ = dK = 0
+        assert float(dq[0, 0].abs().max()) <= TOL[cfg.dtype]
+        assert float(dk[0, 0].abs().max()) <= TOL[cfg.dtype]
