@@ -1,0 +1,135 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark times.
+
+The oracle cannot run every output at these sizes in seconds, so:
+  * top-k: every row of every head is checked with the exact characterisation (pinned to the
+    brute-force sort by the CPU tests), plus brute force on sampled groups;
+  * forward: sampled groups of every head against the gathered fp64 oracle;
+  * backward: dQ on sampled groups, dK/dV of one full head (all groups' contributions), and
+    the sum rules on every head.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_sparse_attention_rank_amd as dsv
+from oracle import topk as otopk
+from parity_util import (TOL, characterise_all_rows, f64, gpu_inputs, gpu_rows, maxerr,
+                         members, oracle_bwd, oracle_fwd, run_bwd, run_fwd, run_topk, say,
+                         workload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sampled_groups(NG, n, seed):
+    rng = np.random.default_rng(seed)
+    return sorted(set([0, NG - 1] + rng.choice(NG, size=n, replace=False).tolist()))
+
+
+def _topk_checks(cfg, x, idx, heads=None, brute_groups=3, seed=0):
+    mem = members(cfg)
+    heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)] if heads is None else heads
+    for b, h in heads:
+        bad = characterise_all_rows(cfg, x, idx, b, h, mem)
+        assert bad == 0, (b, h, bad)
+    b, h = heads[0]
+    rows = gpu_rows(cfg, x, idx, b, h)
+    for g in _sampled_groups(cfg.n_groups, brute_groups, seed):
+        sig = otopk.group_scores_bruteforce(f64(x["q_lr"][b, h]), f64(x["k_lr"][b, h]),
+                                            mem[g:g + 1])
+        ref = otopk.topk_rows_by_sort(sig, int(x["k_per_head"][h]))[0]
+        assert np.array_equal(rows[g], ref), (b, h, g)
+
+
+def _fwd_sampled(cfg, x, idx, o, lse, n_groups=6, seed=1):
+    mem = members(cfg)
+    worst = 0.0
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            groups = _sampled_groups(cfg.n_groups, n_groups, seed + 31 * h + b)
+            rows = gpu_rows(cfg, x, idx, b, h)
+            ro, rl = oracle_fwd(cfg, x, rows, b, h, groups=groups, mem=mem)
+            eo, el = maxerr(f64(o[b, h]), ro), maxerr(f64(lse[b, h]), rl)
+            worst = max(worst, eo, el)
+            assert eo <= TOL[cfg.dtype] and el <= TOL[cfg.dtype], (b, h, eo, el)
+    say(f"   fwd sampled worst max-abs-err {worst:.3e}")
+
+
+def test_mid_topk_fwd_bwd():
+    cfg = workload("mid")
+    say("[full] mid: top-k + fwd + bwd at S=65536, 24 heads")
+    x = gpu_inputs(cfg, backward=True)
+    idx = run_topk(cfg, x)
+    torch.cuda.synchronize()
+    _topk_checks(cfg, x, idx)
+    o, lse = run_fwd(cfg, x, idx)
+    dq, dk, dv = run_bwd(cfg, x, idx, o, lse)
+    torch.cuda.synchronize()
+    _fwd_sampled(cfg, x, idx, o, lse, n_groups=4)
+    mem = members(cfg)
+    # dQ on sampled groups of three heads; dK/dV of head 5 over all its groups
+    for h in (0, 11, 23):
+        groups = _sampled_groups(cfg.n_groups, 3, 100 + h)
+        rows = gpu_rows(cfg, x, idx, 0, h)
+        rq, _, _ = oracle_bwd(cfg, x, rows, 0, h, groups=groups, mem=mem)
+        e = maxerr(f64(dq[0, h]), rq)
+        assert e <= TOL["bf16"], (h, e)
+    h = 5
+    rows = gpu_rows(cfg, x, idx, 0, h)
+    rq, rk, rv = oracle_bwd(cfg, x, rows, 0, h, mem=mem)
+    e = (maxerr(f64(dq[0, h]), rq), maxerr(f64(dk[0, h]), rk), maxerr(f64(dv[0, h]), rv))
+    say(f"   bwd head {h} max-abs-err dq/dk/dv {e}")
+    assert max(e) <= TOL["bf16"], e
+    s_dv = dv.double().sum(dim=2)
+    s_do = x["do"].double().sum(dim=2)
+    assert float((s_dv - s_do).abs().max()) < 1.0
+    assert float(dk.double().sum(dim=2).abs().max()) < 1.0
+
+
+def test_long_heterogeneous_topk_fwd():
+    cfg = workload("long")
+    say("[full] long: S=131072, per-head k drawn from {2,5,10,20}%")
+    x = gpu_inputs(cfg, backward=False)
+    ks = x["k_per_head"]
+    say(f"   k_per_head = {ks}")
+    assert len(set(ks)) > 1
+    idx = run_topk(cfg, x)
+    torch.cuda.synchronize()
+    heavy = int(np.argmax(ks))
+    light = int(np.argmin(ks))
+    _topk_checks(cfg, x, idx, heads=[(0, heavy), (0, light)] +
+                 [(0, h) for h in range(0, cfg.heads, 3)])
+    o, lse = run_fwd(cfg, x, idx)
+    torch.cuda.synchronize()
+    _fwd_sampled(cfg, x, idx, o, lse, n_groups=3)
+
+
+def test_training_steps():
+    cfg = workload("training")
+    say("[full] training: 2 x S=61440, 24 heads, k=5%, 20 seeded steps")
+    for step in range(cfg.steps):
+        x = gpu_inputs(cfg, step=step, backward=True)
+        idx = run_topk(cfg, x)
+        o, lse = run_fwd(cfg, x, idx)
+        dq, dk, dv = run_bwd(cfg, x, idx, o, lse)
+        torch.cuda.synchronize()
+        if step == 0:
+            _topk_checks(cfg, x, idx, brute_groups=2)
+            _fwd_sampled(cfg, x, idx, o, lse, n_groups=2)
+            b, h = 1, 7
+            rows = gpu_rows(cfg, x, idx, b, h)
+            rq, rk, rv = oracle_bwd(cfg, x, rows, b, h, mem=members(cfg))
+            e = (maxerr(f64(dq[b, h]), rq), maxerr(f64(dk[b, h]), rk),
+                 maxerr(f64(dv[b, h]), rv))
+            say(f"   step 0 bwd (b={b}, h={h}) max-abs-err {e}")
+            assert max(e) <= TOL["bf16"], e
+        else:
+            # every step: exact top-k characterisation on two heads, one sampled fwd group
+            hs = [(step % 2, (3 * step) % cfg.heads), ((step + 1) % 2, (7 * step + 1) % cfg.heads)]
+            _topk_checks(cfg, x, idx, heads=hs, brute_groups=0, seed=step)
+            b, h = hs[0]
+            rows = gpu_rows(cfg, x, idx, b, h)
+            ro, _ = oracle_fwd(cfg, x, rows, b, h, groups=[step % cfg.n_groups])
+            assert maxerr(f64(o[b, h]), ro) <= TOL["bf16"]
+        say(f"   step {step} ok")
+        del x, idx, o, lse, dq, dk, dv
+        torch.cuda.empty_cache()
