@@ -119,6 +119,8 @@ def main():
     o = torch.empty(shp, dtype=dt, device=dev)
     lse = torch.empty(shp[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = (torch.empty(shp, dtype=torch.float32, device=dev) for _ in range(3))
+    ws_n = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -132,7 +134,7 @@ def main():
         if ev is not None:
             ev[2].record(stream)
         dsv.sparse_attn_bwd(p, x["q"], x["k"], x["v"], o, x["do"], lse, idx, ks, x["scale"],
-                            dq=dq, dk=dk, dv=dv, stream=stream)
+                            dq=dq, dk=dk, dv=dv, ws=ws, stream=stream)
         if ev is not None:
             ev[3].record(stream)
 

@@ -212,8 +212,12 @@ def sparse_attn_fwd(p: Problem, q, k, v, idx, k_per_head: Sequence[int],
 
 
 def sparse_attn_bwd(p: Problem, q, k, v, o, d_o, lse, idx, k_per_head: Sequence[int],
-                    scale: Optional[float] = None, dq=None, dk=None, dv=None, stream=None):
-    """(dQ, dK, dV) in fp32 for the query-grouped sparse attention."""
+                    scale: Optional[float] = None, dq=None, dk=None, dv=None, ws=None,
+                    stream=None):
+    """(dQ, dK, dV) in fp32 for the query-grouped sparse attention.
+
+    `ws` is a device uint8 tensor of at least workspace_bytes(DSV_OP_BWD, ...) bytes; one is
+    allocated for the call when it is None."""
     torch = _torch()
     dt = _storage_dtype(p)
     shp = (p.batch, p.heads, p.seq, p.head_dim)
@@ -230,9 +234,14 @@ def sparse_attn_bwd(p: Problem, q, k, v, o, d_o, lse, idx, k_per_head: Sequence[
             t = torch.empty(shp, dtype=torch.float32, device=q.device)
         _dev(t, name, torch.float32, shp)
         outs.append(t)
+    need = workspace_bytes(DSV_OP_BWD, p, k_per_head)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp = _dev(ws, "ws", torch.uint8) if ws is not None else None
+    wn = ws.numel() if ws is not None else 0
     _check(lib().dsv_sparse_attn_bwd(ctypes.byref(p), *ptr[:6], ptr[6], _kph(k_per_head),
                                      float(scale), outs[0].data_ptr(), outs[1].data_ptr(),
-                                     outs[2].data_ptr(), None, 0, _stream_ptr(stream)))
+                                     outs[2].data_ptr(), wp, wn, _stream_ptr(stream)))
     return tuple(outs)
 
 
