@@ -119,7 +119,8 @@ def main():
     o = torch.empty(shp, dtype=dt, device=dev)
     lse = torch.empty(shp[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = (torch.empty(shp, dtype=torch.float32, device=dev) for _ in range(3))
-    ws_n = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks)
+    # the backward's minimum workspace covers one (b, h) slot; four slots per launch
+    ws_n = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks) * min(4, cfg.batch * cfg.heads)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -170,7 +171,8 @@ def main():
                             "tflops": f_fwd / (mean(t_fwd) * 1e-3) / 1e12},
         "sparse_attn_bwd": {"ms_mean": mean(t_bwd), "ms_median": med(t_bwd),
                             "tflops": f_bwd / (mean(t_bwd) * 1e-3) / 1e12,
-                            "note": "call = two dK/dV clear kernels + the backward kernel"},
+                            "note": "call = per chunk of (b,h) slots: bucket count + scan + "
+                                    "backward kernel + bucket reduce"},
     }
     dom = max(kernels, key=lambda kname: kernels[kname]["ms_mean"])
     peak = PEAK["bf16_mfma_tflops"] if cfg.dtype == "bf16" else PEAK["fp32_mfma_tflops"]

@@ -18,8 +18,14 @@
 //     are built once per group in LDS.
 //   * dQ^T += K^T dS^T needs dS with queries in lanes: dS goes through a 4 KB LDS tile; K rows
 //     are re-gathered one full row per 16 lanes and transposed in registers (v_perm_b32).
-//   * dK/dV contributions are added with fp32 atomics, 16 consecutive features per 16 lanes;
-//     dK/dV are cleared by a fill kernel on the same stream first.
+//   * dK/dV: each (group, selected key) edge yields one fp32 row of dV and one of dK. fp32
+//     atomics on this chip sustain only ~0.33 T adds/s, so the rows are not added in place:
+//     the key range is cut into 64-key buckets, every edge has a fixed row slot in its bucket
+//     (rows ordered by group, then by row position; the slots come from two small prefix
+//     passes over the index rows) and writes its dV|dK row there, and a reduce kernel then
+//     sums each bucket's rows in LDS (one workgroup per bucket, one lane per feature, no
+//     atomics) and writes every dK/dV row of the bucket exactly once. Heads are processed in
+//     chunks sized to the caller's workspace.
 // fp32 path: plain fp32 FMA (one lane per query, then one lane per feature for dK/dV); it
 // exists for fp32 inputs and is not tuned.
 #include <math.h>
@@ -41,6 +47,146 @@ __device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, i
   h = geo.order[slot];
   b = rem / geo.NG;
   g = rem - b * geo.NG;
+}
+
+
+constexpr int kBucketLog2 = 6;   // 64 keys per dK/dV bucket
+constexpr int kBucket = 1 << kBucketLog2;
+constexpr int kMaxChunk = 64;    // (b, h) slots per chunk
+
+__host__ __device__ inline int n_buckets(int S) { return (S + kBucket - 1) / kBucket; }
+
+// A chunk of consecutive (b, h) slots in launch order (slot s = head rank * B + b).
+struct Chunk {
+  int s0, n;
+  long long edge_base[kMaxChunk + 1];   // first buffer row of each slot; [n] = rows in chunk
+};
+
+__device__ __forceinline__ void chunk_slot(const Geom& geo, int s, int& b, int& h) {
+  const int hs = s / geo.B;
+  b = s - hs * geo.B;
+  h = geo.order[hs];
+}
+
+// Row entry points: rs[g][j] = first position of row g whose key lies in bucket >= j
+// (rs[g][nB] = k). One wave per row; rows are ascending, so each bucket's keys form one run.
+__global__ __launch_bounds__(256) void row_bucket_starts(const int32_t* __restrict__ idx, Chunk ch,
+                                                         uint32_t* __restrict__ rs, Geom geo) {
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int lane = threadIdx.x & 63;
+  if (wave >= ch.n * geo.NG) return;
+  const int sl = wave / geo.NG;
+  const int g = wave - sl * geo.NG;
+  int b, h;
+  chunk_slot(geo, ch.s0 + sl, b, h);
+  const int kh = geo.k[h];
+  const int nB = n_buckets(geo.S);
+  const int32_t* row = idx + geo.row_offset(b, h, g);
+  uint32_t* r = rs + (long long)wave * (nB + 1);
+  for (int p = lane; p < kh; p += 64) {
+    const int jp = clamp_key(row[p], geo.S) >> kBucketLog2;
+    const int jq = p == 0 ? -1 : (clamp_key(row[p - 1], geo.S) >> kBucketLog2);
+    for (int j = jq + 1; j <= jp; ++j) r[j] = (uint32_t)p;
+  }
+  const int jl = clamp_key(row[kh - 1], geo.S) >> kBucketLog2;
+  for (int j = jl + 1 + lane; j <= nB; j += 64) r[j] = (uint32_t)kh;
+}
+
+// Column pass: for bucket j of slot sl, base[g][j] = (rows of bucket j owned by groups < g)
+// - rs[g][j], so that the row of position p (key in bucket j) is off[j] + base[g][j] + p.
+// tot[j] = rows of bucket j. One thread per bucket column, groups walked in order.
+__global__ __launch_bounds__(64) void bucket_columns(const uint32_t* __restrict__ rs,
+                                                     uint32_t* __restrict__ base,
+                                                     uint32_t* __restrict__ tot, Geom geo) {
+  const int nB = n_buckets(geo.S);
+  const int sl = blockIdx.y;
+  const int j = blockIdx.x * 64 + threadIdx.x;
+  if (j >= nB) return;
+  const uint32_t* r = rs + (long long)sl * geo.NG * (nB + 1);
+  uint32_t* bs = base + (long long)sl * geo.NG * nB;
+  uint32_t run = 0;
+  for (int g = 0; g < geo.NG; ++g) {
+    const uint32_t s0 = r[(long long)g * (nB + 1) + j];
+    const uint32_t s1 = r[(long long)g * (nB + 1) + j + 1];
+    bs[(long long)g * nB + j] = run - s0;   // modular arithmetic: adding p gives the row
+    run += s1 - s0;
+  }
+  tot[(long long)sl * (nB + 1) + j] = run;
+}
+
+// off[j] = exclusive prefix of tot over buckets (off[nB] = rows of the slot).
+__global__ __launch_bounds__(256) void bucket_offsets(const uint32_t* __restrict__ tot,
+                                                      uint32_t* __restrict__ off, Geom geo) {
+  const int nB = n_buckets(geo.S);
+  const uint32_t* c = tot + (long long)blockIdx.x * (nB + 1);
+  uint32_t* o = off + (long long)blockIdx.x * (nB + 1);
+  __shared__ uint32_t part[256];
+  const int per = (nB + 255) / 256;
+  const int j0 = threadIdx.x * per;
+  uint32_t sum = 0;
+  for (int j = j0; j < min(j0 + per, nB); ++j) sum += c[j];
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  for (int stride = 1; stride < 256; stride <<= 1) {
+    const uint32_t x = threadIdx.x >= stride ? part[threadIdx.x - stride] : 0u;
+    __syncthreads();
+    part[threadIdx.x] += x;
+    __syncthreads();
+  }
+  uint32_t run = part[threadIdx.x] - sum;
+  for (int j = j0; j < min(j0 + per, nB); ++j) {
+    o[j] = run;
+    run += c[j];
+  }
+  if (threadIdx.x == 255) o[nB] = part[255];
+}
+
+// Sum each bucket's rows: one workgroup per (slot, bucket), thread t owns feature column t of
+// the 2D-wide dV|dK rows, accumulators for the bucket's 64 keys in LDS (plain read-add-write,
+// no two threads share a word), then every key row of the bucket is written once.
+template <int D>
+__global__ __launch_bounds__(2 * D) void bucket_reduce(const uint32_t* __restrict__ off,
+                                                       const int32_t* __restrict__ keyid,
+                                                       const float* __restrict__ contrib, Chunk ch,
+                                                       float* __restrict__ dk,
+                                                       float* __restrict__ dv, Geom geo) {
+  constexpr int W = 2 * D;
+  __shared__ float acc[kBucket * W];
+  const int nB = n_buckets(geo.S);
+  const int sl = blockIdx.x / nB;
+  const int j = blockIdx.x - sl * nB;
+  int b, h;
+  chunk_slot(geo, ch.s0 + sl, b, h);
+  const long long bh = (long long)b * geo.H + h;
+  const int t = threadIdx.x;
+  for (int i = t; i < kBucket * W; i += W) acc[i] = 0.f;
+  __syncthreads();
+  const uint32_t* o = off + (long long)sl * (nB + 1);
+  const long long nrows = ch.edge_base[sl + 1] - ch.edge_base[sl];
+  const long long r0 = ch.edge_base[sl] + std::min<long long>(o[j], nrows);
+  const long long r1 = ch.edge_base[sl] + std::min<long long>(std::max<long long>(o[j + 1], o[j]), nrows);
+  const int key0 = j * kBucket;
+  long long r = r0;
+  for (; r + 8 <= r1; r += 8) {
+    int kk[8];
+    float val[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      kk[u] = min(max(keyid[r + u] - key0, 0), kBucket - 1);
+      val[u] = contrib[(r + u) * W + t];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[kk[u] * W + t] += val[u];
+  }
+  for (; r < r1; ++r) {
+    const int kk = min(max(keyid[r] - key0, 0), kBucket - 1);
+    acc[kk * W + t] += contrib[r * W + t];
+  }
+  __syncthreads();
+  const int nk = min(kBucket, geo.S - key0);
+  float* out = (t < D ? dv : dk) + bh * geo.S * D;
+  const int c = t < D ? t : t - D;
+  for (int l = 0; l < nk; ++l) out[(long long)(key0 + l) * D + c] = acc[l * W + t];
 }
 
 __global__ void fill_zero(float4* __restrict__ p, long long n4) {
@@ -69,8 +215,9 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
-    const int32_t* __restrict__ idx, float scale, float* __restrict__ dq,
-    float* __restrict__ dk, float* __restrict__ dv, Geom geo) {
+    const int32_t* __restrict__ idx, float scale, float* __restrict__ dq, Chunk ch,
+    const uint32_t* __restrict__ base_tab, const uint32_t* __restrict__ off_tab,
+    int32_t* __restrict__ keyid, float* __restrict__ contrib, Geom geo) {
   constexpr int QBP = (QB + 1) & ~1;   // query blocks padded to whole 32-query k-steps
   constexpr int NM = QBP / 2;
   constexpr int KS = D / 32;
@@ -82,8 +229,10 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
   const int lane = threadIdx.x;
   const int lg = lane >> 4;
   const int li = lane & 15;
-  int b, h, g;
-  decode_unit(geo, blockIdx.x, b, h, g);
+  const int sl = blockIdx.x / geo.NG;   // (b, h) slot inside this chunk
+  const int g = blockIdx.x - sl * geo.NG;
+  int b, h;
+  chunk_slot(geo, ch.s0 + sl, b, h);
   const int kh = geo.k[h];
   const long long bh = (long long)b * geo.H + h;
   const long long base = bh * geo.S * D;
@@ -93,6 +242,11 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
   const int32_t* row = idx + geo.row_offset(b, h, g);
   const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
   const int G = geo.G;
+  const int nB = n_buckets(geo.S);
+  const uint32_t* btab = base_tab + ((long long)sl * geo.NG + g) * nB;
+  const uint32_t* otab = off_tab + (long long)sl * (nB + 1);
+  const long long ebase = ch.edge_base[sl];   // first row of this slot in the chunk buffers
+  const uint32_t slot_rows = (uint32_t)(ch.edge_base[sl + 1] - ebase);
 
   // ---- per-group set-up: A operands of S and dP, LSE, Delta, transposed B operands in LDS
   int tok[QB];
@@ -162,8 +316,6 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
 #pragma unroll
     for (int f = 0; f < DPL; ++f) dqacc[qb][f] = floatx4{0.f, 0.f, 0.f, 0.f};
   const float c2 = scale * kLog2e;
-  float* dK = dk + base;
-  float* dV = dv + base;
 
   u32x4 kb_n[2][KS], vb_n[2][KS];   // natural K / V rows (B operands) of the current chunk
   auto load_nat = [&](int cb) {
@@ -184,12 +336,6 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     int tkey[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) tkey[e] = clamp_key(row[min(cb + 8 * lg + e, kh - 1)], geo.S);
-    // keys whose dK/dV rows this lane updates: 16kb + 4lg + j
-    int akey[2][4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) akey[kb][j] = clamp_key(row[min(cb + 16 * kb + 4 * lg + j, kh - 1)], geo.S);
 
     // ---- S = Q K^T, dP = dO V^T ; lane: key 16kb + li, members 16qb + 4lg + j
     u32x4 pa[2][NM], dsa[2][NM];
@@ -243,12 +389,26 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     // the natural K/V registers are free again: request the next chunk's rows now
     if (cb + 32 < kh) load_nat(cb + 32);
 
-    // ---- dV = P^T dO, dK = scale dS^T Q ; lane: feature 16db + li, keys 16kb + 4lg + j
+    // ---- dV = P^T dO, dK = scale dS^T Q ; lane: feature 16db + li, keys 16kb + 4lg + j.
+    // Each valid key's row goes to a fixed slot of its bucket (rows of a bucket are ordered
+    // by group, then by row position); the lane group holding the key's tile rows stores it.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      bool avalid[4];
+      long long srow = -1;
+      if (lg == 0 && cb + 16 * kb + li < kh) {
+        const int p = cb + 16 * kb + li;
+        const int key = clamp_key(row[p], geo.S);
+        const int j = key >> kBucketLog2;
+        const uint32_t rel = otab[j] + btab[j] + (uint32_t)p;
+        // rel < NG*k for ascending rows; a malformed list is dropped rather than written astray
+        if (rel < slot_rows) {
+          srow = ebase + (long long)rel;
+          keyid[srow] = key;
+        }
+      }
+      long long rows_j[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) avalid[j] = cb + 16 * kb + 4 * lg + j < kh;
+      for (int j = 0; j < 4; ++j) rows_j[j] = __shfl(srow, 4 * lg + j, 64);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         floatx4 accv = {0.f, 0.f, 0.f, 0.f}, acck = {0.f, 0.f, 0.f, 0.f};
@@ -262,10 +422,10 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (avalid[j]) {
-            const long long a = (long long)akey[kb][j] * D + 16 * db + li;
-            unsafeAtomicAdd(dV + a, accv[j]);
-            unsafeAtomicAdd(dK + a, acck[j] * scale);
+          if (rows_j[j] >= 0) {
+            float* crow = contrib + rows_j[j] * (2 * D);
+            crow[16 * db + li] = accv[j];
+            crow[D + 16 * db + li] = acck[j] * scale;
           }
         }
       }
@@ -393,24 +553,54 @@ __global__ __launch_bounds__(64) void attn_bwd_f32(
 
 }  // namespace
 
+// Workspace layout for a chunk capacity of `cs` slots and `e` rows:
+//   [rs: cs*NG*(nB+1) u32][base: cs*NG*nB u32][tot: cs*(nB+1) u32][off: cs*(nB+1) u32]
+//   [keyid: e int32][contrib: e rows of 2*d fp32], every region 256-byte aligned.
+struct WsLayout {
+  size_t rs, base, tot, off, key, contrib, total;
+};
+static WsLayout ws_layout(const Geom& geo, long long cs, long long e) {
+  auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t nb = (size_t)n_buckets(geo.S);
+  WsLayout L;
+  L.rs = 0;
+  L.base = L.rs + al(cs * geo.NG * (nb + 1) * 4);
+  L.tot = L.base + al(cs * geo.NG * nb * 4);
+  L.off = L.tot + al(cs * (nb + 1) * 4);
+  L.key = L.off + al(cs * (nb + 1) * 4);
+  L.contrib = L.key + al((size_t)e * 4);
+  L.total = L.contrib + (size_t)e * 2 * geo.d * sizeof(float);
+  return L;
+}
+
+static long long max_slot_rows(const Geom& geo) {
+  int kmax = 0;
+  for (int h = 0; h < geo.H; ++h) kmax = std::max(kmax, geo.k[h]);
+  return (long long)geo.NG * kmax;
+}
+
+size_t bwd_workspace_bytes(const Geom& geo) {
+  if (geo.dtype == DSV_FP32) return 0;
+  return ws_layout(geo, 1, max_slot_rows(geo)).total;
+}
+
 int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v, const void* o,
                     const void* d_o, const float* lse, const int32_t* idx, float scale, float* dq,
-                    float* dk, float* dv, void* stream) {
+                    float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const long long n4 = (long long)geo.B * geo.H * geo.S * geo.d / 4;
-  const int fill_blocks = (int)std::min<long long>((n4 + 255) / 256, 4096);
-  hipLaunchKernelGGL(fill_zero, dim3(fill_blocks), dim3(256), 0, st, (float4*)dk, n4);
-  hipLaunchKernelGGL(fill_zero, dim3(fill_blocks), dim3(256), 0, st, (float4*)dv, n4);
-  const dim3 grid(geo.B * geo.H * geo.NG);
-  const dim3 block(64);
   if (geo.dtype == DSV_FP32) {
+    const long long n4 = (long long)geo.B * geo.H * geo.S * geo.d / 4;
+    const int fill_blocks = (int)std::min<long long>((n4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(fill_zero, dim3(fill_blocks), dim3(256), 0, st, (float4*)dk, n4);
+    hipLaunchKernelGGL(fill_zero, dim3(fill_blocks), dim3(256), 0, st, (float4*)dv, n4);
+    const dim3 grid(geo.B * geo.H * geo.NG);
     const size_t shm = (size_t)geo.G * (2 * geo.d + 2 * 16) * sizeof(float);
 #define DSV_BWD32(DD)                                                                         \
   if (geo.d == DD) {                                                                          \
     if (shm > 65536)                                                                          \
       (void)hipFuncSetAttribute((const void*)attn_bwd_f32<DD>,                                \
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);        \
-    hipLaunchKernelGGL((attn_bwd_f32<DD>), grid, block, shm, st, (const float*)q,             \
+    hipLaunchKernelGGL((attn_bwd_f32<DD>), grid, dim3(64), shm, st, (const float*)q,          \
                        (const float*)k, (const float*)v, (const float*)o, (const float*)d_o,  \
                        lse, idx, scale, dq, dk, dv, geo);                                     \
     return (int)hipGetLastError();                                                            \
@@ -420,18 +610,69 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
 #undef DSV_BWD32
     return (int)hipErrorInvalidValue;
   }
+
+  // ---- bf16 path: chunks of (b, h) slots sized to the workspace
+  const int nslots = geo.B * geo.H;
+  const long long e1 = max_slot_rows(geo);
+  long long cs = std::min<long long>(kMaxChunk, nslots);
+  while (cs > 1 && ws_layout(geo, cs, e1).total > ws_bytes) --cs;
+  long long ecap = e1;   // largest row capacity for this slot capacity
+  {
+    const size_t per_row = 4 + 2 * (size_t)geo.d * sizeof(float);
+    const size_t fixed = ws_layout(geo, cs, 0).total;
+    if (ws_bytes > fixed) ecap = std::max<long long>(e1, (long long)((ws_bytes - fixed) / per_row) - 64);
+    while (ecap > e1 && ws_layout(geo, cs, ecap).total > ws_bytes) ecap -= 64;
+  }
+  const WsLayout L = ws_layout(geo, cs, ecap);
+  char* wsb = static_cast<char*>(ws);
+  uint32_t* rs = reinterpret_cast<uint32_t*>(wsb + L.rs);
+  uint32_t* base_tab = reinterpret_cast<uint32_t*>(wsb + L.base);
+  uint32_t* tot = reinterpret_cast<uint32_t*>(wsb + L.tot);
+  uint32_t* off = reinterpret_cast<uint32_t*>(wsb + L.off);
+  int32_t* keyid = reinterpret_cast<int32_t*>(wsb + L.key);
+  float* contrib = reinterpret_cast<float*>(wsb + L.contrib);
+  const int nB = n_buckets(geo.S);
   const int QBn = geo.G / 16;
+
+  int s0 = 0;
+  while (s0 < nslots) {
+    Chunk ch;
+    ch.s0 = s0;
+    ch.n = 0;
+    long long rows = 0;
+    while (s0 + ch.n < nslots && ch.n < cs) {
+      const int h = geo.order[(s0 + ch.n) / geo.B];
+      const long long r = (long long)geo.NG * geo.k[h];
+      if (ch.n > 0 && rows + r > ecap) break;
+      ch.edge_base[ch.n] = rows;
+      rows += r;
+      ++ch.n;
+    }
+    ch.edge_base[ch.n] = rows;
+    const int rows_waves = ch.n * geo.NG;
+    hipLaunchKernelGGL(row_bucket_starts, dim3((rows_waves + 3) / 4), dim3(256), 0, st, idx, ch,
+                       rs, geo);
+    hipLaunchKernelGGL(bucket_columns, dim3((nB + 63) / 64, ch.n), dim3(64), 0, st, rs, base_tab,
+                       tot, geo);
+    hipLaunchKernelGGL(bucket_offsets, dim3(ch.n), dim3(256), 0, st, tot, off, geo);
 #define DSV_BWD16(DD, QQ)                                                                       \
   if (geo.d == DD && QBn == QQ) {                                                               \
-    hipLaunchKernelGGL((attn_bwd_bf16<DD, QQ>), grid, block, 0, st, (const uint16_t*)q,         \
-                       (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,              \
-                       (const uint16_t*)d_o, lse, idx, scale, dq, dk, dv, geo);                 \
-    return (int)hipGetLastError();                                                              \
-  }
-  DSV_BWD16(64, 1) DSV_BWD16(64, 2) DSV_BWD16(64, 3) DSV_BWD16(64, 4)
-  DSV_BWD16(128, 1) DSV_BWD16(128, 2) DSV_BWD16(128, 3) DSV_BWD16(128, 4)
+    hipLaunchKernelGGL((attn_bwd_bf16<DD, QQ>), dim3(rows_waves), dim3(64), 0, st,              \
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,              \
+                       (const uint16_t*)o, (const uint16_t*)d_o, lse, idx, scale, dq, ch,       \
+                       base_tab, off, keyid, contrib, geo);                                     \
+    hipLaunchKernelGGL((bucket_reduce<DD>), dim3(ch.n * nB), dim3(2 * DD), 0, st, off, keyid,   \
+                       contrib, ch, dk, dv, geo);                                               \
+  } else
+    DSV_BWD16(64, 1) DSV_BWD16(64, 2) DSV_BWD16(64, 3) DSV_BWD16(64, 4)
+    DSV_BWD16(128, 1) DSV_BWD16(128, 2) DSV_BWD16(128, 3) DSV_BWD16(128, 4)
+    return (int)hipErrorInvalidValue;
 #undef DSV_BWD16
-  return (int)hipErrorInvalidValue;
+    const int e = (int)hipGetLastError();
+    if (e) return e;
+    s0 += ch.n;
+  }
+  return 0;
 }
 
 }  // namespace dsv

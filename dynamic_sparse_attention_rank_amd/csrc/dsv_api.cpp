@@ -116,8 +116,9 @@ const char* dsv_last_error(void) { return g_err; }
 
 size_t dsv_workspace_bytes(int op, const dsv_problem* p, const int32_t* k_per_head) {
   if (op < DSV_OP_TOPK || op > DSV_OP_BWD) return (size_t)-1;
-  if (validate_problem(p, k_per_head, nullptr) != DSV_OK) return (size_t)-1;
-  return 0;
+  Geom geo;
+  if (validate_problem(p, k_per_head, &geo) != DSV_OK) return (size_t)-1;
+  return op == DSV_OP_BWD ? bwd_workspace_bytes(geo) : 0;
 }
 
 int64_t dsv_idx_elems(const dsv_problem* p, const int32_t* k_per_head) {
@@ -161,7 +162,10 @@ int dsv_validate(int op, const dsv_problem* p, const int32_t* k_per_head, int re
   if (!ptrs || n_ptrs != n) return fail(DSV_ERR_NULL, "op %d expects %d pointers", op, n);
   for (int i = 0; i < n; ++i)
     if ((st = check_ptr(ptrs[i], names[i], aligns[i])) != DSV_OK) return st;
-  (void)ws_bytes;  // every op needs 0 bytes of workspace
+  const size_t need = op == DSV_OP_BWD ? bwd_workspace_bytes(geo) : 0;
+  if (ws_bytes < need)
+    return fail(DSV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",
+                ws_bytes, need);
   return DSV_OK;
 }
 
@@ -197,13 +201,14 @@ int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, cons
                         const void* o, const void* d_o, const float* lse, const int32_t* idx,
                         const int32_t* k_per_head, float scale, float* dq, float* dk, float* dv,
                         void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
   const void* ptrs[] = {q, k, v, o, d_o, lse, idx, dq, dk, dv};
   int st = dsv_validate(DSV_OP_BWD, p, k_per_head, DSV_GROUP_SUM, ptrs, 10, ws_bytes);
   if (st != DSV_OK) return st;
   Geom geo;
   validate_problem(p, k_per_head, &geo);
-  int e = launch_attn_bwd(geo, q, k, v, o, d_o, lse, idx, scale, dq, dk, dv, stream);
+  if (bwd_workspace_bytes(geo) > 0 && (st = check_ptr(ws, "ws", 256)) != DSV_OK) return st;
+  int e = launch_attn_bwd(geo, q, k, v, o, d_o, lse, idx, scale, dq, dk, dv, ws, ws_bytes,
+                          stream);
   if (e) return fail(DSV_ERR_HIP, "backward launch failed (hipError %d)", e);
   return DSV_OK;
 }

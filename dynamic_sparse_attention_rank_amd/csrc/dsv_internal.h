@@ -41,6 +41,10 @@ int launch_attn_fwd(const Geom& geo, const void* q, const void* k, const void* v
                     const int32_t* idx, float scale, void* o, float* lse, void* stream);
 int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v, const void* o,
                     const void* d_o, const float* lse, const int32_t* idx, float scale, float* dq,
-                    float* dk, float* dv, void* stream);
+                    float* dk, float* dv, void* ws, size_t ws_bytes, void* stream);
+// Minimum device workspace of the backward (bf16 path): room for the heaviest (b, h) slot's
+// edge rows (one fp32 dV|dK row of 2d floats + one key index per (group, selected key)) and
+// its bucket offsets. Larger workspaces let one launch cover several (b, h) slots.
+size_t bwd_workspace_bytes(const Geom& geo);
 
 }  // namespace dsv

@@ -42,7 +42,8 @@ def test_validation_accepts_the_workloads():
     p = mid()
     assert dsv.validate(dsv.DSV_OP_TOPK, p, [6554] * 24, [FAKE] * 3) == 0
     assert dsv.validate(dsv.DSV_OP_FWD, p, [6554] * 24, [FAKE] * 6) == 0
-    assert dsv.validate(dsv.DSV_OP_BWD, p, [6554] * 24, [FAKE] * 10) == 0
+    need = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, [6554] * 24)
+    assert dsv.validate(dsv.DSV_OP_BWD, p, [6554] * 24, [FAKE] * 10, ws_bytes=need) == 0
     tiny = dsv.problem(1, 2, 4, 16, 16, 64, 16, (2, 2, 4), "fp32")
     assert dsv.validate(dsv.DSV_OP_FWD, tiny, [128, 128], [FAKE] * 6) == 0
 
@@ -101,8 +102,23 @@ def test_entry_points_reject_before_any_hip_call():
 def test_workspace_and_idx_layout_agree_with_oracle():
     p = dsv.problem(2, 3, 4, 8, 8, 64, 16, (2, 2, 4), "bf16")
     ks = [5, 17, 3]
-    for op in (dsv.DSV_OP_TOPK, dsv.DSV_OP_FWD, dsv.DSV_OP_BWD):
+    for op in (dsv.DSV_OP_TOPK, dsv.DSV_OP_FWD):
         assert dsv.workspace_bytes(op, p, ks) == 0
+    # backward (bf16), for one (b, h) slot: per-row bucket entry points NG x (nB+1) u32,
+    # per-group bucket bases NG x nB u32, bucket totals and offsets (nB+1) u32 each, then one
+    # key index and one 2d-float dV|dK row per edge of the heaviest slot (NG * max k)
+    al = lambda x: -(-x // 256) * 256
+    nb = -(-p.seq // 64)
+    NG = p.n_groups
+    e = NG * max(ks)
+    need = (al(NG * (nb + 1) * 4) + al(NG * nb * 4) + 2 * al((nb + 1) * 4) + al(e * 4)
+            + e * 2 * 64 * 4)
+    assert dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks) == need
+    pf = dsv.problem(2, 3, 4, 8, 8, 64, 16, (2, 2, 4), "fp32")
+    assert dsv.workspace_bytes(dsv.DSV_OP_BWD, pf, ks) == 0
+    assert dsv.validate(dsv.DSV_OP_BWD, p, ks, [FAKE] * 10, ws_bytes=need) == 0
+    assert dsv.STATUS[dsv.validate(dsv.DSV_OP_BWD, p, ks, [FAKE] * 10, ws_bytes=need - 1)] \
+        == "DSV_ERR_WORKSPACE"
     NG = p.n_groups
     assert dsv.idx_elems(p, ks) == 2 * NG * sum(ks)
     offs = otopk.idx_row_offsets(2, 3, NG, ks)
