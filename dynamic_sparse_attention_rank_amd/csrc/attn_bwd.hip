@@ -22,7 +22,10 @@
 //     atomics on this chip sustain only ~0.33 T adds/s, so the rows are not added in place:
 //     the key range is cut into 64-key buckets, every edge has a fixed row slot in its bucket
 //     (rows ordered by group, then by row position; the slots come from two small prefix
-//     passes over the index rows) and writes its dV|dK row there, and a reduce kernel then
+//     passes over the index rows) and writes its dV|dK row there as 16-bit integers with one
+//     fp32 step per half (the step is an a-priori bound / 32000: |dV| <= sum P * max|dO|,
+//     |dK| <= scale * sum|dS| * max|Q|, so each entry is off by at most 1.6e-5 of that bound,
+//     far below the bf16 rounding of the P and dS MFMA operands), and a reduce kernel then
 //     sums each bucket's rows in LDS (one workgroup per bucket, one lane per feature, no
 //     atomics) and writes every dK/dV row of the bucket exactly once. Heads are processed in
 //     chunks sized to the caller's workspace.
@@ -53,6 +56,13 @@ __device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, i
 constexpr int kBucketLog2 = 6;   // 64 keys per dK/dV bucket
 constexpr int kBucket = 1 << kBucketLog2;
 constexpr int kMaxChunk = 64;    // (b, h) slots per chunk
+// dV|dK rows are stored as int16 * step with |entry| <= bound; 32000 of 32767 levels leave a
+// margin for the fp32 accumulation and bf16 operand rounding inside the bound.
+constexpr float kQLevels = 32000.f;
+
+__device__ __forceinline__ int16_t quantize16(float x) {
+  return (int16_t)fminf(fmaxf(rintf(x), -32767.f), 32767.f);
+}
 
 __host__ __device__ inline int n_buckets(int S) { return (S + kBucket - 1) / kBucket; }
 
@@ -141,58 +151,65 @@ __global__ __launch_bounds__(256) void bucket_offsets(const uint32_t* __restrict
   if (threadIdx.x == 255) o[nB] = part[255];
 }
 
-// Sum each bucket's rows: one workgroup per (slot, bucket), thread t owns feature column t of
-// the 2D-wide dV|dK rows, accumulators for the bucket's 64 keys in LDS (plain read-add-write,
-// no two threads share a word), then every key row of the bucket is written once.
+__global__ void fill_zero(float4* __restrict__ p, long long n4) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Sum each bucket's rows: one workgroup per (slot, bucket, half) where half 0 is dV and half 1
+// is dK; thread t owns feature t of that half, the bucket's 64 key rows accumulate in LDS
+// (plain read-add-write, no two threads share a word; 32 KB, so several workgroups share a
+// CU), 16 rows are requested per iteration, and every key row of the bucket is written once.
 template <int D>
-__global__ __launch_bounds__(2 * D) void bucket_reduce(const uint32_t* __restrict__ off,
-                                                       const int32_t* __restrict__ keyid,
-                                                       const float* __restrict__ contrib, Chunk ch,
-                                                       float* __restrict__ dk,
-                                                       float* __restrict__ dv, Geom geo) {
-  constexpr int W = 2 * D;
-  __shared__ float acc[kBucket * W];
+__global__ __launch_bounds__(D) void bucket_reduce(const uint32_t* __restrict__ off,
+                                                   const int32_t* __restrict__ keyid,
+                                                   const int16_t* __restrict__ contrib,
+                                                   const float2* __restrict__ rstep, Chunk ch,
+                                                   float* __restrict__ dk, float* __restrict__ dv,
+                                                   Geom geo) {
+  constexpr int W = 2 * D;   // entries per stored row (dV | dK)
+  constexpr int U = 16;      // rows per iteration
+  __shared__ float acc[kBucket * D];
   const int nB = n_buckets(geo.S);
-  const int sl = blockIdx.x / nB;
-  const int j = blockIdx.x - sl * nB;
+  const int half = blockIdx.x & 1;
+  const int bj = blockIdx.x >> 1;
+  const int sl = bj / nB;
+  const int j = bj - sl * nB;
   int b, h;
   chunk_slot(geo, ch.s0 + sl, b, h);
   const long long bh = (long long)b * geo.H + h;
   const int t = threadIdx.x;
-  for (int i = t; i < kBucket * W; i += W) acc[i] = 0.f;
+  for (int i = t; i < kBucket * D; i += D) acc[i] = 0.f;
   __syncthreads();
   const uint32_t* o = off + (long long)sl * (nB + 1);
   const long long nrows = ch.edge_base[sl + 1] - ch.edge_base[sl];
   const long long r0 = ch.edge_base[sl] + std::min<long long>(o[j], nrows);
   const long long r1 = ch.edge_base[sl] + std::min<long long>(std::max<long long>(o[j + 1], o[j]), nrows);
   const int key0 = j * kBucket;
+  const int16_t* col = contrib + half * D + t;
   long long r = r0;
-  for (; r + 8 <= r1; r += 8) {
-    int kk[8];
-    float val[8];
+  for (; r + U <= r1; r += U) {
+    int kk[U];
+    float val[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       kk[u] = min(max(keyid[r + u] - key0, 0), kBucket - 1);
-      val[u] = contrib[(r + u) * W + t];
+      const float2 st = rstep[r + u];
+      val[u] = (float)col[(r + u) * W] * (half ? st.y : st.x);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[kk[u] * W + t] += val[u];
+    for (int u = 0; u < U; ++u) acc[kk[u] * D + t] += val[u];
   }
   for (; r < r1; ++r) {
     const int kk = min(max(keyid[r] - key0, 0), kBucket - 1);
-    acc[kk * W + t] += contrib[r * W + t];
+    const float2 st = rstep[r];
+    acc[kk * D + t] += (float)col[r * W] * (half ? st.y : st.x);
   }
   __syncthreads();
   const int nk = min(kBucket, geo.S - key0);
-  float* out = (t < D ? dv : dk) + bh * geo.S * D;
-  const int c = t < D ? t : t - D;
-  for (int l = 0; l < nk; ++l) out[(long long)(key0 + l) * D + c] = acc[l * W + t];
-}
-
-__global__ void fill_zero(float4* __restrict__ p, long long n4) {
-  const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
-    p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float* out = (half ? dk : dv) + bh * geo.S * D + (long long)key0 * D;
+  for (int l = 0; l < nk; ++l) out[(long long)l * D + t] = acc[l * D + t];
 }
 
 // LDS layout of the transposed operands: for feature block db (16 features) and k-step m
@@ -217,7 +234,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
     const int32_t* __restrict__ idx, float scale, float* __restrict__ dq, Chunk ch,
     const uint32_t* __restrict__ base_tab, const uint32_t* __restrict__ off_tab,
-    int32_t* __restrict__ keyid, float* __restrict__ contrib, Geom geo) {
+    int32_t* __restrict__ keyid, int16_t* __restrict__ contrib, float2* __restrict__ rstep,
+    Geom geo) {
   constexpr int QBP = (QB + 1) & ~1;   // query blocks padded to whole 32-query k-steps
   constexpr int NM = QBP / 2;
   constexpr int KS = D / 32;
@@ -280,6 +298,22 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       lds.lse2[qb * 16 + li] = lse[bh * geo.S + tok[qb]] * kLog2e;
     }
   }
+  // max |dO| and max |Q| over the group: bounds for the 16-bit storage of dV|dK rows
+  float max_do = 0.f, max_q = 0.f;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        max_do = fmaxf(max_do, fmaxf(fabsf(bf16_lo(doa[qb][ks][w])), fabsf(bf16_hi(doa[qb][ks][w]))));
+        max_q = fmaxf(max_q, fmaxf(fabsf(bf16_lo(qa[qb][ks][w])), fabsf(bf16_hi(qa[qb][ks][w]))));
+      }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    max_do = wave_xor_max(max_do, m);
+    max_q = wave_xor_max(max_q, m);
+  }
   if (QB < QBP && lg == 0) {   // padded members: no contribution (P = 0 through lse2 = +inf)
     lds.delta[QB * 16 + li] = 0.f;
     lds.lse2[QB * 16 + li] = INFINITY;
@@ -339,6 +373,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
 
     // ---- S = Q K^T, dP = dO V^T ; lane: key 16kb + li, members 16qb + 4lg + j
     u32x4 pa[2][NM], dsa[2][NM];
+    float colp[2], colds[2];   // sum_n P[n, key] and sum_n |dS[n, key]| for key 16kb + li
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bool kvalid = cb + 16 * kb + li < kh;
@@ -365,6 +400,22 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       for (int qb = QB; qb < QBP; ++qb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) pv[qb][j] = dsv_[qb][j] = 0.f;
+      {
+        float cp = 0.f, cd = 0.f;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            cp += pv[qb][j];
+            cd += fabsf(dsv_[qb][j]);
+          }
+        cp = wave_xor_sum(cp, 16);
+        cp = wave_xor_sum(cp, 32);
+        cd = wave_xor_sum(cd, 16);
+        cd = wave_xor_sum(cd, 32);
+        colp[kb] = cp;
+        colds[kb] = cd;
+      }
       // A operands of P^T dO / dS^T Q: element e <-> member 16(2m + e/4) + 4lg + e%4
 #pragma unroll
       for (int m = 0; m < NM; ++m) {
@@ -390,11 +441,17 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     if (cb + 32 < kh) load_nat(cb + 32);
 
     // ---- dV = P^T dO, dK = scale dS^T Q ; lane: feature 16db + li, keys 16kb + 4lg + j.
-    // Each valid key's row goes to a fixed slot of its bucket (rows of a bucket are ordered
-    // by group, then by row position); the lane group holding the key's tile rows stores it.
+    // Each valid key's row goes to a fixed slot of its bucket (rows of a bucket are ordered by
+    // group, then by row position). The row is stored as 16-bit integers times one fp32 step
+    // per half: |dV[d]| <= sum_n P * max|dO| and |dK[d]| <= scale * sum_n |dS| * max|Q| bound
+    // every entry, so the step is that bound / kQLevels (error <= step / 2 per entry).
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       long long srow = -1;
+      const float bound_v = colp[kb] * max_do;
+      const float bound_k = colds[kb] * max_q * scale;
+      const float inv_v = bound_v > 0.f ? kQLevels / bound_v : 0.f;
+      const float inv_k = bound_k > 0.f ? kQLevels / bound_k : 0.f;
       if (lg == 0 && cb + 16 * kb + li < kh) {
         const int p = cb + 16 * kb + li;
         const int key = clamp_key(row[p], geo.S);
@@ -404,11 +461,17 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         if (rel < slot_rows) {
           srow = ebase + (long long)rel;
           keyid[srow] = key;
+          rstep[srow] = make_float2(bound_v / kQLevels, bound_k / kQLevels);
         }
       }
       long long rows_j[4];
+      float iv[4], ik[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) rows_j[j] = __shfl(srow, 4 * lg + j, 64);
+      for (int j = 0; j < 4; ++j) {
+        rows_j[j] = __shfl(srow, 4 * lg + j, 64);
+        iv[j] = __shfl(inv_v, 4 * lg + j, 64);
+        ik[j] = __shfl(inv_k, 4 * lg + j, 64) * scale;
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         floatx4 accv = {0.f, 0.f, 0.f, 0.f}, acck = {0.f, 0.f, 0.f, 0.f};
@@ -423,9 +486,9 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if (rows_j[j] >= 0) {
-            float* crow = contrib + rows_j[j] * (2 * D);
-            crow[16 * db + li] = accv[j];
-            crow[D + 16 * db + li] = acck[j] * scale;
+            int16_t* crow = contrib + rows_j[j] * (2 * D);
+            crow[16 * db + li] = quantize16(accv[j] * iv[j]);
+            crow[D + 16 * db + li] = quantize16(acck[j] * ik[j]);
           }
         }
       }
@@ -555,9 +618,10 @@ __global__ __launch_bounds__(64) void attn_bwd_f32(
 
 // Workspace layout for a chunk capacity of `cs` slots and `e` rows:
 //   [rs: cs*NG*(nB+1) u32][base: cs*NG*nB u32][tot: cs*(nB+1) u32][off: cs*(nB+1) u32]
-//   [keyid: e int32][contrib: e rows of 2*d fp32], every region 256-byte aligned.
+//   [keyid: e int32][step: e float2][contrib: e rows of 2*d int16], every region
+//   256-byte aligned.
 struct WsLayout {
-  size_t rs, base, tot, off, key, contrib, total;
+  size_t rs, base, tot, off, key, step, contrib, total;
 };
 static WsLayout ws_layout(const Geom& geo, long long cs, long long e) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -568,8 +632,9 @@ static WsLayout ws_layout(const Geom& geo, long long cs, long long e) {
   L.tot = L.base + al(cs * geo.NG * nb * 4);
   L.off = L.tot + al(cs * (nb + 1) * 4);
   L.key = L.off + al(cs * (nb + 1) * 4);
-  L.contrib = L.key + al((size_t)e * 4);
-  L.total = L.contrib + (size_t)e * 2 * geo.d * sizeof(float);
+  L.step = L.key + al((size_t)e * 4);
+  L.contrib = L.step + al((size_t)e * 8);
+  L.total = L.contrib + (size_t)e * 2 * geo.d * sizeof(int16_t);
   return L;
 }
 
@@ -618,7 +683,7 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
   while (cs > 1 && ws_layout(geo, cs, e1).total > ws_bytes) --cs;
   long long ecap = e1;   // largest row capacity for this slot capacity
   {
-    const size_t per_row = 4 + 2 * (size_t)geo.d * sizeof(float);
+    const size_t per_row = 4 + 8 + 2 * (size_t)geo.d * sizeof(int16_t);
     const size_t fixed = ws_layout(geo, cs, 0).total;
     if (ws_bytes > fixed) ecap = std::max<long long>(e1, (long long)((ws_bytes - fixed) / per_row) - 64);
     while (ecap > e1 && ws_layout(geo, cs, ecap).total > ws_bytes) ecap -= 64;
@@ -630,7 +695,8 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
   uint32_t* tot = reinterpret_cast<uint32_t*>(wsb + L.tot);
   uint32_t* off = reinterpret_cast<uint32_t*>(wsb + L.off);
   int32_t* keyid = reinterpret_cast<int32_t*>(wsb + L.key);
-  float* contrib = reinterpret_cast<float*>(wsb + L.contrib);
+  float2* rstep = reinterpret_cast<float2*>(wsb + L.step);
+  int16_t* contrib = reinterpret_cast<int16_t*>(wsb + L.contrib);
   const int nB = n_buckets(geo.S);
   const int QBn = geo.G / 16;
 
@@ -660,9 +726,9 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
     hipLaunchKernelGGL((attn_bwd_bf16<DD, QQ>), dim3(rows_waves), dim3(64), 0, st,              \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,              \
                        (const uint16_t*)o, (const uint16_t*)d_o, lse, idx, scale, dq, ch,       \
-                       base_tab, off, keyid, contrib, geo);                                     \
-    hipLaunchKernelGGL((bucket_reduce<DD>), dim3(ch.n * nB), dim3(2 * DD), 0, st, off, keyid,   \
-                       contrib, ch, dk, dv, geo);                                               \
+                       base_tab, off, keyid, contrib, rstep, geo);                              \
+    hipLaunchKernelGGL((bucket_reduce<DD>), dim3(ch.n * nB * 2), dim3(DD), 0, st, off, keyid,   \
+                       contrib, rstep, ch, dk, dv, geo);                                        \
   } else
     DSV_BWD16(64, 1) DSV_BWD16(64, 2) DSV_BWD16(64, 3) DSV_BWD16(64, 4)
     DSV_BWD16(128, 1) DSV_BWD16(128, 2) DSV_BWD16(128, 3) DSV_BWD16(128, 4)
