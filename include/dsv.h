@@ -31,7 +31,8 @@
  *   descriptor is a device pointer. The library allocates nothing and keeps no state:
  *   calls are re-entrant and thread-safe. `stream` is a hipStream_t (NULL = legacy default
  *   stream). Calls are asynchronous: inputs must stay unchanged, and outputs unread, until
- *   the stream has passed the call. Outputs are overwritten, never accumulated.
+ *   the stream has passed the call. Outputs are overwritten, never accumulated. A
+ *   workspace belongs to one call at a time: calls in flight together need separate ones.
  *
  * Errors
  *   Arguments are validated before anything is enqueued. On a non-OK status nothing has been
@@ -78,8 +79,10 @@ typedef struct {
   int32_t dtype;                 /* dsv_dtype of Q,K,V,O,dO,Q_lr,K_lr */
 } dsv_problem;
 
-/* Bytes of device workspace `op` needs for this problem (0 today for every op; the argument
- * pair ws/ws_bytes is kept so that later versions can use scratch without an ABI change).
+/* Minimum bytes of device workspace `op` needs for this problem. DSV_OP_TOPK and DSV_OP_FWD
+ * need none (their ws may be NULL). DSV_OP_BWD on the bf16 path needs the per-edge dV|dK
+ * staging rows of one (b,h) head (NG*k_max*(4*d + 12) bytes plus small per-bucket tables); a
+ * larger workspace lets one launch cover several heads. The fp32 path needs none.
  * Returns (size_t)-1 if the problem is invalid. */
 size_t dsv_workspace_bytes(int op, const dsv_problem* p, const int32_t* k_per_head);
 
@@ -122,11 +125,17 @@ int dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, cons
  * low-rank factors).
  *   o, d_o : [B][H][S][d] device, dtype p->dtype (o is the forward output).
  *   lse    : forward LSE.
- *   dq,dk,dv : [B][H][S][d] fp32 device (written; dk/dv are cleared by the call, then every
- *              key receives the sum over all groups that selected it).
+ *   dq,dk,dv : [B][H][S][d] fp32 device (written in full: every key receives the sum over
+ *              all groups that selected it, 0 if none did).
+ *   ws       : device, 256-byte aligned, at least dsv_workspace_bytes(DSV_OP_BWD, ...) bytes
+ *              (bf16 path); owned by the caller, contents on entry ignored, clobbered.
  * With P = exp(scale*q.k - LSE), Delta_n = dO_n.O_n, dS = P*(dO.v - Delta):
  *   dQ_n = scale*sum_m dS[n,m] k_m,  dK_m = scale*sum_n dS[n,m] q_n,  dV_m = sum_n P[n,m] dO_n.
- * dK/dV are summed with fp32 atomics: their low bits depend on the summation order. */
+ * bf16 path: each (group, selected key) edge writes its dV and dK rows to a fixed slot of the
+ * key's 64-key bucket in ws, as 16-bit integers with one fp32 step per row half (the step is
+ * an a-priori bound of the half / 32000); a second kernel sums each bucket's slots in a fixed
+ * order. dK/dV are therefore bitwise reproducible from run to run. The stream is used for
+ * several launches per call (heads are processed in chunks that fit ws). */
 int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,
                         const void* o, const void* d_o, const float* lse, const int32_t* idx,
                         const int32_t* k_per_head, float scale, float* dq, float* dk, float* dv,
