@@ -18,17 +18,17 @@
 //     are built once per group in LDS.
 //   * dQ^T += K^T dS^T needs dS with queries in lanes: dS goes through a 4 KB LDS tile; K rows
 //     are re-gathered one full row per 16 lanes and transposed in registers (v_perm_b32).
-//   * dK/dV: each (group, selected key) edge yields one fp32 row of dV and one of dK. fp32
-//     atomics on this chip sustain only ~0.33 T adds/s, so the rows are not added in place:
-//     the key range is cut into 64-key buckets, every edge has a fixed row slot in its bucket
-//     (rows ordered by group, then by row position; the slots come from two small prefix
-//     passes over the index rows) and writes its dV|dK row there as 16-bit integers with one
-//     fp32 step per half (the step is an a-priori bound / 32000: |dV| <= sum P * max|dO|,
-//     |dK| <= scale * sum|dS| * max|Q|, so each entry is off by at most 1.6e-5 of that bound,
-//     far below the bf16 rounding of the P and dS MFMA operands), and a reduce kernel then
-//     sums each bucket's rows in LDS (one workgroup per bucket, one lane per feature, no
-//     atomics) and writes every dK/dV row of the bucket exactly once. Heads are processed in
-//     chunks sized to the caller's workspace.
+//   * dK/dV: each (group, selected key) edge yields one row of dV and one of dK, summed over
+//     all groups that selected the key. fp32 atomics on this chip sustain only ~0.33 T adds/s,
+//     so the rows are not added in place. The edge (g, p) owns staging row g*k + p, so each
+//     wave writes its rows contiguously, as 16-bit integers with one fp32 step per half (the
+//     step is an a-priori bound / 32000: |dV| <= sum P * max|dO|, |dK| <= scale * sum|dS| *
+//     max|Q|, so each entry is off by at most 1.6e-5 of that bound, far below the bf16
+//     rounding of the P and dS MFMA operands). Small pre-passes list, for every 64-key
+//     bucket, its edges in (group, position) order; a reduce kernel then sums each bucket's
+//     rows in LDS (one wave per bucket and half, one row per instruction, no atomics) and
+//     writes every dK/dV row of the bucket exactly once, so dK/dV are bitwise reproducible.
+//     Heads are processed in chunks sized to the caller's workspace.
 // fp32 path: plain fp32 FMA (one lane per query, then one lane per feature for dK/dV); it
 // exists for fp32 inputs and is not tuned.
 #include <math.h>
@@ -102,25 +102,23 @@ __global__ __launch_bounds__(256) void row_bucket_starts(const int32_t* __restri
   for (int j = jl + 1 + lane; j <= nB; j += 64) r[j] = (uint32_t)kh;
 }
 
-// Column pass: for bucket j of slot sl, base[g][j] = (rows of bucket j owned by groups < g)
-// - rs[g][j], so that the row of position p (key in bucket j) is off[j] + base[g][j] + p.
-// tot[j] = rows of bucket j. One thread per bucket column, groups walked in order.
-__global__ __launch_bounds__(64) void bucket_columns(const uint32_t* __restrict__ rs,
-                                                     uint32_t* __restrict__ base,
-                                                     uint32_t* __restrict__ tot, Geom geo) {
+// Row-run length of bucket j in row g: the entry points lie in [0, k] whatever the row holds
+// (every j is written), but only an ascending row makes them non-decreasing; a decreasing pair
+// counts as an empty run so that a malformed row cannot produce a negative length.
+__device__ __forceinline__ uint32_t run_len(uint32_t a, uint32_t b) { return b > a ? b - a : 0u; }
+
+// tot[j] = staging rows whose key lies in bucket j (all groups of the slot). One thread per
+// bucket column, groups walked in order.
+__global__ __launch_bounds__(64) void bucket_totals(const uint32_t* __restrict__ rs,
+                                                    uint32_t* __restrict__ tot, Geom geo) {
   const int nB = n_buckets(geo.S);
   const int sl = blockIdx.y;
   const int j = blockIdx.x * 64 + threadIdx.x;
   if (j >= nB) return;
   const uint32_t* r = rs + (long long)sl * geo.NG * (nB + 1);
-  uint32_t* bs = base + (long long)sl * geo.NG * nB;
   uint32_t run = 0;
-  for (int g = 0; g < geo.NG; ++g) {
-    const uint32_t s0 = r[(long long)g * (nB + 1) + j];
-    const uint32_t s1 = r[(long long)g * (nB + 1) + j + 1];
-    bs[(long long)g * nB + j] = run - s0;   // modular arithmetic: adding p gives the row
-    run += s1 - s0;
-  }
+  for (int g = 0; g < geo.NG; ++g)
+    run += run_len(r[(long long)g * (nB + 1) + j], r[(long long)g * (nB + 1) + j + 1]);
   tot[(long long)sl * (nB + 1) + j] = run;
 }
 
@@ -151,71 +149,145 @@ __global__ __launch_bounds__(256) void bucket_offsets(const uint32_t* __restrict
   if (threadIdx.x == 255) o[nB] = part[255];
 }
 
+// Bucket-ordered edge list: perm[off[j] + i], i < tot[j], holds the edges (g, p) whose key
+// lies in bucket j, as the slot-relative staging row g*k + p, ordered by group, then by
+// position. One wave per (slot, bucket); 64 groups per step, positions from a wave scan.
+__global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ rs,
+                                                  const uint32_t* __restrict__ off, Chunk ch,
+                                                  uint32_t* __restrict__ perm, Geom geo) {
+  const int nB = n_buckets(geo.S);
+  const int sl = blockIdx.x / nB;
+  const int j = blockIdx.x - sl * nB;
+  const int lane = threadIdx.x;
+  int b, h;
+  chunk_slot(geo, ch.s0 + sl, b, h);
+  const uint32_t kh = (uint32_t)geo.k[h];
+  const uint32_t slot_rows = (uint32_t)(ch.edge_base[sl + 1] - ch.edge_base[sl]);
+  const uint32_t* r = rs + (long long)sl * geo.NG * (nB + 1);
+  uint32_t* pm = perm + ch.edge_base[sl];
+  uint32_t pos0 = off[(long long)sl * (nB + 1) + j];
+  for (int g0 = 0; g0 < geo.NG; g0 += 64) {
+    const int g = g0 + lane;
+    uint32_t a = 0, len = 0;
+    if (g < geo.NG) {
+      a = r[(long long)g * (nB + 1) + j];
+      len = run_len(a, r[(long long)g * (nB + 1) + j + 1]);
+    }
+    uint32_t incl = len;   // inclusive prefix over lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += y;
+    }
+    const uint32_t pos = pos0 + incl - len;
+    const uint32_t e0 = (uint32_t)g * kh + a;
+    for (uint32_t i = 0; i < len; ++i)
+      if (pos + i < slot_rows) pm[pos + i] = e0 + i;   // a malformed row is dropped
+    pos0 += __shfl(incl, 63, 64);
+  }
+}
+
 __global__ void fill_zero(float4* __restrict__ p, long long n4) {
   const long long stride = (long long)gridDim.x * blockDim.x;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// Sum each bucket's rows: one workgroup per (slot, bucket, half) where half 0 is dV and half 1
-// is dK; thread t owns feature t of that half, the bucket's 64 key rows accumulate in LDS
-// (plain read-add-write, no two threads share a word; 32 KB, so several workgroups share a
-// CU), 16 rows are requested per iteration, and every key row of the bucket is written once.
+// Sum each bucket's staging rows: one wave per (slot, bucket, half), half 0 = dV, 1 = dK.
+// Lane l owns features (D/64)*l .. of the half; the bucket's 64 key rows accumulate in LDS.
+// Each step takes 64 entries of the bucket's edge list (edge row, key, step: one per lane),
+// then walks them one row per instruction, so no two lanes ever touch the same LDS word and
+// rows with equal keys are added in list order. 32 row loads are in flight per wave. Every
+// key row of the bucket is then written once (zero where no group selected the key).
 template <int D>
-__global__ __launch_bounds__(D) void bucket_reduce(const uint32_t* __restrict__ off,
-                                                   const int32_t* __restrict__ keyid,
-                                                   const int16_t* __restrict__ contrib,
-                                                   const float2* __restrict__ rstep, Chunk ch,
+__global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__ off,
+                                                   const uint32_t* __restrict__ perm,
+                                                   const int32_t* __restrict__ idx,
+                                                   const float2* __restrict__ rstep,
+                                                   const int16_t* __restrict__ cv,
+                                                   const int16_t* __restrict__ ck, Chunk ch,
                                                    float* __restrict__ dk, float* __restrict__ dv,
                                                    Geom geo) {
-  constexpr int W = 2 * D;   // entries per stored row (dV | dK)
-  constexpr int U = 16;      // rows per iteration
-  __shared__ float acc[kBucket * D];
+  constexpr int FPL = D / 64;   // features per lane
+  constexpr int U = 32;         // rows in flight
+  __shared__ __attribute__((aligned(16))) float acc[kBucket * D];
   const int nB = n_buckets(geo.S);
   const int half = blockIdx.x & 1;
   const int bj = blockIdx.x >> 1;
   const int sl = bj / nB;
   const int j = bj - sl * nB;
+  const int lane = threadIdx.x;
   int b, h;
   chunk_slot(geo, ch.s0 + sl, b, h);
   const long long bh = (long long)b * geo.H + h;
-  const int t = threadIdx.x;
-  for (int i = t; i < kBucket * D; i += D) acc[i] = 0.f;
+  for (int i = lane; i < kBucket * D / 4; i += 64)
+    reinterpret_cast<float4*>(acc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   __syncthreads();
+  const long long eb = ch.edge_base[sl];
+  const long long nrows = ch.edge_base[sl + 1] - eb;
   const uint32_t* o = off + (long long)sl * (nB + 1);
-  const long long nrows = ch.edge_base[sl + 1] - ch.edge_base[sl];
-  const long long r0 = ch.edge_base[sl] + std::min<long long>(o[j], nrows);
-  const long long r1 = ch.edge_base[sl] + std::min<long long>(std::max<long long>(o[j + 1], o[j]), nrows);
+  const long long s0 = std::min<long long>(o[j], nrows);
+  const long long s1 = std::min<long long>(std::max<long long>(o[j + 1], o[j]), nrows);
+  const uint32_t* pm = perm + eb;
+  const int32_t* keys = idx + geo.row_offset(b, h, 0);   // key of slot row e is keys[e]
+  const int16_t* src = (half ? ck : cv) + eb * D + FPL * lane;
   const int key0 = j * kBucket;
-  const int16_t* col = contrib + half * D + t;
-  long long r = r0;
-  for (; r + U <= r1; r += U) {
-    int kk[U];
-    float val[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      kk[u] = min(max(keyid[r + u] - key0, 0), kBucket - 1);
-      const float2 st = rstep[r + u];
-      val[u] = (float)col[(r + u) * W] * (half ? st.y : st.x);
+  for (long long r0 = s0; r0 < s1; r0 += 64) {
+    const int n = (int)std::min<long long>(64, s1 - r0);
+    // lanes past the end read row 0 of the slot and add it with step 0
+    uint32_t e = 0;
+    int kk = 0;
+    float sc = 0.f;
+    if (lane < n) {
+      e = std::min<uint32_t>(pm[r0 + lane], (uint32_t)(nrows - 1));
+      kk = min(max(clamp_key(keys[e], geo.S) - key0, 0), kBucket - 1);
+      const float2 st = rstep[eb + e];
+      sc = half ? st.y : st.x;
     }
+    for (int u0 = 0; u0 < n; u0 += U) {
+      uint32_t x[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) acc[kk[u] * D + t] += val[u];
-  }
-  for (; r < r1; ++r) {
-    const int kk = min(max(keyid[r] - key0, 0), kBucket - 1);
-    const float2 st = rstep[r];
-    acc[kk * D + t] += (float)col[r * W] * (half ? st.y : st.x);
+      for (int u = 0; u < U; ++u) {
+        const uint32_t eu = __builtin_amdgcn_readlane(e, u0 + u);
+        if constexpr (FPL == 2)
+          x[u] = *reinterpret_cast<const uint32_t*>(src + (long long)eu * D);
+        else
+          x[u] = (uint16_t)src[(long long)eu * D];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ku = __builtin_amdgcn_readlane(kk, u0 + u);
+        const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), u0 + u));
+        float* a = acc + ku * D + FPL * lane;
+        if constexpr (FPL == 2) {
+          float2 w = *reinterpret_cast<float2*>(a);
+          w.x += su * (float)(int16_t)(x[u] & 0xffffu);
+          w.y += su * (float)(int16_t)(x[u] >> 16);
+          *reinterpret_cast<float2*>(a) = w;
+        } else {
+          a[0] += su * (float)(int16_t)x[u];
+        }
+      }
+    }
   }
   __syncthreads();
   const int nk = min(kBucket, geo.S - key0);
-  float* out = (half ? dk : dv) + bh * geo.S * D + (long long)key0 * D;
-  for (int l = 0; l < nk; ++l) out[(long long)l * D + t] = acc[l * D + t];
+  float* out = (half ? dk : dv) + bh * geo.S * D + (long long)key0 * D + FPL * lane;
+  for (int l = 0; l < nk; ++l) {
+    if constexpr (FPL == 2)
+      *reinterpret_cast<float2*>(out + (long long)l * D) =
+          *reinterpret_cast<const float2*>(acc + l * D + FPL * lane);
+    else
+      out[(long long)l * D] = acc[l * D + lane];
+  }
 }
 
-// LDS layout of the transposed operands: for feature block db (16 features) and k-step m
-// (32 queries), lane (lg, li) reads 8 queries (lg, e), e = 0..7 <-> query
-// 16*(2m + e/4) + 4*lg + (e%4), of feature 16*db + li. Stored as [db][m][lane][8] bf16 so that
-// the read is one conflict-free 16-byte access per lane.
+// LDS layout of the transposed operands: for output tile db and k-step m (32 queries), lane
+// (lg, li) reads 8 queries (lg, e), e = 0..7 <-> query 16*(2m + e/4) + 4*lg + (e%4), of
+// feature (D/16)*li + db. Tile db thus covers features db, db + D/16, ..., and after all tiles
+// lane li holds the D/16 consecutive features (D/16)*li .. of its keys, which it stores with
+// one 16-byte (D = 128) or 8-byte (D = 64) write. Stored as [db][m][lane][8] bf16 so that the
+// read is one conflict-free 16-byte access per lane.
 template <int D, int QBP>
 struct BwdLds {
   static constexpr int NDB = D / 16;
@@ -233,9 +305,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
     const int32_t* __restrict__ idx, float scale, float* __restrict__ dq, Chunk ch,
-    const uint32_t* __restrict__ base_tab, const uint32_t* __restrict__ off_tab,
-    int32_t* __restrict__ keyid, int16_t* __restrict__ contrib, float2* __restrict__ rstep,
-    Geom geo) {
+    int16_t* __restrict__ cv, int16_t* __restrict__ ck, float2* __restrict__ rstep, Geom geo) {
   constexpr int QBP = (QB + 1) & ~1;   // query blocks padded to whole 32-query k-steps
   constexpr int NM = QBP / 2;
   constexpr int KS = D / 32;
@@ -260,11 +330,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
   const int32_t* row = idx + geo.row_offset(b, h, g);
   const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
   const int G = geo.G;
-  const int nB = n_buckets(geo.S);
-  const uint32_t* btab = base_tab + ((long long)sl * geo.NG + g) * nB;
-  const uint32_t* otab = off_tab + (long long)sl * (nB + 1);
-  const long long ebase = ch.edge_base[sl];   // first row of this slot in the chunk buffers
-  const uint32_t slot_rows = (uint32_t)(ch.edge_base[sl + 1] - ebase);
+  // staging row of edge (g, p): the slot's first row + g*k + p (index order)
+  const long long grow = ch.edge_base[sl] + (long long)g * kh;
 
   // ---- per-group set-up: A operands of S and dP, LSE, Delta, transposed B operands in LDS
   int tok[QB];
@@ -332,8 +399,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       td[e] = 0;
       if (mem < G) {
         const int n = gg.token(g, mem);
-        tq[e] = Q[(long long)n * D + 16 * db + lli];
-        td[e] = d_o[base + (long long)n * D + 16 * db + lli];
+        tq[e] = Q[(long long)n * D + NDB * lli + db];
+        td[e] = d_o[base + (long long)n * D + NDB * lli + db];
       }
     }
 #pragma unroll
@@ -440,38 +507,28 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     // the natural K/V registers are free again: request the next chunk's rows now
     if (cb + 32 < kh) load_nat(cb + 32);
 
-    // ---- dV = P^T dO, dK = scale dS^T Q ; lane: feature 16db + li, keys 16kb + 4lg + j.
-    // Each valid key's row goes to a fixed slot of its bucket (rows of a bucket are ordered by
-    // group, then by row position). The row is stored as 16-bit integers times one fp32 step
-    // per half: |dV[d]| <= sum_n P * max|dO| and |dK[d]| <= scale * sum_n |dS| * max|Q| bound
-    // every entry, so the step is that bound / kQLevels (error <= step / 2 per entry).
+    // ---- dV = P^T dO, dK = scale dS^T Q ; lane: keys 16kb + 4lg + j, features
+    // (D/16)*li + db. Each valid key's dV and dK rows go to its edge's staging row as 16-bit
+    // integers times one fp32 step per half: |dV[d]| <= sum_n P * max|dO| and
+    // |dK[d]| <= scale * sum_n |dS| * max|Q| bound every entry, so the step is that bound /
+    // kQLevels (error <= step / 2 per entry).
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      long long srow = -1;
       const float bound_v = colp[kb] * max_do;
       const float bound_k = colds[kb] * max_q * scale;
       const float inv_v = bound_v > 0.f ? kQLevels / bound_v : 0.f;
       const float inv_k = bound_k > 0.f ? kQLevels / bound_k : 0.f;
-      if (lg == 0 && cb + 16 * kb + li < kh) {
-        const int p = cb + 16 * kb + li;
-        const int key = clamp_key(row[p], geo.S);
-        const int j = key >> kBucketLog2;
-        const uint32_t rel = otab[j] + btab[j] + (uint32_t)p;
-        // rel < NG*k for ascending rows; a malformed list is dropped rather than written astray
-        if (rel < slot_rows) {
-          srow = ebase + (long long)rel;
-          keyid[srow] = key;
-          rstep[srow] = make_float2(bound_v / kQLevels, bound_k / kQLevels);
-        }
-      }
-      long long rows_j[4];
+      const int p0 = cb + 16 * kb;   // row position of key 16kb + 0
+      if (lg == 0 && p0 + li < kh)
+        rstep[grow + p0 + li] = make_float2(bound_v / kQLevels, bound_k / kQLevels);
       float iv[4], ik[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        rows_j[j] = __shfl(srow, 4 * lg + j, 64);
         iv[j] = __shfl(inv_v, 4 * lg + j, 64);
         ik[j] = __shfl(inv_k, 4 * lg + j, 64) * scale;
       }
+      // packed 16-bit entries: word w of key 4lg + j holds features NDB*li + 2w, + 2w + 1
+      uint32_t wv[4][NDB / 2], wk[4][NDB / 2];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         floatx4 accv = {0.f, 0.f, 0.f, 0.f}, acck = {0.f, 0.f, 0.f, 0.f};
@@ -485,10 +542,28 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (rows_j[j] >= 0) {
-            int16_t* crow = contrib + rows_j[j] * (2 * D);
-            crow[16 * db + li] = quantize16(accv[j] * iv[j]);
-            crow[D + 16 * db + li] = quantize16(acck[j] * ik[j]);
+          const uint32_t qv = (uint16_t)quantize16(accv[j] * iv[j]);
+          const uint32_t qk = (uint16_t)quantize16(acck[j] * ik[j]);
+          if (db & 1) {
+            wv[j][db >> 1] |= qv << 16;
+            wk[j][db >> 1] |= qk << 16;
+          } else {
+            wv[j][db >> 1] = qv;
+            wk[j][db >> 1] = qk;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int p = p0 + 4 * lg + j;
+        if (p < kh) {
+          const long long off = (grow + p) * D + NDB * li;
+          if constexpr (D == 128) {
+            *reinterpret_cast<u32x4*>(cv + off) = u32x4{wv[j][0], wv[j][1], wv[j][2], wv[j][3]};
+            *reinterpret_cast<u32x4*>(ck + off) = u32x4{wk[j][0], wk[j][1], wk[j][2], wk[j][3]};
+          } else {
+            *reinterpret_cast<u32x2*>(cv + off) = u32x2{wv[j][0], wv[j][1]};
+            *reinterpret_cast<u32x2*>(ck + off) = u32x2{wk[j][0], wk[j][1]};
           }
         }
       }
@@ -616,25 +691,24 @@ __global__ __launch_bounds__(64) void attn_bwd_f32(
 
 }  // namespace
 
-// Workspace layout for a chunk capacity of `cs` slots and `e` rows:
-//   [rs: cs*NG*(nB+1) u32][base: cs*NG*nB u32][tot: cs*(nB+1) u32][off: cs*(nB+1) u32]
-//   [keyid: e int32][step: e float2][contrib: e rows of 2*d int16], every region
-//   256-byte aligned.
+// Workspace layout for a chunk capacity of `cs` slots and `e` staging rows:
+//   [rs: cs*NG*(nB+1) u32][tot: cs*(nB+1) u32][off: cs*(nB+1) u32][perm: e u32]
+//   [step: e float2][dV rows: e*d int16][dK rows: e*d int16], every region 256-byte aligned.
 struct WsLayout {
-  size_t rs, base, tot, off, key, step, contrib, total;
+  size_t rs, tot, off, perm, step, cv, ck, total;
 };
 static WsLayout ws_layout(const Geom& geo, long long cs, long long e) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t nb = (size_t)n_buckets(geo.S);
   WsLayout L;
   L.rs = 0;
-  L.base = L.rs + al(cs * geo.NG * (nb + 1) * 4);
-  L.tot = L.base + al(cs * geo.NG * nb * 4);
+  L.tot = L.rs + al(cs * geo.NG * (nb + 1) * 4);
   L.off = L.tot + al(cs * (nb + 1) * 4);
-  L.key = L.off + al(cs * (nb + 1) * 4);
-  L.step = L.key + al((size_t)e * 4);
-  L.contrib = L.step + al((size_t)e * 8);
-  L.total = L.contrib + (size_t)e * 2 * geo.d * sizeof(int16_t);
+  L.perm = L.off + al(cs * (nb + 1) * 4);
+  L.step = L.perm + al((size_t)e * 4);
+  L.cv = L.step + al((size_t)e * 8);
+  L.ck = L.cv + al((size_t)e * geo.d * sizeof(int16_t));
+  L.total = L.ck + (size_t)e * geo.d * sizeof(int16_t);
   return L;
 }
 
@@ -691,12 +765,12 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
   const WsLayout L = ws_layout(geo, cs, ecap);
   char* wsb = static_cast<char*>(ws);
   uint32_t* rs = reinterpret_cast<uint32_t*>(wsb + L.rs);
-  uint32_t* base_tab = reinterpret_cast<uint32_t*>(wsb + L.base);
   uint32_t* tot = reinterpret_cast<uint32_t*>(wsb + L.tot);
   uint32_t* off = reinterpret_cast<uint32_t*>(wsb + L.off);
-  int32_t* keyid = reinterpret_cast<int32_t*>(wsb + L.key);
+  uint32_t* perm = reinterpret_cast<uint32_t*>(wsb + L.perm);
   float2* rstep = reinterpret_cast<float2*>(wsb + L.step);
-  int16_t* contrib = reinterpret_cast<int16_t*>(wsb + L.contrib);
+  int16_t* cv = reinterpret_cast<int16_t*>(wsb + L.cv);
+  int16_t* ck = reinterpret_cast<int16_t*>(wsb + L.ck);
   const int nB = n_buckets(geo.S);
   const int QBn = geo.G / 16;
 
@@ -718,17 +792,17 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
     const int rows_waves = ch.n * geo.NG;
     hipLaunchKernelGGL(row_bucket_starts, dim3((rows_waves + 3) / 4), dim3(256), 0, st, idx, ch,
                        rs, geo);
-    hipLaunchKernelGGL(bucket_columns, dim3((nB + 63) / 64, ch.n), dim3(64), 0, st, rs, base_tab,
-                       tot, geo);
+    hipLaunchKernelGGL(bucket_totals, dim3((nB + 63) / 64, ch.n), dim3(64), 0, st, rs, tot, geo);
     hipLaunchKernelGGL(bucket_offsets, dim3(ch.n), dim3(256), 0, st, tot, off, geo);
+    hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64), 0, st, rs, off, ch, perm, geo);
 #define DSV_BWD16(DD, QQ)                                                                       \
   if (geo.d == DD && QBn == QQ) {                                                               \
     hipLaunchKernelGGL((attn_bwd_bf16<DD, QQ>), dim3(rows_waves), dim3(64), 0, st,              \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,              \
-                       (const uint16_t*)o, (const uint16_t*)d_o, lse, idx, scale, dq, ch,       \
-                       base_tab, off, keyid, contrib, rstep, geo);                              \
-    hipLaunchKernelGGL((bucket_reduce<DD>), dim3(ch.n * nB * 2), dim3(DD), 0, st, off, keyid,   \
-                       contrib, rstep, ch, dk, dv, geo);                                        \
+                       (const uint16_t*)o, (const uint16_t*)d_o, lse, idx, scale, dq, ch, cv,   \
+                       ck, rstep, geo);                                                         \
+    hipLaunchKernelGGL((bucket_reduce<DD>), dim3(ch.n * nB * 2), dim3(64), 0, st, off, perm,    \
+                       idx, rstep, cv, ck, ch, dk, dv, geo);                                    \
   } else
     DSV_BWD16(64, 1) DSV_BWD16(64, 2) DSV_BWD16(64, 3) DSV_BWD16(64, 4)
     DSV_BWD16(128, 1) DSV_BWD16(128, 2) DSV_BWD16(128, 3) DSV_BWD16(128, 4)

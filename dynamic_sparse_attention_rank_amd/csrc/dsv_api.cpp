@@ -162,6 +162,13 @@ int dsv_validate(int op, const dsv_problem* p, const int32_t* k_per_head, int re
   if (!ptrs || n_ptrs != n) return fail(DSV_ERR_NULL, "op %d expects %d pointers", op, n);
   for (int i = 0; i < n; ++i)
     if ((st = check_ptr(ptrs[i], names[i], aligns[i])) != DSV_OK) return st;
+  if (op == DSV_OP_BWD && geo.dtype == DSV_BF16) {
+    int kmax = 0;
+    for (int h = 0; h < geo.H; ++h) kmax = std::max(kmax, geo.k[h]);
+    if ((long long)geo.NG * kmax >= (1LL << 31))
+      return fail(DSV_ERR_UNSUPPORTED, "backward: NG * max k = %lld edges per head exceeds 2^31",
+                  (long long)geo.NG * kmax);
+  }
   const size_t need = op == DSV_OP_BWD ? bwd_workspace_bytes(geo) : 0;
   if (ws_bytes < need)
     return fail(DSV_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed",

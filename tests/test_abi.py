@@ -105,15 +105,15 @@ def test_workspace_and_idx_layout_agree_with_oracle():
     for op in (dsv.DSV_OP_TOPK, dsv.DSV_OP_FWD):
         assert dsv.workspace_bytes(op, p, ks) == 0
     # backward (bf16), for one (b, h) slot: per-row bucket entry points NG x (nB+1) u32,
-    # per-group bucket bases NG x nB u32, bucket totals and offsets (nB+1) u32 each, then per
-    # edge of the heaviest slot (NG * max k): a key index, two fp32 steps and a 2d-entry int16
-    # dV|dK row
+    # bucket totals and offsets (nB+1) u32 each, then per edge of the heaviest slot
+    # (NG * max k): a bucket-list entry (u32), two fp32 steps, a d-entry int16 dV row and a
+    # d-entry int16 dK row
     al = lambda x: -(-x // 256) * 256
     nb = -(-p.seq // 64)
     NG = p.n_groups
     e = NG * max(ks)
-    need = (al(NG * (nb + 1) * 4) + al(NG * nb * 4) + 2 * al((nb + 1) * 4) + al(e * 4)
-            + al(e * 8) + e * 2 * 64 * 2)
+    need = (al(NG * (nb + 1) * 4) + 2 * al((nb + 1) * 4) + al(e * 4) + al(e * 8)
+            + al(e * 64 * 2) + e * 64 * 2)
     assert dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks) == need
     pf = dsv.problem(2, 3, 4, 8, 8, 64, 16, (2, 2, 4), "fp32")
     assert dsv.workspace_bytes(dsv.DSV_OP_BWD, pf, ks) == 0
