@@ -24,7 +24,7 @@
 //     wave writes its rows contiguously, as 16-bit integers with one fp32 step per half (the
 //     step is an a-priori bound / 32000: |dV| <= sum P * max|dO|, |dK| <= scale * sum|dS| *
 //     max|Q|, so each entry is off by at most 1.6e-5 of that bound, far below the bf16
-//     rounding of the P and dS MFMA operands). Small pre-passes list, for every 64-key
+//     rounding of the P and dS MFMA operands). Small pre-passes list, for every 32-key
 //     bucket, its edges in (group, position) order; a reduce kernel then sums each bucket's
 //     rows in LDS (one wave per bucket and half, one row per instruction, no atomics) and
 //     writes every dK/dV row of the bucket exactly once, so dK/dV are bitwise reproducible.
@@ -53,7 +53,9 @@ __device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, i
 }
 
 
-constexpr int kBucketLog2 = 6;   // 64 keys per dK/dV bucket
+// 32 keys per dK/dV bucket: the reduce keeps a bucket's rows in LDS (32 x d fp32 per wave),
+// so smaller buckets let more reduce waves share a CU
+constexpr int kBucketLog2 = 5;
 constexpr int kBucket = 1 << kBucketLog2;
 constexpr int kMaxChunk = 64;    // (b, h) slots per chunk
 // dV|dK rows are stored as int16 * step with |entry| <= bound; 32000 of 32767 levels leave a
@@ -107,19 +109,20 @@ __global__ __launch_bounds__(256) void row_bucket_starts(const int32_t* __restri
 // counts as an empty run so that a malformed row cannot produce a negative length.
 __device__ __forceinline__ uint32_t run_len(uint32_t a, uint32_t b) { return b > a ? b - a : 0u; }
 
-// tot[j] = staging rows whose key lies in bucket j (all groups of the slot). One thread per
-// bucket column, groups walked in order.
+// tot[j] = staging rows whose key lies in bucket j (all groups of the slot). One wave per
+// (slot, bucket), lanes over groups.
 __global__ __launch_bounds__(64) void bucket_totals(const uint32_t* __restrict__ rs,
                                                     uint32_t* __restrict__ tot, Geom geo) {
   const int nB = n_buckets(geo.S);
-  const int sl = blockIdx.y;
-  const int j = blockIdx.x * 64 + threadIdx.x;
-  if (j >= nB) return;
+  const int sl = blockIdx.x / nB;
+  const int j = blockIdx.x - sl * nB;
   const uint32_t* r = rs + (long long)sl * geo.NG * (nB + 1);
   uint32_t run = 0;
-  for (int g = 0; g < geo.NG; ++g)
+  for (int g = threadIdx.x; g < geo.NG; g += 64)
     run += run_len(r[(long long)g * (nB + 1) + j], r[(long long)g * (nB + 1) + j + 1]);
-  tot[(long long)sl * (nB + 1) + j] = run;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) run += __shfl_xor(run, m, 64);
+  if (threadIdx.x == 0) tot[(long long)sl * (nB + 1) + j] = run;
 }
 
 // off[j] = exclusive prefix of tot over buckets (off[nB] = rows of the slot).
@@ -194,7 +197,7 @@ __global__ void fill_zero(float4* __restrict__ p, long long n4) {
 }
 
 // Sum each bucket's staging rows: one wave per (slot, bucket, half), half 0 = dV, 1 = dK.
-// Lane l owns features (D/64)*l .. of the half; the bucket's 64 key rows accumulate in LDS.
+// Lane l owns features (D/64)*l .. of the half; the bucket's key rows accumulate in LDS.
 // Each step takes 64 entries of the bucket's edge list (edge row, key, step: one per lane),
 // then walks them one row per instruction, so no two lanes ever touch the same LDS word and
 // rows with equal keys are added in list order. 32 row loads are in flight per wave. Every
@@ -558,12 +561,17 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         const int p = p0 + 4 * lg + j;
         if (p < kh) {
           const long long off = (grow + p) * D + NDB * li;
+          // streaming (non-temporal) writes: the rows are read once, by the reduce
           if constexpr (D == 128) {
-            *reinterpret_cast<u32x4*>(cv + off) = u32x4{wv[j][0], wv[j][1], wv[j][2], wv[j][3]};
-            *reinterpret_cast<u32x4*>(ck + off) = u32x4{wk[j][0], wk[j][1], wk[j][2], wk[j][3]};
+            __builtin_nontemporal_store(u32x4{wv[j][0], wv[j][1], wv[j][2], wv[j][3]},
+                                        reinterpret_cast<u32x4*>(cv + off));
+            __builtin_nontemporal_store(u32x4{wk[j][0], wk[j][1], wk[j][2], wk[j][3]},
+                                        reinterpret_cast<u32x4*>(ck + off));
           } else {
-            *reinterpret_cast<u32x2*>(cv + off) = u32x2{wv[j][0], wv[j][1]};
-            *reinterpret_cast<u32x2*>(ck + off) = u32x2{wk[j][0], wk[j][1]};
+            __builtin_nontemporal_store(u32x2{wv[j][0], wv[j][1]},
+                                        reinterpret_cast<u32x2*>(cv + off));
+            __builtin_nontemporal_store(u32x2{wk[j][0], wk[j][1]},
+                                        reinterpret_cast<u32x2*>(ck + off));
           }
         }
       }
@@ -792,7 +800,7 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
     const int rows_waves = ch.n * geo.NG;
     hipLaunchKernelGGL(row_bucket_starts, dim3((rows_waves + 3) / 4), dim3(256), 0, st, idx, ch,
                        rs, geo);
-    hipLaunchKernelGGL(bucket_totals, dim3((nB + 63) / 64, ch.n), dim3(64), 0, st, rs, tot, geo);
+    hipLaunchKernelGGL(bucket_totals, dim3(ch.n * nB), dim3(64), 0, st, rs, tot, geo);
     hipLaunchKernelGGL(bucket_offsets, dim3(ch.n), dim3(256), 0, st, tot, off, geo);
     hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64), 0, st, rs, off, ch, perm, geo);
 #define DSV_BWD16(DD, QQ)                                                                       \

@@ -109,7 +109,7 @@ def test_workspace_and_idx_layout_agree_with_oracle():
     # (NG * max k): a bucket-list entry (u32), two fp32 steps, a d-entry int16 dV row and a
     # d-entry int16 dK row
     al = lambda x: -(-x // 256) * 256
-    nb = -(-p.seq // 64)
+    nb = -(-p.seq // 32)
     NG = p.n_groups
     e = NG * max(ks)
     need = (al(NG * (nb + 1) * 4) + 2 * al((nb + 1) * 4) + al(e * 4) + al(e * 8)
