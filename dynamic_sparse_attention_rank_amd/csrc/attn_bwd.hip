@@ -61,9 +61,14 @@ constexpr int kMaxChunk = 64;    // (b, h) slots per chunk
 // dV|dK rows are stored as int16 * step with |entry| <= bound; 32000 of 32767 levels leave a
 // margin for the fp32 accumulation and bf16 operand rounding inside the bound.
 constexpr float kQLevels = 32000.f;
+constexpr float kPkScale = kQLevels / 32767.f;   // v_cvt_pknorm_i16_f32 multiplies by 32767
 
-__device__ __forceinline__ int16_t quantize16(float x) {
-  return (int16_t)fminf(fmaxf(rintf(x), -32767.f), 32767.f);
+// kPkScale / bound rounded down to a power of two (clamped to [2^-126, 2^100]); 0 if bound is
+// not positive.
+__device__ __forceinline__ float pow2_scale(float bound) {
+  if (!(bound > 0.f)) return 0.f;
+  const float x = fminf(fmaxf(kPkScale * __builtin_amdgcn_rcpf(bound), 1.17549435e-38f), 1.2676506e30f);
+  return __uint_as_float(__float_as_uint(x) & 0xff800000u);
 }
 
 __host__ __device__ inline int n_buckets(int S) { return (S + kBucket - 1) / kBucket; }
@@ -285,22 +290,34 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
   }
 }
 
-// LDS layout of the transposed operands: for output tile db and k-step m (32 queries), lane
-// (lg, li) reads 8 queries (lg, e), e = 0..7 <-> query 16*(2m + e/4) + 4*lg + (e%4), of
-// feature (D/16)*li + db. Tile db thus covers features db, db + D/16, ..., and after all tiles
-// lane li holds the D/16 consecutive features (D/16)*li .. of its keys, which it stores with
-// one 16-byte (D = 128) or 8-byte (D = 64) write. Stored as [db][m][lane][8] bf16 so that the
-// read is one conflict-free 16-byte access per lane.
-template <int D, int QBP>
+// LDS copy of the group's Q and dO rows (bf16, [member][feature]). Chunk c (8 features,
+// 16 bytes) of row r is stored at chunk position c ^ (r mod D/8): the 16-byte reads of the
+// S / dP operands (16 rows, one chunk) then hit distinct banks, and the transposed 8-byte
+// reads of ds_read_b64_tr_b16 stay inside one chunk. Rows past the group size are zero.
+template <int D>
 struct BwdLds {
-  static constexpr int NDB = D / 16;
-  static constexpr int NM = QBP / 2;
-  uint16_t qt[NDB * NM * 64 * 8];
-  uint16_t dot[NDB * NM * 64 * 8];
+  uint16_t qn[64 * D];
+  uint16_t dn[64 * D];
   uint16_t ds[64 * 40];   // dS tile [query][key], 32 keys + 8 pad per row
   float lse2[64] __attribute__((aligned(16)));    // LSE * log2(e) per group member
   float delta[64] __attribute__((aligned(16)));   // Delta per group member
 };
+
+// element offset of feature `col` (col % 4 == 0) of row r in the swizzled layout
+template <int D>
+__device__ __forceinline__ int swz(int r, int col) {
+  return r * D + ((((col >> 3) ^ r) & (D / 8 - 1)) << 3) + (col & 7);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane block, lane j passes the address of 4 elements
+// (row R0 + j/4, columns C0 + 4(j%4)) and lane i receives column C0 + i of rows R0 .. R0 + 3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((__attribute__((address_space(3))) const uint16_t*)p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 template <int D, int QB>
 __global__ __launch_bounds__(64) void attn_bwd_bf16(
@@ -313,8 +330,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
   constexpr int NM = QBP / 2;
   constexpr int KS = D / 32;
   constexpr int NDB = D / 16;
-  constexpr int DPL = D / 16;
-  using L = BwdLds<D, QBP>;
+  constexpr int CPR = D / 8;           // 16-byte chunks per row
+  using L = BwdLds<D>;
   __shared__ __attribute__((aligned(16))) L lds;
 
   const int lane = threadIdx.x;
@@ -336,89 +353,51 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
   // staging row of edge (g, p): the slot's first row + g*k + p (index order)
   const long long grow = ch.edge_base[sl] + (long long)g * kh;
 
-  // ---- per-group set-up: A operands of S and dP, LSE, Delta, transposed B operands in LDS
-  int tok[QB];
-  u32x4 qa[QB][KS], doa[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    tok[qb] = gg.token(g, qb * 16 + li);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qa[qb][ks] = ld16(Q + (long long)tok[qb] * D + ks * 32 + 8 * lg);
-      doa[qb][ks] = ld16(d_o + base + (long long)tok[qb] * D + ks * 32 + 8 * lg);
-    }
-  }
-  // Delta_n = dO_n . O_n: lane (lg, li) covers features 32ks + 8lg .. of member 16qb + li
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float acc = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4 ov = ld16(o + base + (long long)tok[qb] * D + ks * 32 + 8 * lg);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc = fmaf(bf16_lo(doa[qb][ks][w]), bf16_lo(ov[w]), acc);
-        acc = fmaf(bf16_hi(doa[qb][ks][w]), bf16_hi(ov[w]), acc);
-      }
-    }
-    acc = wave_xor_sum(acc, 16);
-    acc = wave_xor_sum(acc, 32);
-    if (lg == 0) {
-      lds.delta[qb * 16 + li] = acc;
-      lds.lse2[qb * 16 + li] = lse[bh * geo.S + tok[qb]] * kLog2e;
-    }
-  }
-  // max |dO| and max |Q| over the group: bounds for the 16-bit storage of dV|dK rows
+  // ---- per-group set-up: Q and dO rows into LDS, Delta = dO.O, LSE, max |dO| and max |Q|
+  // (the bounds of the 16-bit dV|dK staging rows). CPR lanes per row, one chunk each.
   float max_do = 0.f, max_q = 0.f;
+  {
+    const int rr = lane / CPR, c = lane % CPR;
+    for (int r0 = 0; r0 < 16 * QBP; r0 += 64 / CPR) {
+      const int r = r0 + rr;
+      u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = qv;
+      float dacc = 0.f;
+      int n = 0;
+      if (r < G) {
+        n = gg.token(g, r);
+        qv = ld16(Q + (long long)n * D + 8 * c);
+        dv4 = ld16(d_o + base + (long long)n * D + 8 * c);
+        const u32x4 ov = ld16(o + base + (long long)n * D + 8 * c);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        max_do = fmaxf(max_do, fmaxf(fabsf(bf16_lo(doa[qb][ks][w])), fabsf(bf16_hi(doa[qb][ks][w]))));
-        max_q = fmaxf(max_q, fmaxf(fabsf(bf16_lo(qa[qb][ks][w])), fabsf(bf16_hi(qa[qb][ks][w]))));
+        for (int w = 0; w < 4; ++w) {
+          dacc = fmaf(bf16_lo(dv4[w]), bf16_lo(ov[w]), dacc);
+          dacc = fmaf(bf16_hi(dv4[w]), bf16_hi(ov[w]), dacc);
+          max_do = fmaxf(max_do, fmaxf(fabsf(bf16_lo(dv4[w])), fabsf(bf16_hi(dv4[w]))));
+          max_q = fmaxf(max_q, fmaxf(fabsf(bf16_lo(qv[w])), fabsf(bf16_hi(qv[w]))));
+        }
       }
+      *reinterpret_cast<u32x4*>(&lds.qn[swz<D>(r, 8 * c)]) = qv;
+      *reinterpret_cast<u32x4*>(&lds.dn[swz<D>(r, 8 * c)]) = dv4;
+#pragma unroll
+      for (int m = 1; m < CPR; m <<= 1) dacc += __shfl_xor(dacc, m, 64);
+      if (c == 0) {   // padded members: no contribution (P = 0 through lse2 = +inf)
+        lds.delta[r] = r < G ? dacc : 0.f;
+        lds.lse2[r] = r < G ? lse[bh * geo.S + n] * kLog2e : INFINITY;
+      }
+    }
+  }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
     max_do = wave_xor_max(max_do, m);
     max_q = wave_xor_max(max_q, m);
   }
-  if (QB < QBP && lg == 0) {   // padded members: no contribution (P = 0 through lse2 = +inf)
-    lds.delta[QB * 16 + li] = 0.f;
-    lds.lse2[QB * 16 + li] = INFINITY;
-  }
-  // transposed operands: entry (db, m, lane', e) = X[member(m, lane', e)][16 db + li']
-  for (int i = lane; i < NDB * NM * 64; i += 64) {
-    const int ln = i & 63;
-    const int m = (i >> 6) % NM;
-    const int db = (i >> 6) / NM;
-    const int llg = ln >> 4, lli = ln & 15;
-    uint16_t tq[8], td[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int mem = 16 * (2 * m + e / 4) + 4 * llg + (e & 3);
-      tq[e] = 0;
-      td[e] = 0;
-      if (mem < G) {
-        const int n = gg.token(g, mem);
-        tq[e] = Q[(long long)n * D + NDB * lli + db];
-        td[e] = d_o[base + (long long)n * D + NDB * lli + db];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      lds.qt[i * 8 + e] = tq[e];
-      lds.dot[i * 8 + e] = td[e];
-    }
-  }
   __syncthreads();
 
-  floatx4 dqacc[QB][DPL];
+  floatx4 dqacc[QB][NDB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int f = 0; f < DPL; ++f) dqacc[qb][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < NDB; ++f) dqacc[qb][f] = floatx4{0.f, 0.f, 0.f, 0.f};
   const float c2 = scale * kLog2e;
 
   u32x4 kb_n[2][KS], vb_n[2][KS];   // natural K / V rows (B operands) of the current chunk
@@ -435,15 +414,23 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
   };
   load_nat(0);
 
-  for (int cb = 0; cb < kh; cb += 32) {
-    // K rows for the dQ operand: keys 8lg + e of the chunk, features DPL*li ..
-    int tkey[8];
+  // 0/1 selection operands: sel[h] as the B operand of a 16x16x32 MFMA maps contraction slot
+  // (lg, e) <-> feature 32ks + 8lg + e to output column li iff 8lg + e == 16h + li, so
+  // A x sel[h] copies features 32ks + 16h .. + 15 of the A rows into the C layout (exact).
+  u32x4 sel[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tkey[e] = clamp_key(row[min(cb + 8 * lg + e, kh - 1)], geo.S);
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = (8 * lg + 2 * w == 16 * hh + li) ? 0x3f80u : 0u;
+      const uint32_t hi = (8 * lg + 2 * w + 1 == 16 * hh + li) ? 0x3f80u : 0u;
+      sel[hh][w] = lo | (hi << 16);
+    }
 
-    // ---- S = Q K^T, dP = dO V^T ; lane: key 16kb + li, members 16qb + 4lg + j
+  for (int cb = 0; cb < kh; cb += 32) {
+    // ---- S = Q K^T, dP = dO V^T ; lane: key 16kb + li, members 16qb + 4lg + j. The A
+    // operands (member 16qb + li, features 32ks + 8lg ..) are 16-byte LDS row reads.
     u32x4 pa[2][NM], dsa[2][NM];
-    float colp[2], colds[2];   // sum_n P[n, key] and sum_n |dS[n, key]| for key 16kb + li
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bool kvalid = cb + 16 * kb + li < kh;
@@ -453,15 +440,16 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         floatx4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s = mfma_bf16(qa[qb][ks], kb_n[kb][ks], s);
-          dp = mfma_bf16(doa[qb][ks], vb_n[kb][ks], dp);
+          const int off = swz<D>(qb * 16 + li, 32 * ks + 8 * lg);
+          s = mfma_bf16(*reinterpret_cast<const u32x4*>(&lds.qn[off]), kb_n[kb][ks], s);
+          dp = mfma_bf16(*reinterpret_cast<const u32x4*>(&lds.dn[off]), vb_n[kb][ks], dp);
         }
         // LSE / Delta of the members this tile gives the lane: 16qb + 4lg + j
         const floatx4 l2 = *reinterpret_cast<const floatx4*>(&lds.lse2[qb * 16 + 4 * lg]);
         const floatx4 dl = *reinterpret_cast<const floatx4*>(&lds.delta[qb * 16 + 4 * lg]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = kvalid ? exp2f(s[j] * c2 - l2[j]) : 0.f;
+          const float p = kvalid ? __builtin_amdgcn_exp2f(fmaf(s[j], c2, -l2[j])) : 0.f;
           pv[qb][j] = p;
           dsv_[qb][j] = p * (dp[j] - dl[j]);
         }
@@ -470,6 +458,14 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       for (int qb = QB; qb < QBP; ++qb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) pv[qb][j] = dsv_[qb][j] = 0.f;
+      // The dV and dK rows of this chunk's edges are staged as 16-bit integers times one fp32
+      // step per half. |dV[d]| <= sum_n P * max|dO| and |dK[d]| <= scale * sum_n |dS| * max|Q|
+      // bound every entry of the key's rows. The lane's key is 16kb + li: its P and dS are
+      // multiplied by sv, sk = kQLevels / (32767 * bound) rounded down to a power of two
+      // before they become bf16 MFMA operands (a power of two commutes with the bf16 rounding,
+      // so the operands are exactly the rounded P and dS, scaled), the products then lie in
+      // [-1, 1] and v_cvt_pknorm_i16_f32 quantizes two of them per instruction: the key's
+      // rows use between 16000 and 32000 of the 32767 levels, error <= step / 2 per entry.
       {
         float cp = 0.f, cd = 0.f;
 #pragma unroll
@@ -483,22 +479,27 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         cp = wave_xor_sum(cp, 32);
         cd = wave_xor_sum(cd, 16);
         cd = wave_xor_sum(cd, 32);
-        colp[kb] = cp;
-        colds[kb] = cd;
-      }
-      // A operands of P^T dO / dS^T Q: element e <-> member 16(2m + e/4) + 4lg + e%4
+        const float sv = pow2_scale(cp * max_do);
+        const float sk = pow2_scale(cd * max_q);   // dK = scale * (sum dS q): scale in the step
+        if (lg == 0 && kvalid)
+          rstep[grow + cb + 16 * kb + li] =
+              make_float2(sv > 0.f ? 1.f / (32767.f * sv) : 0.f,
+                          sk > 0.f ? scale / (32767.f * sk) : 0.f);
+        // B operands of dO^T P / Q^T dS: column li <-> key, slot (lg, e) <-> member
+        // 16(2m + e/4) + 4lg + e%4
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        pa[kb][m][0] = pack_bf16(pv[2 * m][0], pv[2 * m][1]);
-        pa[kb][m][1] = pack_bf16(pv[2 * m][2], pv[2 * m][3]);
-        pa[kb][m][2] = pack_bf16(pv[2 * m + 1][0], pv[2 * m + 1][1]);
-        pa[kb][m][3] = pack_bf16(pv[2 * m + 1][2], pv[2 * m + 1][3]);
-        dsa[kb][m][0] = pack_bf16(dsv_[2 * m][0], dsv_[2 * m][1]);
-        dsa[kb][m][1] = pack_bf16(dsv_[2 * m][2], dsv_[2 * m][3]);
-        dsa[kb][m][2] = pack_bf16(dsv_[2 * m + 1][0], dsv_[2 * m + 1][1]);
-        dsa[kb][m][3] = pack_bf16(dsv_[2 * m + 1][2], dsv_[2 * m + 1][3]);
+        for (int m = 0; m < NM; ++m) {
+          pa[kb][m][0] = pack_bf16(pv[2 * m][0] * sv, pv[2 * m][1] * sv);
+          pa[kb][m][1] = pack_bf16(pv[2 * m][2] * sv, pv[2 * m][3] * sv);
+          pa[kb][m][2] = pack_bf16(pv[2 * m + 1][0] * sv, pv[2 * m + 1][1] * sv);
+          pa[kb][m][3] = pack_bf16(pv[2 * m + 1][2] * sv, pv[2 * m + 1][3] * sv);
+          dsa[kb][m][0] = pack_bf16(dsv_[2 * m][0] * sk, dsv_[2 * m][1] * sk);
+          dsa[kb][m][1] = pack_bf16(dsv_[2 * m][2] * sk, dsv_[2 * m][3] * sk);
+          dsa[kb][m][2] = pack_bf16(dsv_[2 * m + 1][0] * sk, dsv_[2 * m + 1][1] * sk);
+          dsa[kb][m][3] = pack_bf16(dsv_[2 * m + 1][2] * sk, dsv_[2 * m + 1][3] * sk);
+        }
       }
-      // dS tile -> LDS as [member][key]
+      // dS tile (unscaled) -> LDS as [member][key]
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -507,115 +508,90 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
           lds.ds[(qb * 16 + 4 * lg + j) * 40 + 16 * kb + li] = (uint16_t)(w & 0xffffu);
         }
     }
+
+    // ---- dQ^T += K^T dS^T. The A operand K^T (row li <-> feature 16fb + li, slot (lg, e) <->
+    // key 4lg + e for e < 4, 16 + 4lg + e - 4 for e >= 4) is made from the natural K rows
+    // already in registers: kb_n x sel moves feature block fb of each 16-key tile into the C
+    // layout (lane li <-> feature, keys 4lg + j), which packed to bf16 is exactly that
+    // operand. The B operand dS^T is read from the LDS tile with the same key order.
+    __syncthreads();   // dS tile complete (single-wave workgroup: orders the LDS writes)
+    {
+      u32x4 bds[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(&lds.ds[(qb * 16 + li) * 40 + 4 * lg]);
+        const u32x2 hi =
+            *reinterpret_cast<const u32x2*>(&lds.ds[(qb * 16 + li) * 40 + 16 + 4 * lg]);
+        bds[qb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int fb = 0; fb < NDB; ++fb) {
+        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+        const floatx4 t0 = mfma_bf16(kb_n[0][fb >> 1], sel[fb & 1], z);
+        const floatx4 t1 = mfma_bf16(kb_n[1][fb >> 1], sel[fb & 1], z);
+        const u32x4 ka = {pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]),
+                          pack_bf16(t1[0], t1[1]), pack_bf16(t1[2], t1[3])};
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) dqacc[qb][fb] = mfma_bf16(ka, bds[qb], dqacc[qb][fb]);
+      }
+    }
+
     // the natural K/V registers are free again: request the next chunk's rows now
     if (cb + 32 < kh) load_nat(cb + 32);
 
-    // ---- dV = P^T dO, dK = scale dS^T Q ; lane: keys 16kb + 4lg + j, features
-    // (D/16)*li + db. Each valid key's dV and dK rows go to its edge's staging row as 16-bit
-    // integers times one fp32 step per half: |dV[d]| <= sum_n P * max|dO| and
-    // |dK[d]| <= scale * sum_n |dS| * max|Q| bound every entry, so the step is that bound /
-    // kQLevels (error <= step / 2 per entry).
+    // ---- dV^T = dO^T P, dK^T = Q^T dS (pre-scaled, see above). A operands by transposed LDS
+    // reads: row li <-> feature 16fb + li, slot (lg, e) <-> member 32m + 16(e/4) + 4lg + e%4.
+    // Lane: key 16kb + li, features 16fb + 4lg + j; each staging row gets 8 bytes per lane.
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const float bound_v = colp[kb] * max_do;
-      const float bound_k = colds[kb] * max_q * scale;
-      const float inv_v = bound_v > 0.f ? kQLevels / bound_v : 0.f;
-      const float inv_k = bound_k > 0.f ? kQLevels / bound_k : 0.f;
-      const int p0 = cb + 16 * kb;   // row position of key 16kb + 0
-      if (lg == 0 && p0 + li < kh)
-        rstep[grow + p0 + li] = make_float2(bound_v / kQLevels, bound_k / kQLevels);
-      float iv[4], ik[4];
+    for (int fb = 0; fb < NDB; ++fb) {
+      floatx4 av[2], ak[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        iv[j] = __shfl(inv_v, 4 * lg + j, 64);
-        ik[j] = __shfl(inv_k, 4 * lg + j, 64) * scale;
-      }
-      // packed 16-bit entries: word w of key 4lg + j holds features NDB*li + 2w, + 2w + 1
-      uint32_t wv[4][NDB / 2], wk[4][NDB / 2];
+      for (int kb = 0; kb < 2; ++kb) av[kb] = ak[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        floatx4 accv = {0.f, 0.f, 0.f, 0.f}, acck = {0.f, 0.f, 0.f, 0.f};
+      for (int m = 0; m < NM; ++m) {
+        const int r1 = 32 * m + 4 * lg + (li >> 2);
+        const int col = 16 * fb + 4 * (li & 3);
+        const u32x2 d1 = lds_read_tr16(&lds.dn[swz<D>(r1, col)]);
+        const u32x2 d2 = lds_read_tr16(&lds.dn[swz<D>(r1 + 16, col)]);
+        const u32x2 q1 = lds_read_tr16(&lds.qn[swz<D>(r1, col)]);
+        const u32x2 q2 = lds_read_tr16(&lds.qn[swz<D>(r1 + 16, col)]);
+        const u32x4 adoT = {d1[0], d1[1], d2[0], d2[1]};
+        const u32x4 aqT = {q1[0], q1[1], q2[0], q2[1]};
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const int off = ((db * NM + m) * 64 + lane) * 8;
-          const u32x4 bdo = *reinterpret_cast<const u32x4*>(&lds.dot[off]);
-          const u32x4 bq = *reinterpret_cast<const u32x4*>(&lds.qt[off]);
-          accv = mfma_bf16(pa[kb][m], bdo, accv);
-          acck = mfma_bf16(dsa[kb][m], bq, acck);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t qv = (uint16_t)quantize16(accv[j] * iv[j]);
-          const uint32_t qk = (uint16_t)quantize16(acck[j] * ik[j]);
-          if (db & 1) {
-            wv[j][db >> 1] |= qv << 16;
-            wk[j][db >> 1] |= qk << 16;
-          } else {
-            wv[j][db >> 1] = qv;
-            wk[j][db >> 1] = qk;
-          }
+        for (int kb = 0; kb < 2; ++kb) {
+          av[kb] = mfma_bf16(adoT, pa[kb][m], av[kb]);
+          ak[kb] = mfma_bf16(aqT, dsa[kb][m], ak[kb]);
         }
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int p = p0 + 4 * lg + j;
+      for (int kb = 0; kb < 2; ++kb) {
+        const int p = cb + 16 * kb + li;
         if (p < kh) {
-          const long long off = (grow + p) * D + NDB * li;
-          // streaming (non-temporal) writes: the rows are read once, by the reduce
-          if constexpr (D == 128) {
-            __builtin_nontemporal_store(u32x4{wv[j][0], wv[j][1], wv[j][2], wv[j][3]},
-                                        reinterpret_cast<u32x4*>(cv + off));
-            __builtin_nontemporal_store(u32x4{wk[j][0], wk[j][1], wk[j][2], wk[j][3]},
-                                        reinterpret_cast<u32x4*>(ck + off));
-          } else {
-            __builtin_nontemporal_store(u32x2{wv[j][0], wv[j][1]},
-                                        reinterpret_cast<u32x2*>(cv + off));
-            __builtin_nontemporal_store(u32x2{wk[j][0], wk[j][1]},
-                                        reinterpret_cast<u32x2*>(ck + off));
-          }
+          const long long off = (grow + p) * D + 16 * fb + 4 * lg;
+          const u32x2 wv = {
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(av[kb][0], av[kb][1])),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(av[kb][2], av[kb][3]))};
+          const u32x2 wk = {
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(ak[kb][0], ak[kb][1])),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(ak[kb][2], ak[kb][3]))};
+          *reinterpret_cast<u32x2*>(cv + off) = wv;
+          *reinterpret_cast<u32x2*>(ck + off) = wk;
         }
       }
     }
-
-    // ---- dQ^T += K^T dS^T ; K transposed in registers, dS^T from the LDS tile
-    u32x4 vA[DPL];
-    {
-      if constexpr (D == 128) {
-        u32x4 raw[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) raw[e] = ld16(K + (long long)tkey[e] * D + DPL * li);
-        transpose8x8_b16(raw, vA);
-      } else {
-        u32x2 raw[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) raw[e] = ld8(K + (long long)tkey[e] * D + DPL * li);
-        transpose8x4_b16(raw, vA);
-      }
-    }
-    __syncthreads();   // dS tile complete (single-wave workgroup: orders the LDS writes)
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      // B operand: member 16qb + li, keys 8lg + e (e = 0..7), zero past the row end
-      u32x4 bds = *reinterpret_cast<const u32x4*>(&lds.ds[(qb * 16 + li) * 40 + 8 * lg]);
-#pragma unroll
-      for (int f = 0; f < DPL; ++f) dqacc[qb][f] = mfma_bf16(vA[f], bds, dqacc[qb][f]);
-    }
-    __syncthreads();   // the next chunk overwrites the tile
+    __syncthreads();   // the next chunk overwrites the dS tile
   }
 
-  // ---- store dQ (fp32): lane holds member 16qb + li, features DPL*(4lg + j) + f
+  // ---- store dQ (fp32): lane holds member 16qb + li, features 16fb + 4lg + j
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    float* drow = dq + base + (long long)tok[qb] * D;
+    const int n = gg.token(g, qb * 16 + li);
+    float* drow = dq + base + (long long)n * D;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int f4 = 0; f4 < DPL / 4; ++f4) {
-        float4 w = make_float4(dqacc[qb][4 * f4][j] * scale, dqacc[qb][4 * f4 + 1][j] * scale,
-                               dqacc[qb][4 * f4 + 2][j] * scale, dqacc[qb][4 * f4 + 3][j] * scale);
-        *reinterpret_cast<float4*>(drow + DPL * (4 * lg + j) + 4 * f4) = w;
-      }
-    }
+    for (int fb = 0; fb < NDB; ++fb)
+      *reinterpret_cast<float4*>(drow + 16 * fb + 4 * lg) =
+          make_float4(dqacc[qb][fb][0] * scale, dqacc[qb][fb][1] * scale,
+                      dqacc[qb][fb][2] * scale, dqacc[qb][fb][3] * scale);
   }
 }
 
