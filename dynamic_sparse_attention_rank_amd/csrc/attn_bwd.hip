@@ -73,6 +73,10 @@ __device__ __forceinline__ float pow2_scale(float bound) {
 
 __host__ __device__ inline int n_buckets(int S) { return (S + kBucket - 1) / kBucket; }
 
+// Staging rows per group: k rounded up to the 32-key chunk, so that the backward kernel's
+// stores are unconditional (the tail rows of a group hold zeros and are never read).
+__host__ __device__ inline int padded_k(int k) { return (k + 31) & ~31; }
+
 // A chunk of consecutive (b, h) slots in launch order (slot s = head rank * B + b).
 struct Chunk {
   int s0, n;
@@ -158,8 +162,8 @@ __global__ __launch_bounds__(256) void bucket_offsets(const uint32_t* __restrict
 }
 
 // Bucket-ordered edge list: perm[off[j] + i], i < tot[j], holds the edges (g, p) whose key
-// lies in bucket j, as the slot-relative staging row g*k + p, ordered by group, then by
-// position. One wave per (slot, bucket); 64 groups per step, positions from a wave scan.
+// lies in bucket j, as the slot-relative staging row g*padded_k + p, ordered by group, then
+// by position. One wave per (slot, bucket); 64 groups per step, positions from a wave scan.
 __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ rs,
                                                   const uint32_t* __restrict__ off, Chunk ch,
                                                   uint32_t* __restrict__ perm, Geom geo) {
@@ -169,7 +173,7 @@ __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ r
   const int lane = threadIdx.x;
   int b, h;
   chunk_slot(geo, ch.s0 + sl, b, h);
-  const uint32_t kh = (uint32_t)geo.k[h];
+  const uint32_t kp = (uint32_t)padded_k(geo.k[h]);
   const uint32_t slot_rows = (uint32_t)(ch.edge_base[sl + 1] - ch.edge_base[sl]);
   const uint32_t* r = rs + (long long)sl * geo.NG * (nB + 1);
   uint32_t* pm = perm + ch.edge_base[sl];
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ r
       if (lane >= d) incl += y;
     }
     const uint32_t pos = pos0 + incl - len;
-    const uint32_t e0 = (uint32_t)g * kh + a;
+    const uint32_t e0 = (uint32_t)g * kp + a;
     for (uint32_t i = 0; i < len; ++i)
       if (pos + i < slot_rows) pm[pos + i] = e0 + i;   // a malformed row is dropped
     pos0 += __shfl(incl, 63, 64);
@@ -237,7 +241,8 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
   const long long s0 = std::min<long long>(o[j], nrows);
   const long long s1 = std::min<long long>(std::max<long long>(o[j + 1], o[j]), nrows);
   const uint32_t* pm = perm + eb;
-  const int32_t* keys = idx + geo.row_offset(b, h, 0);   // key of slot row e is keys[e]
+  const int32_t* keys = idx + geo.row_offset(b, h, 0);   // row of group g: keys + g*k
+  const uint32_t kh = (uint32_t)geo.k[h], kp = (uint32_t)padded_k(geo.k[h]);
   const int16_t* src = (half ? ck : cv) + eb * D + FPL * lane;
   const int key0 = j * kBucket;
   for (long long r0 = s0; r0 < s1; r0 += 64) {
@@ -248,7 +253,8 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
     float sc = 0.f;
     if (lane < n) {
       e = std::min<uint32_t>(pm[r0 + lane], (uint32_t)(nrows - 1));
-      kk = min(max(clamp_key(keys[e], geo.S) - key0, 0), kBucket - 1);
+      const uint32_t gq = e / kp, pq = std::min(e - gq * kp, kh - 1);
+      kk = min(max(clamp_key(keys[(long long)gq * kh + pq], geo.S) - key0, 0), kBucket - 1);
       const float2 st = rstep[eb + e];
       sc = half ? st.y : st.x;
     }
@@ -350,8 +356,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
   const int32_t* row = idx + geo.row_offset(b, h, g);
   const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
   const int G = geo.G;
-  // staging row of edge (g, p): the slot's first row + g*k + p (index order)
-  const long long grow = ch.edge_base[sl] + (long long)g * kh;
+  // staging row of edge (g, p): the slot's first row + g*padded_k + p (index order)
+  const long long grow = ch.edge_base[sl] + (long long)g * padded_k(kh);
 
   // ---- per-group set-up: Q and dO rows into LDS, Delta = dO.O, LSE, max |dO| and max |Q|
   // (the bounds of the 16-bit dV|dK staging rows). CPR lanes per row, one chunk each.
@@ -400,11 +406,19 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     for (int f = 0; f < NDB; ++f) dqacc[qb][f] = floatx4{0.f, 0.f, 0.f, 0.f};
   const float c2 = scale * kLog2e;
 
+  // Every global access in the chunk loop below is unconditional (positions are clamped, tail
+  // rows are padding): with gfx9's single in-order vmcnt, a conditional store would force the
+  // wait for the prefetched K/V rows to drain every store as well.
   u32x4 kb_n[2][KS], vb_n[2][KS];   // natural K / V rows (B operands) of the current chunk
-  auto load_nat = [&](int cb) {
+  int nkey[2];                      // keys of the chunk after the prefetched one
+  auto load_keys = [&](int cb, int out[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) out[kb] = row[min(cb + 16 * kb + li, kh - 1)];
+  };
+  auto load_nat = [&](const int keys[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = clamp_key(row[min(cb + 16 * kb + li, kh - 1)], geo.S);
+      const int key = clamp_key(keys[kb], geo.S);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         kb_n[kb][ks] = ld16(K + (long long)key * D + ks * 32 + 8 * lg);
@@ -412,7 +426,12 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       }
     }
   };
-  load_nat(0);
+  {
+    int k0[2];
+    load_keys(0, k0);
+    load_nat(k0);
+    load_keys(32, nkey);
+  }
 
   // 0/1 selection operands: sel[h] as the B operand of a 16x16x32 MFMA maps contraction slot
   // (lg, e) <-> feature 32ks + 8lg + e to output column li iff 8lg + e == 16h + li, so
@@ -427,7 +446,11 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       sel[hh][w] = lo | (hi << 16);
     }
 
-  for (int cb = 0; cb < kh; cb += 32) {
+  // One 32-key chunk. The first chunk runs before the loop (peeled) so that both paths into
+  // the loop end with the same prefetch-then-store sequence: the compiler's wait for the
+  // prefetched K/V rows at the top of the loop then leaves the previous chunk's stores in
+  // flight instead of draining them.
+  auto chunk = [&](const int cb) {
     // ---- S = Q K^T, dP = dO V^T ; lane: key 16kb + li, members 16qb + 4lg + j. The A
     // operands (member 16qb + li, features 32ks + 8lg ..) are 16-byte LDS row reads.
     u32x4 pa[2][NM], dsa[2][NM];
@@ -481,10 +504,11 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         cd = wave_xor_sum(cd, 32);
         const float sv = pow2_scale(cp * max_do);
         const float sk = pow2_scale(cd * max_q);   // dK = scale * (sum dS q): scale in the step
-        if (lg == 0 && kvalid)
-          rstep[grow + cb + 16 * kb + li] =
-              make_float2(sv > 0.f ? 1.f / (32767.f * sv) : 0.f,
-                          sk > 0.f ? scale / (32767.f * sk) : 0.f);
+        // the four lanes of a key store the same value (an unconditional store)
+        // (sv, sk are powers of two, so their reciprocals are exact)
+        rstep[grow + cb + 16 * kb + li] =
+            make_float2(sv > 0.f ? __builtin_amdgcn_rcpf(sv) * (1.f / 32767.f) : 0.f,
+                        sk > 0.f ? __builtin_amdgcn_rcpf(sk) * (scale / 32767.f) : 0.f);
         // B operands of dO^T P / Q^T dS: column li <-> key, slot (lg, e) <-> member
         // 16(2m + e/4) + 4lg + e%4
 #pragma unroll
@@ -514,7 +538,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     // already in registers: kb_n x sel moves feature block fb of each 16-key tile into the C
     // layout (lane li <-> feature, keys 4lg + j), which packed to bf16 is exactly that
     // operand. The B operand dS^T is read from the LDS tile with the same key order.
-    __syncthreads();   // dS tile complete (single-wave workgroup: orders the LDS writes)
+    wave_lds_fence();   // dS tile complete
     {
       u32x4 bds[QB];
 #pragma unroll
@@ -536,8 +560,11 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       }
     }
 
-    // the natural K/V registers are free again: request the next chunk's rows now
-    if (cb + 32 < kh) load_nat(cb + 32);
+    // the natural K/V registers are free again: request the next chunk's rows now (past the
+    // end the clamped positions reload the last key) and the keys of the one after
+    load_nat(nkey);
+    load_keys(cb + 64, nkey);
+    asm volatile("" ::: "memory");   // keep these loads ahead of the stores below
 
     // ---- dV^T = dO^T P, dK^T = Q^T dS (pre-scaled, see above). A operands by transposed LDS
     // reads: row li <-> feature 16fb + li, slot (lg, e) <-> member 32m + 16(e/4) + 4lg + e%4.
@@ -565,22 +592,22 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int p = cb + 16 * kb + li;
-        if (p < kh) {
-          const long long off = (grow + p) * D + 16 * fb + 4 * lg;
-          const u32x2 wv = {
-              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(av[kb][0], av[kb][1])),
-              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(av[kb][2], av[kb][3]))};
-          const u32x2 wk = {
-              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(ak[kb][0], ak[kb][1])),
-              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(ak[kb][2], ak[kb][3]))};
-          *reinterpret_cast<u32x2*>(cv + off) = wv;
-          *reinterpret_cast<u32x2*>(ck + off) = wk;
-        }
+        // row cb + 16kb + li < padded_k: past the row end it is a (zero) padding row
+        const long long off = (grow + cb + 16 * kb + li) * D + 16 * fb + 4 * lg;
+        const u32x2 wv = {
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(av[kb][0], av[kb][1])),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(av[kb][2], av[kb][3]))};
+        const u32x2 wk = {
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(ak[kb][0], ak[kb][1])),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(ak[kb][2], ak[kb][3]))};
+        *reinterpret_cast<u32x2*>(cv + off) = wv;
+        *reinterpret_cast<u32x2*>(ck + off) = wk;
       }
     }
-    __syncthreads();   // the next chunk overwrites the dS tile
-  }
+    wave_lds_fence();   // the next chunk overwrites the dS tile
+  };
+  chunk(0);
+  for (int cb = 32; cb < kh; cb += 32) chunk(cb);
 
   // ---- store dQ (fp32): lane holds member 16qb + li, features 16fb + 4lg + j
 #pragma unroll
@@ -699,7 +726,7 @@ static WsLayout ws_layout(const Geom& geo, long long cs, long long e) {
 static long long max_slot_rows(const Geom& geo) {
   int kmax = 0;
   for (int h = 0; h < geo.H; ++h) kmax = std::max(kmax, geo.k[h]);
-  return (long long)geo.NG * kmax;
+  return (long long)geo.NG * padded_k(kmax);
 }
 
 size_t bwd_workspace_bytes(const Geom& geo) {
@@ -766,7 +793,7 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
     long long rows = 0;
     while (s0 + ch.n < nslots && ch.n < cs) {
       const int h = geo.order[(s0 + ch.n) / geo.B];
-      const long long r = (long long)geo.NG * geo.k[h];
+      const long long r = (long long)geo.NG * padded_k(geo.k[h]);
       if (ch.n > 0 && rows + r > ecap) break;
       ch.edge_base[ch.n] = rows;
       rows += r;

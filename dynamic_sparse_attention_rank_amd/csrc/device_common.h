@@ -85,6 +85,12 @@ __device__ __forceinline__ void transpose8x4_b16(const u32x2 in[8], u32x4 out[4]
 __device__ __forceinline__ float wave_xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
+// Ordering point for the LDS accesses of a single-wave workgroup: waits for this wave's
+// outstanding LDS operations and keeps the compiler from moving memory accesses across it.
+// __syncthreads() would also wait for every outstanding global load and store (its fence),
+// which serialises streaming stores and prefetches with the computation.
+__device__ __forceinline__ void wave_lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
 }

@@ -165,9 +165,9 @@ int dsv_validate(int op, const dsv_problem* p, const int32_t* k_per_head, int re
   if (op == DSV_OP_BWD && geo.dtype == DSV_BF16) {
     int kmax = 0;
     for (int h = 0; h < geo.H; ++h) kmax = std::max(kmax, geo.k[h]);
-    if ((long long)geo.NG * kmax >= (1LL << 31))
-      return fail(DSV_ERR_UNSUPPORTED, "backward: NG * max k = %lld edges per head exceeds 2^31",
-                  (long long)geo.NG * kmax);
+    const long long rows = (long long)geo.NG * ((kmax + 31) & ~31);
+    if (rows >= (1LL << 31))
+      return fail(DSV_ERR_UNSUPPORTED, "backward: %lld staging rows per head exceed 2^31", rows);
   }
   const size_t need = op == DSV_OP_BWD ? bwd_workspace_bytes(geo) : 0;
   if (ws_bytes < need)

@@ -81,7 +81,8 @@ typedef struct {
 
 /* Minimum bytes of device workspace `op` needs for this problem. DSV_OP_TOPK and DSV_OP_FWD
  * need none (their ws may be NULL). DSV_OP_BWD on the bf16 path needs the per-edge dV|dK
- * staging rows of one (b,h) head (NG*k_max*(4*d + 12) bytes plus small per-bucket tables); a
+ * staging rows of one (b,h) head (NG*k32*(4*d + 12) bytes, k32 = max k rounded up to a
+ * multiple of 32, plus small per-bucket tables); a
  * larger workspace lets one launch cover several heads. The fp32 path needs none.
  * Returns (size_t)-1 if the problem is invalid. */
 size_t dsv_workspace_bytes(int op, const dsv_problem* p, const int32_t* k_per_head);

@@ -111,7 +111,7 @@ def test_workspace_and_idx_layout_agree_with_oracle():
     al = lambda x: -(-x // 256) * 256
     nb = -(-p.seq // 32)
     NG = p.n_groups
-    e = NG * max(ks)
+    e = NG * (-(-max(ks) // 32) * 32)
     need = (al(NG * (nb + 1) * 4) + 2 * al((nb + 1) * 4) + al(e * 4) + al(e * 8)
             + al(e * 64 * 2) + e * 64 * 2)
     assert dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks) == need
