@@ -309,26 +309,10 @@ struct BwdLds {
   float delta[64] __attribute__((aligned(16)));   // Delta per group member
 };
 
-// element offset of feature `col` (col % 4 == 0) of row r in the swizzled layout
-template <int D>
-__device__ __forceinline__ int swz(int r, int col) {
-  return r * D + ((((col >> 3) ^ r) & (D / 8 - 1)) << 3) + (col & 7);
-}
-
-// ds_read_b64_tr_b16: within each 16-lane block, lane j passes the address of 4 elements
-// (row R0 + j/4, columns C0 + 4(j%4)) and lane i receives column C0 + i of rows R0 .. R0 + 3.
-__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
-  typedef short v4i16 __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_v4i16*)((__attribute__((address_space(3))) const uint16_t*)p));
-  return __builtin_bit_cast(u32x2, v);
-}
-
 template <int D, int QB>
 __global__ __launch_bounds__(64) void attn_bwd_bf16(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ q, const uint16_t* k,   // k, v: not restrict, so that the
+    const uint16_t* v, const uint16_t* __restrict__ o,   // prefetch stays ordered (see below)
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
     const int32_t* __restrict__ idx, float scale, float* __restrict__ dq, Chunk ch,
     int16_t* __restrict__ cv, int16_t* __restrict__ ck, float2* __restrict__ rstep, Geom geo) {
@@ -433,18 +417,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     load_keys(32, nkey);
   }
 
-  // 0/1 selection operands: sel[h] as the B operand of a 16x16x32 MFMA maps contraction slot
-  // (lg, e) <-> feature 32ks + 8lg + e to output column li iff 8lg + e == 16h + li, so
-  // A x sel[h] copies features 32ks + 16h .. + 15 of the A rows into the C layout (exact).
   u32x4 sel[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t lo = (8 * lg + 2 * w == 16 * hh + li) ? 0x3f80u : 0u;
-      const uint32_t hi = (8 * lg + 2 * w + 1 == 16 * hh + li) ? 0x3f80u : 0u;
-      sel[hh][w] = lo | (hi << 16);
-    }
+  make_selection(lane, sel);
 
   // One 32-key chunk. The first chunk runs before the loop (peeled) so that both paths into
   // the loop end with the same prefetch-then-store sequence: the compiler's wait for the

@@ -6,19 +6,19 @@
 //     O[n] = sum_{m in idx(g)} softmax_m(scale * q_n . k_m) v_m,   LSE[n] = log sum_m exp(...)
 //
 // bf16 path (gfx950 MFMA): one wave per group (G = 16..64 queries, d = 64 or 128).
-//   * The group's Q is held in registers as the B operand of S^T = K Q^T
-//     (v_mfma_f32_16x16x32_bf16), so each 16x16 score tile gives a lane one query and 4 keys.
-//   * Keys are consumed in chunks of 32 from the ascending index row. A lane gathers K rows in
-//     16-byte pieces straight into MFMA operand registers; V rows are gathered one full
-//     256-byte row per 16 lanes and transposed in registers (v_perm_b32) into the A operand of
-//     O^T += V^T P^T. The key order inside the contraction is permuted so that the P^T operand
-//     is exactly the score tile a lane already holds: no LDS and no cross-lane traffic on the
-//     hot loop except the occasional max reduction.
+//   * The group's Q rows sit in LDS (one swizzled copy); S^T = K Q^T reads them as 16-byte B
+//     operands, so a 16x16 score tile gives a lane one query and 4 keys.
+//   * Keys are consumed in chunks of 32 from the ascending index row. K and V rows are both
+//     gathered in 16-byte pieces straight into MFMA operand registers (lane: one key, 8
+//     features). The V^T operand of O^T += V^T P^T is made from those registers by an MFMA
+//     against a 0/1 selection matrix (exact), with the key order chosen so that the P^T
+//     operand is exactly the score tile a lane already holds.
 //   * Online softmax in the log2 domain with an fp32 running max and sum; the max is only
 //     raised (and O rescaled) when a new score exceeds it by more than 2^8, which keeps exp2
 //     arguments <= 8 and makes rescaling rare. Results are exact regardless of when it is raised.
-//   * The next chunk's K/V rows are requested while the current chunk is still being
-//     computed (indices one chunk further ahead).
+//   * The next chunk's K/V rows are requested as soon as the current ones have been turned
+//     into operands, and the key indices one chunk further ahead; every load in the loop is
+//     unconditional (positions clamped), so the waits for them are exact.
 // fp32 path: plain fp32 FMA per lane (one lane per query); it exists for fp32 inputs and is
 // not tuned.
 #include <math.h>
@@ -42,37 +42,17 @@ __device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, i
   g = rem - b * geo.NG;
 }
 
-template <int D>
-struct VRaw;   // one lane's slice of 8 V rows: DPL = D/16 consecutive features per row
-template <>
-struct VRaw<128> {
-  u32x4 r[8];
-};
-template <>
-struct VRaw<64> {
-  u32x2 r[8];
-};
-
-template <int D>
-struct FwdChunk {
-  u32x4 k[2][D / 32];   // K rows (16kb + li), features 32ks + 8lg .. +8
-  VRaw<D> v;            // V rows of this lane's 8 keys, features DPL*li .. +DPL
-};
-
-struct ChunkKeys {
-  int kk[2];   // key index for K rows 16kb + li
-  int vk[8];   // key index for this lane's 8 V rows
-};
-
 template <int D, int QB>
 __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__ q,
-                                                    const uint16_t* __restrict__ k,
-                                                    const uint16_t* __restrict__ v,
+                                                    const uint16_t* k,   // k, v: not restrict,
+                                                    const uint16_t* v,   // see the prefetch
                                                     const int32_t* __restrict__ idx, float scale,
                                                     uint16_t* __restrict__ o,
                                                     float* __restrict__ lse, Geom geo) {
-  constexpr int DPL = D / 16;   // features per lane per V row; also O^T dimension blocks
+  constexpr int NDB = D / 16;   // feature blocks of O^T
   constexpr int KS = D / 32;    // contraction steps of S^T = K Q^T
+  constexpr int CPR = D / 8;    // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) uint16_t qn[16 * QB * D];
   const int lane = threadIdx.x;
   const int lg = lane >> 4;
   const int li = lane & 15;
@@ -86,88 +66,86 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
   const int32_t* row = idx + geo.row_offset(b, h, g);
   const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
 
-  int tok[QB];
-  u32x4 qop[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    tok[qb] = gg.token(g, qb * 16 + li);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qop[qb][ks] = ld16(Q + (long long)tok[qb] * D + ks * 32 + 8 * lg);
+  // ---- the group's Q rows into LDS (CPR lanes per row, one 16-byte chunk each)
+  {
+    const int rr = lane / CPR, c = lane % CPR;
+    for (int r0 = 0; r0 < 16 * QB; r0 += 64 / CPR) {
+      const int r = r0 + rr;
+      const int n = gg.token(g, r);
+      *reinterpret_cast<u32x4*>(&qn[swz<D>(r, 8 * c)]) = ld16(Q + (long long)n * D + 8 * c);
+    }
   }
+  __syncthreads();
 
-  floatx4 oacc[QB][DPL];
+  floatx4 oacc[QB][NDB];
   float mrun[QB], lrun[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     mrun[qb] = -INFINITY;
     lrun[qb] = 0.f;
 #pragma unroll
-    for (int f = 0; f < DPL; ++f) oacc[qb][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < NDB; ++f) oacc[qb][f] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = scale * kLog2e;
+  u32x4 sel[2];
+  make_selection(lane, sel);
 
-  auto load_keys = [&](int cb, ChunkKeys& ck) {
+  u32x4 kb_n[2][KS], vb_n[2][KS];   // K / V rows 16kb + li of the current chunk, features
+  int nkey[2];                      // 32ks + 8lg ..; keys of the chunk after the next one
+  auto load_keys = [&](int cb, int out[2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) ck.kk[kb] = clamp_key(row[min(cb + 16 * kb + li, kh - 1)], geo.S);
+    for (int kb = 0; kb < 2; ++kb) out[kb] = row[min(cb + 16 * kb + li, kh - 1)];
+  };
+  auto load_nat = [&](const int keys[2]) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int p = cb + (e < 4 ? 4 * lg + e : 16 + 4 * lg + (e - 4));
-      ck.vk[e] = clamp_key(row[min(p, kh - 1)], geo.S);
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = clamp_key(keys[kb], geo.S);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kb_n[kb][ks] = ld16(K + (long long)key * D + ks * 32 + 8 * lg);
+        vb_n[kb][ks] = ld16(V + (long long)key * D + ks * 32 + 8 * lg);
+      }
     }
   };
-  auto load_k = [&](const ChunkKeys& ck, FwdChunk<D>& ch) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        ch.k[kb][ks] = ld16(K + (long long)ck.kk[kb] * D + ks * 32 + 8 * lg);
-  };
-  auto load_v = [&](const ChunkKeys& ck, FwdChunk<D>& ch) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if constexpr (D == 128)
-        ch.v.r[e] = ld16(V + (long long)ck.vk[e] * D + DPL * li);
-      else
-        ch.v.r[e] = ld8(V + (long long)ck.vk[e] * D + DPL * li);
-    }
-  };
-
-  // One K/V buffer: the next chunk's K rows are requested as soon as the score MFMAs have
-  // consumed the current ones, and its V rows right after the current V has been
-  // transposed, so both loads overlap the softmax and the P.V MFMAs. Indices run one chunk
-  // further ahead.
-  ChunkKeys keys_nx;
-  FwdChunk<D> ch;
   {
-    ChunkKeys k0;
+    int k0[2];
     load_keys(0, k0);
-    load_k(k0, ch);
-    load_v(k0, ch);
-    load_keys(32, keys_nx);   // clamped reads stay inside the row even when k <= 32
+    load_nat(k0);
+    load_keys(32, nkey);
   }
+
   for (int cb = 0; cb < kh; cb += 32) {
-    const bool more = cb + 32 < kh;
+    // ---- S^T = K Q^T ; lane: query 16qb + li, keys 16kb + 4lg + j
     floatx4 s[2][QB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int qb = 0; qb < QB; ++qb) {
+      s[0][qb] = s[1][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        floatx4 a = {0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 qop = *reinterpret_cast<const u32x4*>(&qn[swz<D>(16 * qb + li, 32 * ks + 8 * lg)]);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) a = mfma_bf16(ch.k[kb][ks], qop[qb][ks], a);
-        s[kb][qb] = a;
+        for (int kb = 0; kb < 2; ++kb) s[kb][qb] = mfma_bf16(kb_n[kb][ks], qop, s[kb][qb]);
       }
-    if (more) load_k(keys_nx, ch);
-    // V^T operand: vA[f] = feature DPL*li + f of the lane's 8 keys
-    u32x4 vA[DPL];
-    if constexpr (D == 128)
-      transpose8x8_b16(ch.v.r, vA);
-    else
-      transpose8x4_b16(ch.v.r, vA);
-    if (more) {
-      load_v(keys_nx, ch);
-      load_keys(cb + 64, keys_nx);
     }
+    // ---- V^T operands: row li <-> feature 16fb + li, slot (lg, e) <-> key 4lg + e (e < 4),
+    // 16 + 4lg + e - 4 (e >= 4), from the V rows in registers (selection MFMA, exact)
+    u32x4 vT[NDB];
+#pragma unroll
+    for (int fb = 0; fb < NDB; ++fb) {
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      const floatx4 t0 = mfma_bf16(vb_n[0][fb >> 1], sel[fb & 1], z);
+      const floatx4 t1 = mfma_bf16(vb_n[1][fb >> 1], sel[fb & 1], z);
+      vT[fb] = u32x4{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]),
+                     pack_bf16(t1[2], t1[3])};
+    }
+    // K/V registers consumed: request the next chunk (past the end the clamped positions
+    // reload the last key; those loads are never used) and the keys of the one after. The
+    // compiler barrier keeps the loads after the MFMAs above, so the two K/V buffers are
+    // never live together.
+    asm volatile("" ::: "memory");
+    load_nat(nkey);
+    load_keys(cb + 64, nkey);
+
     const bool tail = cb + 32 > kh;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -190,7 +168,7 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
         mrun[qb] = mnew;
         lrun[qb] *= alpha;
 #pragma unroll
-        for (int f = 0; f < DPL; ++f) oacc[qb][f] *= alpha;
+        for (int f = 0; f < NDB; ++f) oacc[qb][f] *= alpha;
       }
       float p[2][4];
       float psum = 0.f;
@@ -198,47 +176,34 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          p[kb][j] = exp2f(t[kb][j] - mrun[qb]);
+          p[kb][j] = __builtin_amdgcn_exp2f(t[kb][j] - mrun[qb]);
           psum += p[kb][j];
         }
       lrun[qb] += psum;
-      // P^T operand: element e <-> key (e < 4 ? 4lg + e : 16 + 4lg + e - 4), matching vA
-      u32x4 pb;
-      pb[0] = pack_bf16(p[0][0], p[0][1]);
-      pb[1] = pack_bf16(p[0][2], p[0][3]);
-      pb[2] = pack_bf16(p[1][0], p[1][1]);
-      pb[3] = pack_bf16(p[1][2], p[1][3]);
+      // P^T operand: element e <-> key (e < 4 ? 4lg + e : 16 + 4lg + e - 4), matching vT
+      const u32x4 pb = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
+                        pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
 #pragma unroll
-      for (int f = 0; f < DPL; ++f) oacc[qb][f] = mfma_bf16(vA[f], pb, oacc[qb][f]);
+      for (int fb = 0; fb < NDB; ++fb) oacc[qb][fb] = mfma_bf16(vT[fb], pb, oacc[qb][fb]);
     }
   }
 
-  // finalise: full row sums, normalise, store O (bf16) and LSE (fp32)
+  // finalise: full row sums, normalise, store O (bf16) and LSE (fp32). Lane: query
+  // 16qb + li, features 16fb + 4lg + j.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     float l = wave_xor_sum(lrun[qb], 16);
     l = wave_xor_sum(l, 32);
     const float inv = 1.0f / l;
-    uint16_t* orow = o + base + (long long)tok[qb] * D;
+    const int n = gg.token(g, 16 * qb + li);
+    uint16_t* orow = o + base + (long long)n * D;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // dims DPL*(4lg + j) + f, f = 0..DPL-1
-      if constexpr (D == 128) {
-        u32x4 w;
-#pragma unroll
-        for (int f2 = 0; f2 < 4; ++f2)
-          w[f2] = pack_bf16(oacc[qb][2 * f2][j] * inv, oacc[qb][2 * f2 + 1][j] * inv);
-        *reinterpret_cast<u32x4*>(orow + DPL * (4 * lg + j)) = w;
-      } else {
-        u32x2 w;
-#pragma unroll
-        for (int f2 = 0; f2 < 2; ++f2)
-          w[f2] = pack_bf16(oacc[qb][2 * f2][j] * inv, oacc[qb][2 * f2 + 1][j] * inv);
-        *reinterpret_cast<u32x2*>(orow + DPL * (4 * lg + j)) = w;
-      }
-    }
+    for (int fb = 0; fb < NDB; ++fb)
+      *reinterpret_cast<u32x2*>(orow + 16 * fb + 4 * lg) =
+          u32x2{pack_bf16(oacc[qb][fb][0] * inv, oacc[qb][fb][1] * inv),
+                pack_bf16(oacc[qb][fb][2] * inv, oacc[qb][fb][3] * inv)};
     if (lg == 0)
-      lse[((long long)b * geo.H + h) * geo.S + tok[qb]] = (mrun[qb] + log2f(l)) * kLn2;
+      lse[((long long)b * geo.H + h) * geo.S + n] = (mrun[qb] + log2f(l)) * kLn2;
   }
 }
 

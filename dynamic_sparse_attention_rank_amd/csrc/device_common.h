@@ -124,4 +124,42 @@ struct GroupGeom {
   }
 };
 
+
+// ---- LDS row copies read both ways -----------------------------------------------------------
+// A [row][feature] bf16 tile with D features per row, chunk c (8 features, 16 bytes) of row r
+// stored at chunk position c ^ (r mod D/8): 16-byte reads of one chunk from 16 consecutive
+// rows hit distinct banks, and the 8-byte transposed reads below stay inside one chunk.
+// element offset of feature `col` (col % 4 == 0) of row r in the swizzled layout
+template <int D>
+__device__ __forceinline__ int swz(int r, int col) {
+  return r * D + ((((col >> 3) ^ r) & (D / 8 - 1)) << 3) + (col & 7);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane block, lane j passes the address of 4 elements
+// (row R0 + j/4, columns C0 + 4(j%4)) and lane i receives column C0 + i of rows R0 .. R0 + 3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((__attribute__((address_space(3))) const uint16_t*)p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+
+// 0/1 selection operands: sel[h] as the B operand of a 16x16x32 MFMA maps contraction slot
+// (lg, e) <-> feature 32ks + 8lg + e to output column li iff 8lg + e == 16h + li, so
+// A x sel[h] copies features 32ks + 16h .. + 15 of the A rows into the C layout: lane li then
+// holds feature 32ks + 16h + li of A rows 4lg + j. Exact for bf16 A (one product by 1.0).
+__device__ __forceinline__ void make_selection(int lane, u32x4 sel[2]) {
+  const int lg = lane >> 4, li = lane & 15;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t lo = (8 * lg + 2 * w == 16 * hh + li) ? 0x3f80u : 0u;
+      const uint32_t hi = (8 * lg + 2 * w + 1 == 16 * hh + li) ? 0x3f80u : 0u;
+      sel[hh][w] = lo | (hi << 16);
+    }
+}
+
 }  // namespace dsv
