@@ -7,12 +7,18 @@ d = 128, r = 32, 4x4x4 query groups, k = 6,554 (10%), bf16.
 
 Prints one JSON line. `value` is the selected-KV attention TFLOP/s of the whole step
 (fwd + bwd FLOPs over the step time, top-k time included); the per-op times, the attention-only
-and dense-equivalent rates, the top-k time, the dominant kernel's roofline and the oracle's
-rate on the host cores are reported beside it.
+and dense-equivalent rates, the top-k time, the per-kernel times, the dominant kernel's roofline
+and the oracle's rate on the host cores are reported beside it.
+
+Timing: HIP events on the launch stream around every op (torch events) and, inside the
+backward, around every head chunk's stages (raw hipEvent_t handles passed to
+dsv_sparse_attn_bwd_profiled), so each kernel's average launch duration is measured live.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import math
 import os
@@ -32,6 +38,87 @@ def flops(cfg, ks):
     fwd = 4.0 * B * S * d * sum(ks)
     dense_fwd = 4.0 * B * cfg.heads * S * S * d
     return fwd, 2.5 * fwd, dense_fwd, 2.5 * dense_fwd
+
+
+def bwd_units(cfg, ks):
+    """Algorithmic HBM bytes of the two backward kernels for the whole step.
+
+    Backward kernel (per (b,h) slot, E = NG*k edges): the staging rows it writes, E*(4d + 8)
+    (an int16 dV row and dK row, two fp32 steps), the idx row reads, 4E, Q, K, V, O and dO
+    read once, 10*S*d, LSE, 4*S, and dQ written once, 4*S*d (gathered K/V re-reads are cache
+    traffic, not counted). Bucket reduce: the staging rows and steps read once, E*(4d + 8),
+    its edge list and key reads, 8E, and dK and dV written once, 8*S*d."""
+    B, S, d, NG = cfg.batch, cfg.seq, cfg.head_dim, cfg.n_groups
+    pass1 = red = 0
+    for kh in ks:
+        E = NG * kh
+        pass1 += B * (E * (4 * d + 8) + 4 * E + 10 * S * d + 4 * S + 4 * S * d)
+        red += B * (E * (4 * d + 8) + 8 * E + 8 * S * d)
+    return pass1, red
+
+
+def hip_events(n):
+    """n raw hipEvent_t handles (timing enabled) from the HIP runtime libdsv uses."""
+    import dynamic_sparse_attention_rank_amd as dsv
+    L = dsv.lib()
+    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.hipEventCreate.restype = ctypes.c_int
+    out = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        if L.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        out.append(e.value)
+    return out
+
+
+def hip_elapsed_ms(a, b):
+    import dynamic_sparse_attention_rank_amd as dsv
+    L = dsv.lib()
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    L.hipEventElapsedTime.restype = ctypes.c_int
+    ms = ctypes.c_float()
+    if L.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+        raise RuntimeError("hipEventElapsedTime failed")
+    return ms.value
+
+
+def hip_destroy(evs):
+    import dynamic_sparse_attention_rank_amd as dsv
+    L = dsv.lib()
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    for e in evs:
+        L.hipEventDestroy(e)
+
+
+def kernel_sources_sha256(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "dynamic_sparse_attention_rank_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
+    if there is none for this kernel and workload or its sources have changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals, cur = {}, None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("kernel:"):
+            cur = line.split(":", 1)[1].strip()
+            vals[cur] = {}
+        elif cur and ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            vals[cur][key.strip()] = val.strip()
+    v = vals.get(kernel)
+    if not v or v.get("sources_sha256") != kernel_sources_sha256(v.get("sources", "").split()):
+        return None
+    return float(v["fetch_bytes_per_launch"]) + float(v["write_bytes_per_launch"])
 
 
 def topk_units(cfg, ks):
@@ -94,6 +181,9 @@ def main():
     ap.add_argument("--config", default="mid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after timing, run one plain fp32 copy kernel of this many MiB (read "
+                         "and written once): the reference for scaling HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the DSV hot path is measured on one GPU's share "
@@ -123,8 +213,11 @@ def main():
     ws_n = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks) * min(4, cfg.batch * cfg.heads)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    staged = cfg.dtype == "bf16"   # per-stage backward events exist on the bf16 path
+    nch = dsv.bwd_chunks(p, ks, ws.numel()) if staged else 0
+    stage_ev = hip_events(4 * nch * args.steps) if staged else []
 
-    def step(ev=None):
+    def step(ev=None, sev=None):
         if ev is not None:
             ev[0].record(stream)
         dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], ks, idx=idx, stream=stream)
@@ -135,7 +228,7 @@ def main():
         if ev is not None:
             ev[2].record(stream)
         dsv.sparse_attn_bwd(p, x["q"], x["k"], x["v"], o, x["do"], lse, idx, ks, x["scale"],
-                            dq=dq, dk=dk, dv=dv, ws=ws, stream=stream)
+                            dq=dq, dk=dk, dv=dv, ws=ws, stream=stream, events=sev)
         if ev is not None:
             ev[3].record(stream)
 
@@ -147,7 +240,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], stage_ev[4 * nch * i:4 * nch * (i + 1)] if staged else None)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
@@ -163,28 +256,58 @@ def main():
     dense_attn = (fd_fwd + fd_bwd) / (ms_attn * 1e-3) / 1e12
     scores, tk_bytes = topk_units(cfg, ks)
 
-    kernels = {
-        "lowrank_topk": {"ms_mean": mean(t_topk), "ms_median": med(t_topk),
-                         "scores_per_s": scores / (mean(t_topk) * 1e-3),
-                         "hbm_gbs_algorithmic": tk_bytes / (mean(t_topk) * 1e-3) / 1e9},
-        "sparse_attn_fwd": {"ms_mean": mean(t_fwd), "ms_median": med(t_fwd),
-                            "tflops": f_fwd / (mean(t_fwd) * 1e-3) / 1e12},
-        "sparse_attn_bwd": {"ms_mean": mean(t_bwd), "ms_median": med(t_bwd),
-                            "tflops": f_bwd / (mean(t_bwd) * 1e-3) / 1e12,
-                            "note": "call = per chunk of (b,h) slots: bucket count + scan + "
-                                    "backward kernel + bucket reduce"},
-    }
-    dom = max(kernels, key=lambda kname: kernels[kname]["ms_mean"])
     peak = PEAK["bf16_mfma_tflops"] if cfg.dtype == "bf16" else PEAK["fp32_mfma_tflops"]
-    if dom == "lowrank_topk":
-        ach = tk_bytes / (kernels[dom]["ms_mean"] * 1e-3) / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK["hbm_gbs"],
-                "unit": "GB/s", "frac": ach / PEAK["hbm_gbs"], "traffic": None}
+    # per-kernel table: launches per step, average launch duration, per-step total and the
+    # algorithmic work of one average launch (bytes or FLOPs), with the roofline it is held to
+    kernels = {
+        "topk_kernel": {"op": "dsv_lowrank_topk", "launches_per_step": 1,
+                        "ms_per_launch": mean(t_topk), "ms_median": med(t_topk),
+                        "bound": "hbm", "units_per_launch": tk_bytes,
+                        "scores_per_s": scores / (mean(t_topk) * 1e-3)},
+        "attn_fwd_bf16" if staged else "attn_fwd_f32": {
+            "op": "dsv_sparse_attn_fwd", "launches_per_step": 1, "ms_per_launch": mean(t_fwd),
+            "ms_median": med(t_fwd), "bound": "mfma", "units_per_launch": f_fwd},
+    }
+    if staged:
+        pre, p1, red = [], [], []
+        for i in range(args.steps):
+            e = stage_ev[4 * nch * i:4 * nch * (i + 1)]
+            for c in range(nch):
+                pre.append(hip_elapsed_ms(e[4 * c], e[4 * c + 1]))
+                p1.append(hip_elapsed_ms(e[4 * c + 1], e[4 * c + 2]))
+                red.append(hip_elapsed_ms(e[4 * c + 2], e[4 * c + 3]))
+        b1, b2 = bwd_units(cfg, ks)
+        kernels["attn_bwd_bf16"] = {"op": "dsv_sparse_attn_bwd", "launches_per_step": nch,
+                                    "ms_per_launch": mean(p1), "ms_median": med(p1),
+                                    "bound": "hbm", "units_per_launch": b1 / nch,
+                                    "tflops_all_bwd_flops": f_bwd / (sum(p1) / args.steps * 1e-3) / 1e12}
+        kernels["bucket_reduce"] = {"op": "dsv_sparse_attn_bwd", "launches_per_step": nch,
+                                    "ms_per_launch": mean(red), "ms_median": med(red),
+                                    "bound": "hbm", "units_per_launch": b2 / nch}
+        kernels["bwd_index_prepasses"] = {
+            "op": "dsv_sparse_attn_bwd", "launches_per_step": nch, "ms_per_launch": mean(pre),
+            "ms_median": med(pre), "bound": None, "units_per_launch": None,
+            "note": "row_bucket_starts + bucket_totals + bucket_offsets + bucket_perm"}
+        hip_destroy(stage_ev)
     else:
-        fl = f_fwd if dom == "sparse_attn_fwd" else f_bwd
-        ach = fl / (kernels[dom]["ms_mean"] * 1e-3) / 1e12
+        kernels["attn_bwd_f32"] = {"op": "dsv_sparse_attn_bwd", "launches_per_step": 1,
+                                   "ms_per_launch": mean(t_bwd), "ms_median": med(t_bwd),
+                                   "bound": "mfma", "units_per_launch": f_bwd}
+    for kv in kernels.values():
+        kv["ms_per_step"] = kv["ms_per_launch"] * kv["launches_per_step"]
+    dom = max((kn for kn in kernels if kernels[kn]["bound"]),
+              key=lambda kn: kernels[kn]["ms_per_step"])
+    kd = kernels[dom]
+    sec = kd["ms_per_launch"] * 1e-3
+    if kd["bound"] == "hbm":
+        ach = kd["units_per_launch"] / sec / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": ach, "peak": PEAK["hbm_gbs"],
+                "unit": "GB/s", "frac": ach / PEAK["hbm_gbs"]}
+    else:
+        ach = kd["units_per_launch"] / sec / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak,
-                "unit": "TFLOP/s", "frac": ach / peak, "traffic": None}
+                "unit": "TFLOP/s", "frac": ach / peak}
+    roof["traffic"] = counter_traffic(dom, cfg.name)
 
     out = {
         "metric": "sparse attn fwd+bwd TFLOP/s (selected-KV & dense-equiv) + top-k ms, S=64K",
@@ -209,11 +332,21 @@ def main():
         "fwd_ms": mean(t_fwd),
         "bwd_ms": mean(t_bwd),
         "kernels": kernels,
+        "bwd_chunks": nch,
         "roofline": roof,
         "cpu_baseline": None,
     }
     log(f"timed: {ms_step:.3f} ms/step (top-k {mean(t_topk):.3f}, fwd {mean(t_fwd):.3f}, "
         f"bwd {mean(t_bwd):.3f} ms)")
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)   # one elementwise kernel: n*4 bytes read, n*4 written
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB "
+            f"written by one kernel")
+        del src, dst
     if not args.no_cpu_baseline:
         log(f"oracle on host cores for ~{args.cpu_seconds:.0f} s")
         rows = dsv.idx_rows(idx, p, ks, 0, 0).cpu().numpy()

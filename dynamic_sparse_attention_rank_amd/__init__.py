@@ -24,7 +24,8 @@ STATUS = {0: "DSV_OK", 1: "DSV_ERR_NULL", 2: "DSV_ERR_SHAPE", 3: "DSV_ERR_K",
           4: "DSV_ERR_DTYPE", 5: "DSV_ERR_ALIGN", 6: "DSV_ERR_WORKSPACE",
           7: "DSV_ERR_UNSUPPORTED", 8: "DSV_ERR_HIP"}
 EXPORTED = ("dsv_workspace_bytes", "dsv_idx_elems", "dsv_idx_row_offset", "dsv_lowrank_topk",
-            "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd", "dsv_validate", "dsv_status_string",
+            "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd", "dsv_bwd_chunks",
+            "dsv_sparse_attn_bwd_profiled", "dsv_validate", "dsv_status_string",
             "dsv_last_error", "dsv_version")
 
 
@@ -87,6 +88,11 @@ def lib() -> ctypes.CDLL:
         L.dsv_sparse_attn_fwd.argtypes = [P, vp, vp, vp, vp, i32p, f, vp, vp, vp, sz, vp]
         L.dsv_sparse_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32p, f, vp, vp, vp,
                                           vp, sz, vp]
+        L.dsv_sparse_attn_bwd_profiled.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32p, f, vp,
+                                                   vp, vp, vp, sz, vp, ctypes.POINTER(vp),
+                                                   ctypes.c_int]
+        L.dsv_bwd_chunks.argtypes = [P, i32p, sz]
+        L.dsv_bwd_chunks.restype = ctypes.c_int
         L.dsv_validate.argtypes = [ctypes.c_int, P, i32p, ctypes.c_int,
                                    ctypes.POINTER(vp), ctypes.c_int, sz]
         L.dsv_status_string.restype = ctypes.c_char_p
@@ -94,7 +100,7 @@ def lib() -> ctypes.CDLL:
         L.dsv_last_error.restype = ctypes.c_char_p
         L.dsv_version.restype = ctypes.c_char_p
         for fn in ("dsv_lowrank_topk", "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd",
-                   "dsv_validate"):
+                   "dsv_sparse_attn_bwd_profiled", "dsv_validate"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -211,13 +217,19 @@ def sparse_attn_fwd(p: Problem, q, k, v, idx, k_per_head: Sequence[int],
     return o, lse
 
 
+def bwd_chunks(p: Problem, k_per_head: Sequence[int], ws_bytes: int) -> int:
+    """Head chunks the backward uses with a workspace of ws_bytes (-1 if invalid/too small)."""
+    return int(lib().dsv_bwd_chunks(ctypes.byref(p), _kph(k_per_head), ws_bytes))
+
+
 def sparse_attn_bwd(p: Problem, q, k, v, o, d_o, lse, idx, k_per_head: Sequence[int],
                     scale: Optional[float] = None, dq=None, dk=None, dv=None, ws=None,
-                    stream=None):
+                    stream=None, events: Optional[Sequence[int]] = None):
     """(dQ, dK, dV) in fp32 for the query-grouped sparse attention.
 
     `ws` is a device uint8 tensor of at least workspace_bytes(DSV_OP_BWD, ...) bytes; one is
-    allocated for the call when it is None."""
+    allocated for the call when it is None. `events` (profiling, bf16 only): raw hipEvent_t
+    handles, 4 per head chunk, passed to dsv_sparse_attn_bwd_profiled."""
     torch = _torch()
     dt = _storage_dtype(p)
     shp = (p.batch, p.heads, p.seq, p.head_dim)
@@ -239,9 +251,14 @@ def sparse_attn_bwd(p: Problem, q, k, v, o, d_o, lse, idx, k_per_head: Sequence[
         ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     wp = _dev(ws, "ws", torch.uint8) if ws is not None else None
     wn = ws.numel() if ws is not None else 0
-    _check(lib().dsv_sparse_attn_bwd(ctypes.byref(p), *ptr[:6], ptr[6], _kph(k_per_head),
-                                     float(scale), outs[0].data_ptr(), outs[1].data_ptr(),
-                                     outs[2].data_ptr(), wp, wn, _stream_ptr(stream)))
+    args = (ctypes.byref(p), *ptr[:6], ptr[6], _kph(k_per_head), float(scale),
+            outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr(), wp, wn,
+            _stream_ptr(stream))
+    if events is None:
+        _check(lib().dsv_sparse_attn_bwd(*args))
+    else:
+        ev = (ctypes.c_void_p * len(events))(*events)
+        _check(lib().dsv_sparse_attn_bwd_profiled(*args, ev, len(events)))
     return tuple(outs)
 
 

@@ -708,10 +708,57 @@ size_t bwd_workspace_bytes(const Geom& geo) {
   return ws_layout(geo, 1, max_slot_rows(geo)).total;
 }
 
+// Chunk capacity for a workspace: cs slots, ecap staging rows.
+static void chunk_capacity(const Geom& geo, size_t ws_bytes, long long& cs, long long& ecap) {
+  const int nslots = geo.B * geo.H;
+  const long long e1 = max_slot_rows(geo);
+  cs = std::min<long long>(kMaxChunk, nslots);
+  while (cs > 1 && ws_layout(geo, cs, e1).total > ws_bytes) --cs;
+  ecap = e1;   // largest row capacity for this slot capacity
+  const size_t per_row = 4 + 8 + 2 * (size_t)geo.d * sizeof(int16_t);
+  const size_t fixed = ws_layout(geo, cs, 0).total;
+  if (ws_bytes > fixed) ecap = std::max<long long>(e1, (long long)((ws_bytes - fixed) / per_row) - 64);
+  while (ecap > e1 && ws_layout(geo, cs, ecap).total > ws_bytes) ecap -= 64;
+}
+
+// Next chunk of consecutive slots from s0 (at most cs slots, at most ecap staging rows).
+static Chunk next_chunk(const Geom& geo, int s0, long long cs, long long ecap) {
+  const int nslots = geo.B * geo.H;
+  Chunk ch;
+  ch.s0 = s0;
+  ch.n = 0;
+  long long rows = 0;
+  while (s0 + ch.n < nslots && ch.n < cs) {
+    const int h = geo.order[(s0 + ch.n) / geo.B];
+    const long long r = (long long)geo.NG * padded_k(geo.k[h]);
+    if (ch.n > 0 && rows + r > ecap) break;
+    ch.edge_base[ch.n] = rows;
+    rows += r;
+    ++ch.n;
+  }
+  ch.edge_base[ch.n] = rows;
+  return ch;
+}
+
+int bwd_chunk_count(const Geom& geo, size_t ws_bytes) {
+  if (geo.dtype == DSV_FP32) return 1;
+  long long cs, ecap;
+  chunk_capacity(geo, ws_bytes, cs, ecap);
+  int n = 0;
+  for (int s0 = 0; s0 < geo.B * geo.H; ++n) s0 += next_chunk(geo, s0, cs, ecap).n;
+  return n;
+}
+
 int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v, const void* o,
                     const void* d_o, const float* lse, const int32_t* idx, float scale, float* dq,
-                    float* dk, float* dv, void* ws, size_t ws_bytes, void* stream) {
+                    float* dk, float* dv, void* ws, size_t ws_bytes, void* stream,
+                    void* const* events) {
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // optional profiling marks: events[4c + i] before the chunk's pre-passes (i = 0), its
+  // backward kernel (1) and its reduce (2), and after the reduce (3)
+  auto mark = [&](int i) {
+    if (events) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+  };
   if (geo.dtype == DSV_FP32) {
     const long long n4 = (long long)geo.B * geo.H * geo.S * geo.d / 4;
     const int fill_blocks = (int)std::min<long long>((n4 + 255) / 256, 4096);
@@ -737,16 +784,8 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
 
   // ---- bf16 path: chunks of (b, h) slots sized to the workspace
   const int nslots = geo.B * geo.H;
-  const long long e1 = max_slot_rows(geo);
-  long long cs = std::min<long long>(kMaxChunk, nslots);
-  while (cs > 1 && ws_layout(geo, cs, e1).total > ws_bytes) --cs;
-  long long ecap = e1;   // largest row capacity for this slot capacity
-  {
-    const size_t per_row = 4 + 8 + 2 * (size_t)geo.d * sizeof(int16_t);
-    const size_t fixed = ws_layout(geo, cs, 0).total;
-    if (ws_bytes > fixed) ecap = std::max<long long>(e1, (long long)((ws_bytes - fixed) / per_row) - 64);
-    while (ecap > e1 && ws_layout(geo, cs, ecap).total > ws_bytes) ecap -= 64;
-  }
+  long long cs, ecap;
+  chunk_capacity(geo, ws_bytes, cs, ecap);
   const WsLayout L = ws_layout(geo, cs, ecap);
   char* wsb = static_cast<char*>(ws);
   uint32_t* rs = reinterpret_cast<uint32_t*>(wsb + L.rs);
@@ -760,34 +799,26 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
   const int QBn = geo.G / 16;
 
   int s0 = 0;
-  while (s0 < nslots) {
-    Chunk ch;
-    ch.s0 = s0;
-    ch.n = 0;
-    long long rows = 0;
-    while (s0 + ch.n < nslots && ch.n < cs) {
-      const int h = geo.order[(s0 + ch.n) / geo.B];
-      const long long r = (long long)geo.NG * padded_k(geo.k[h]);
-      if (ch.n > 0 && rows + r > ecap) break;
-      ch.edge_base[ch.n] = rows;
-      rows += r;
-      ++ch.n;
-    }
-    ch.edge_base[ch.n] = rows;
+  for (int c = 0; s0 < nslots; ++c) {
+    const Chunk ch = next_chunk(geo, s0, cs, ecap);
     const int rows_waves = ch.n * geo.NG;
+    mark(4 * c);
     hipLaunchKernelGGL(row_bucket_starts, dim3((rows_waves + 3) / 4), dim3(256), 0, st, idx, ch,
                        rs, geo);
     hipLaunchKernelGGL(bucket_totals, dim3(ch.n * nB), dim3(64), 0, st, rs, tot, geo);
     hipLaunchKernelGGL(bucket_offsets, dim3(ch.n), dim3(256), 0, st, tot, off, geo);
     hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64), 0, st, rs, off, ch, perm, geo);
+    mark(4 * c + 1);
 #define DSV_BWD16(DD, QQ)                                                                       \
   if (geo.d == DD && QBn == QQ) {                                                               \
     hipLaunchKernelGGL((attn_bwd_bf16<DD, QQ>), dim3(rows_waves), dim3(64), 0, st,              \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,              \
                        (const uint16_t*)o, (const uint16_t*)d_o, lse, idx, scale, dq, ch, cv,   \
                        ck, rstep, geo);                                                         \
+    mark(4 * c + 2);                                                                            \
     hipLaunchKernelGGL((bucket_reduce<DD>), dim3(ch.n * nB * 2), dim3(64), 0, st, off, perm,    \
                        idx, rstep, cv, ck, ch, dk, dv, geo);                                    \
+    mark(4 * c + 3);                                                                            \
   } else
     DSV_BWD16(64, 1) DSV_BWD16(64, 2) DSV_BWD16(64, 3) DSV_BWD16(64, 4)
     DSV_BWD16(128, 1) DSV_BWD16(128, 2) DSV_BWD16(128, 3) DSV_BWD16(128, 4)

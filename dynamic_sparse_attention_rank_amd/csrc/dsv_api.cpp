@@ -204,20 +204,56 @@ int dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, cons
   return DSV_OK;
 }
 
-int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,
-                        const void* o, const void* d_o, const float* lse, const int32_t* idx,
-                        const int32_t* k_per_head, float scale, float* dq, float* dk, float* dv,
-                        void* ws, size_t ws_bytes, void* stream) {
+static int bwd_common(const dsv_problem* p, const void* q, const void* k, const void* v,
+                      const void* o, const void* d_o, const float* lse, const int32_t* idx,
+                      const int32_t* k_per_head, float scale, float* dq, float* dk, float* dv,
+                      void* ws, size_t ws_bytes, void* stream, void* const* events,
+                      int n_events) {
   const void* ptrs[] = {q, k, v, o, d_o, lse, idx, dq, dk, dv};
   int st = dsv_validate(DSV_OP_BWD, p, k_per_head, DSV_GROUP_SUM, ptrs, 10, ws_bytes);
   if (st != DSV_OK) return st;
   Geom geo;
   validate_problem(p, k_per_head, &geo);
   if (bwd_workspace_bytes(geo) > 0 && (st = check_ptr(ws, "ws", 256)) != DSV_OK) return st;
+  if (events) {
+    if (geo.dtype != DSV_BF16)
+      return fail(DSV_ERR_UNSUPPORTED, "stage events are recorded on the bf16 path only");
+    const int need = 4 * bwd_chunk_count(geo, ws_bytes);
+    if (n_events != need)
+      return fail(DSV_ERR_NULL, "expected %d stage events (4 per head chunk), got %d", need,
+                  n_events);
+    for (int i = 0; i < n_events; ++i)
+      if (!events[i]) return fail(DSV_ERR_NULL, "stage event %d is NULL", i);
+  }
   int e = launch_attn_bwd(geo, q, k, v, o, d_o, lse, idx, scale, dq, dk, dv, ws, ws_bytes,
-                          stream);
+                          stream, events);
   if (e) return fail(DSV_ERR_HIP, "backward launch failed (hipError %d)", e);
   return DSV_OK;
+}
+
+int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,
+                        const void* o, const void* d_o, const float* lse, const int32_t* idx,
+                        const int32_t* k_per_head, float scale, float* dq, float* dk, float* dv,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return bwd_common(p, q, k, v, o, d_o, lse, idx, k_per_head, scale, dq, dk, dv, ws, ws_bytes,
+                    stream, nullptr, 0);
+}
+
+int dsv_bwd_chunks(const dsv_problem* p, const int32_t* k_per_head, size_t ws_bytes) {
+  Geom geo;
+  if (validate_problem(p, k_per_head, &geo) != DSV_OK) return -1;
+  if (ws_bytes < bwd_workspace_bytes(geo)) return -1;
+  return bwd_chunk_count(geo, ws_bytes);
+}
+
+int dsv_sparse_attn_bwd_profiled(const dsv_problem* p, const void* q, const void* k,
+                                 const void* v, const void* o, const void* d_o, const float* lse,
+                                 const int32_t* idx, const int32_t* k_per_head, float scale,
+                                 float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                                 void* stream, void* const* events, int n_events) {
+  if (!events) return fail(DSV_ERR_NULL, "events is NULL");
+  return bwd_common(p, q, k, v, o, d_o, lse, idx, k_per_head, scale, dq, dk, dv, ws, ws_bytes,
+                    stream, events, n_events);
 }
 
 }  // extern "C"

@@ -39,12 +39,16 @@ void set_error(const char* fmt, ...);
 int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int32_t* idx, void* stream);
 int launch_attn_fwd(const Geom& geo, const void* q, const void* k, const void* v,
                     const int32_t* idx, float scale, void* o, float* lse, void* stream);
+// `events` (may be NULL): 4 hipEvent_t per head chunk, recorded around the chunk's stages.
 int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v, const void* o,
                     const void* d_o, const float* lse, const int32_t* idx, float scale, float* dq,
-                    float* dk, float* dv, void* ws, size_t ws_bytes, void* stream);
-// Minimum device workspace of the backward (bf16 path): room for the heaviest (b, h) slot's
-// edge rows (one fp32 dV|dK row of 2d floats + one key index per (group, selected key)) and
-// its bucket offsets. Larger workspaces let one launch cover several (b, h) slots.
+                    float* dk, float* dv, void* ws, size_t ws_bytes, void* stream,
+                    void* const* events);
+// Minimum device workspace of the backward (bf16 path): the bucket tables and staging rows
+// of the heaviest (b, h) slot (per (group, selected key) edge: an int16 dV row and dK row,
+// two fp32 steps and a bucket-list entry). Larger workspaces let a launch cover more slots.
 size_t bwd_workspace_bytes(const Geom& geo);
+// Number of head chunks (launch groups) the backward uses with this workspace (1 on fp32).
+int bwd_chunk_count(const Geom& geo, size_t ws_bytes);
 
 }  // namespace dsv

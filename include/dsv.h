@@ -142,6 +142,23 @@ int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, cons
                         const int32_t* k_per_head, float scale, float* dq, float* dk, float* dv,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Number of head chunks dsv_sparse_attn_bwd uses with a workspace of ws_bytes: the heads
+ * are processed in that many groups of launches, each staging its rows in the workspace.
+ * 1 on the fp32 path; -1 if the problem is invalid or ws_bytes is below the minimum. */
+int dsv_bwd_chunks(const dsv_problem* p, const int32_t* k_per_head, size_t ws_bytes);
+
+/* dsv_sparse_attn_bwd for profiling (bf16 path only): identical work and results, and it
+ * also records caller-created hipEvent_t handles on `stream` around the stages of every head
+ * chunk c: events[4c] before the chunk's index pre-passes, events[4c+1] before its backward
+ * kernel, events[4c+2] before its bucket reduce, events[4c+3] after it. n_events must equal
+ * 4 * dsv_bwd_chunks(p, k_per_head, ws_bytes); the caller owns the events (created with
+ * timing enabled) and reads them after the stream has passed the call. */
+int dsv_sparse_attn_bwd_profiled(const dsv_problem* p, const void* q, const void* k,
+                                 const void* v, const void* o, const void* d_o, const float* lse,
+                                 const int32_t* idx, const int32_t* k_per_head, float scale,
+                                 float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                                 void* stream, void* const* events, int n_events);
+
 /* Validation only: returns the status the corresponding call would return for these
  * arguments before enqueueing anything (no HIP call is made). Pointers are checked for NULL
  * and 16-byte alignment; pass any non-NULL aligned values to check shapes alone. */

@@ -131,3 +131,32 @@ def test_workspace_and_idx_layout_agree_with_oracle():
     bad = dsv.problem(2, 3, 4, 8, 8, 64, 16, (3, 2, 4), "bf16")
     assert dsv.idx_elems(bad, ks) == 0
     assert dsv.workspace_bytes(dsv.DSV_OP_FWD, bad, ks) == np.iinfo(np.uint64).max
+
+
+def test_bwd_chunks_and_profiled_entry_point_validation():
+    """Chunk count follows the workspace; the profiling variant rejects a wrong event count,
+    NULL events and the fp32 path before any HIP call."""
+    L = dsv.lib()
+    p = mid()
+    ks = [6554] * 24
+    need = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks)
+    assert dsv.bwd_chunks(p, ks, need) == 24          # the minimum holds one (b, h) slot
+    assert dsv.bwd_chunks(p, ks, need - 1) == -1
+    big = dsv.bwd_chunks(p, ks, 4 * need)
+    assert 1 <= big < 24
+    assert dsv.bwd_chunks(p, ks, 64 * need) == 1
+    kp = (ctypes.c_int32 * 24)(*ks)
+    args = [ctypes.byref(p)] + [FAKE] * 7 + [kp, 0.1, FAKE, FAKE, FAKE, FAKE, need, None]
+    ev = (ctypes.c_void_p * 96)(*([FAKE] * 96))
+    st = L.dsv_sparse_attn_bwd_profiled(*args, ev, 95)
+    assert dsv.STATUS[st] == "DSV_ERR_NULL" and "stage events" in dsv.last_error()
+    st = L.dsv_sparse_attn_bwd_profiled(*args, None, 96)
+    assert dsv.STATUS[st] == "DSV_ERR_NULL"
+    ev[3] = None
+    st = L.dsv_sparse_attn_bwd_profiled(*args, ev, 96)
+    assert dsv.STATUS[st] == "DSV_ERR_NULL"
+    pf = dsv.problem(1, 2, 4, 16, 16, 64, 16, (2, 2, 4), "fp32")
+    kf = (ctypes.c_int32 * 2)(128, 128)
+    st = L.dsv_sparse_attn_bwd_profiled(ctypes.byref(pf), *([FAKE] * 7), kf, 0.1, FAKE, FAKE,
+                                        FAKE, None, 0, None, ev, 4)
+    assert dsv.STATUS[st] == "DSV_ERR_UNSUPPORTED"

@@ -227,3 +227,44 @@ def test_bwd_edge_cases(label, over, ks):
     if ks[0] == 1:   # a single key per group: dQ = dK = 0
         assert float(dq[0, 0].abs().max()) <= TOL[cfg.dtype]
         assert float(dk[0, 0].abs().max()) <= TOL[cfg.dtype]
+
+
+def test_bwd_profiled_matches_plain_bitwise():
+    """dsv_sparse_attn_bwd_profiled does the same work: bitwise-equal dQ/dK/dV, and its stage
+    events are ordered on the stream."""
+    import ctypes
+    import torch
+    cfg = workload("small", heads=4)
+    say("[bwd] profiled entry point, small x 4 heads")
+    x = gpu_inputs(cfg, backward=True)
+    idx = run_topk(cfg, x)
+    o, lse = run_fwd(cfg, x, idx)
+    p = dsv.problem_for(cfg)
+    ks = x["k_per_head"]
+    need = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks)
+    ws = torch.empty(2 * need, dtype=torch.uint8, device="cuda")
+    nch = dsv.bwd_chunks(p, ks, ws.numel())
+    assert nch >= 2
+    ref = dsv.sparse_attn_bwd(p, x["q"], x["k"], x["v"], o, x["do"], lse, idx, ks, ws=ws)
+    ref = [t.clone() for t in ref]
+    L = dsv.lib()
+    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    evs = []
+    for _ in range(4 * nch):
+        e = ctypes.c_void_p()
+        assert L.hipEventCreate(ctypes.byref(e)) == 0
+        evs.append(e.value)
+    got = dsv.sparse_attn_bwd(p, x["q"], x["k"], x["v"], o, x["do"], lse, idx, ks, ws=ws,
+                              events=evs)
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+    ms = ctypes.c_float()
+    for i in range(len(evs) - 1):
+        assert L.hipEventElapsedTime(ctypes.byref(ms), evs[i], evs[i + 1]) == 0
+        assert ms.value >= 0.0
+    for e in evs:
+        L.hipEventDestroy(e)
