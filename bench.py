@@ -43,17 +43,17 @@ def flops(cfg, ks):
 def bwd_units(cfg, ks):
     """Algorithmic HBM bytes of the two backward kernels for the whole step.
 
-    Backward kernel (per (b,h) slot, E = NG*k edges): the staging rows it writes, E*(4d + 8)
-    (an int16 dV row and dK row, two fp32 steps), the idx row reads, 4E, Q, K, V, O and dO
-    read once, 10*S*d, LSE, 4*S, and dQ written once, 4*S*d (gathered K/V re-reads are cache
-    traffic, not counted). Bucket reduce: the staging rows and steps read once, E*(4d + 8),
-    its edge list and key reads, 8E, and dK and dV written once, 8*S*d."""
+    Backward kernel (per (b,h) slot, E = NG*k edges): the staging rows it writes, 4dE (an
+    fp16 dV row and dK row), their scales, E/2 (two fp32 per 16 rows), the idx row reads, 4E,
+    Q, K, V, O and dO read once, 10*S*d, LSE, 4*S, and dQ written once, 4*S*d (gathered K/V
+    re-reads are cache traffic, not counted). Bucket reduce: the staging rows and scales read
+    once, E*(4d + 1/2), its edge list, 4E, and dK and dV written once, 8*S*d."""
     B, S, d, NG = cfg.batch, cfg.seq, cfg.head_dim, cfg.n_groups
     pass1 = red = 0
     for kh in ks:
         E = NG * kh
-        pass1 += B * (E * (4 * d + 8) + 4 * E + 10 * S * d + 4 * S + 4 * S * d)
-        red += B * (E * (4 * d + 8) + 8 * E + 8 * S * d)
+        pass1 += B * (E * (4 * d + 0.5) + 4 * E + 10 * S * d + 4 * S + 4 * S * d)
+        red += B * (E * (4 * d + 0.5) + 4 * E + 8 * S * d)
     return pass1, red
 
 

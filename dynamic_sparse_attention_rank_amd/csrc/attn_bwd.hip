@@ -58,17 +58,33 @@ __device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, i
 constexpr int kBucketLog2 = 5;
 constexpr int kBucket = 1 << kBucketLog2;
 constexpr int kMaxChunk = 64;    // (b, h) slots per chunk
-// dV|dK rows are stored as int16 * step with |entry| <= bound; 32000 of 32767 levels leave a
-// margin for the fp32 accumulation and bf16 operand rounding inside the bound.
-constexpr float kQLevels = 32000.f;
-constexpr float kPkScale = kQLevels / 32767.f;   // v_cvt_pknorm_i16_f32 multiplies by 32767
+// Staged dV|dK partial rows are fp16 times one power-of-two scale per (group, 16-key block):
+// kStageMax / bound rounded down to a power of two keeps every scaled entry within
+// kStageMax (fp16 reaches 65504), and fp16's 11-bit significand gives each entry a relative
+// error <= 2^-11 whatever its size, down to 2^-28 of the bound where fp16 turns subnormal.
+constexpr float kStageMax = 16384.f;
 
-// kPkScale / bound rounded down to a power of two (clamped to [2^-126, 2^100]); 0 if bound is
-// not positive.
+// kStageMax / bound rounded down to a power of two (clamped to [2^-126, 2^100]); 0 if bound
+// is not positive.
 __device__ __forceinline__ float pow2_scale(float bound) {
   if (!(bound > 0.f)) return 0.f;
-  const float x = fminf(fmaxf(kPkScale * __builtin_amdgcn_rcpf(bound), 1.17549435e-38f), 1.2676506e30f);
+  const float x =
+      fminf(fmaxf(kStageMax * __builtin_amdgcn_rcpf(bound), 1.17549435e-38f), 1.2676506e30f);
   return __uint_as_float(__float_as_uint(x) & 0xff800000u);
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 v;
+  v.x = (_Float16)lo;
+  v.y = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
 __host__ __device__ inline int n_buckets(int S) { return (S + kBucket - 1) / kBucket; }
@@ -162,10 +178,12 @@ __global__ __launch_bounds__(256) void bucket_offsets(const uint32_t* __restrict
 }
 
 // Bucket-ordered edge list: perm[off[j] + i], i < tot[j], holds the edges (g, p) whose key
-// lies in bucket j, as the slot-relative staging row g*padded_k + p, ordered by group, then
-// by position. One wave per (slot, bucket); 64 groups per step, positions from a wave scan.
+// lies in bucket j, ordered by group, then by position, each as (slot-relative staging row
+// g*padded_k + p) << 5 | (key - 32 j). One wave per (slot, bucket); 64 groups per step,
+// positions from a wave scan; the keys of a step's runs are read 8 per lane at a time.
 __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ rs,
-                                                  const uint32_t* __restrict__ off, Chunk ch,
+                                                  const uint32_t* __restrict__ off,
+                                                  const int32_t* __restrict__ idx, Chunk ch,
                                                   uint32_t* __restrict__ perm, Geom geo) {
   const int nB = n_buckets(geo.S);
   const int sl = blockIdx.x / nB;
@@ -173,10 +191,13 @@ __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ r
   const int lane = threadIdx.x;
   int b, h;
   chunk_slot(geo, ch.s0 + sl, b, h);
+  const uint32_t kh = (uint32_t)geo.k[h];
   const uint32_t kp = (uint32_t)padded_k(geo.k[h]);
   const uint32_t slot_rows = (uint32_t)(ch.edge_base[sl + 1] - ch.edge_base[sl]);
   const uint32_t* r = rs + (long long)sl * geo.NG * (nB + 1);
+  const int32_t* keys = idx + geo.row_offset(b, h, 0);   // row of group g: keys + g*k
   uint32_t* pm = perm + ch.edge_base[sl];
+  const int key0 = j * kBucket;
   uint32_t pos0 = off[(long long)sl * (nB + 1) + j];
   for (int g0 = 0; g0 < geo.NG; g0 += 64) {
     const int g = g0 + lane;
@@ -193,8 +214,24 @@ __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ r
     }
     const uint32_t pos = pos0 + incl - len;
     const uint32_t e0 = (uint32_t)g * kp + a;
-    for (uint32_t i = 0; i < len; ++i)
-      if (pos + i < slot_rows) pm[pos + i] = e0 + i;   // a malformed row is dropped
+    const int32_t* krow = keys + (long long)g * kh + a;
+    uint32_t maxlen = len;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) maxlen = max(maxlen, (uint32_t)__shfl_xor((int)maxlen, m, 64));
+    for (uint32_t i0 = 0; i0 < maxlen; i0 += 8) {
+      int kv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kv[u] = i0 + u < len ? krow[i0 + u] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = i0 + u;
+        // a malformed row is dropped rather than written past the slot's list
+        if (i < len && pos + i < slot_rows) {
+          const int ko = min(max(clamp_key(kv[u], geo.S) - key0, 0), kBucket - 1);
+          pm[pos + i] = ((e0 + i) << 5) | (uint32_t)ko;
+        }
+      }
+    }
     pos0 += __shfl(incl, 63, 64);
   }
 }
@@ -214,10 +251,9 @@ __global__ void fill_zero(float4* __restrict__ p, long long n4) {
 template <int D>
 __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__ off,
                                                    const uint32_t* __restrict__ perm,
-                                                   const int32_t* __restrict__ idx,
-                                                   const float2* __restrict__ rstep,
-                                                   const int16_t* __restrict__ cv,
-                                                   const int16_t* __restrict__ ck, Chunk ch,
+                                                   const float2* __restrict__ bstep,
+                                                   const uint16_t* __restrict__ cv,
+                                                   const uint16_t* __restrict__ ck, Chunk ch,
                                                    float* __restrict__ dk, float* __restrict__ dv,
                                                    Geom geo) {
   constexpr int FPL = D / 64;   // features per lane
@@ -241,9 +277,7 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
   const long long s0 = std::min<long long>(o[j], nrows);
   const long long s1 = std::min<long long>(std::max<long long>(o[j + 1], o[j]), nrows);
   const uint32_t* pm = perm + eb;
-  const int32_t* keys = idx + geo.row_offset(b, h, 0);   // row of group g: keys + g*k
-  const uint32_t kh = (uint32_t)geo.k[h], kp = (uint32_t)padded_k(geo.k[h]);
-  const int16_t* src = (half ? ck : cv) + eb * D + FPL * lane;
+  const uint16_t* src = (half ? ck : cv) + eb * D + FPL * lane;
   const int key0 = j * kBucket;
   for (long long r0 = s0; r0 < s1; r0 += 64) {
     const int n = (int)std::min<long long>(64, s1 - r0);
@@ -252,10 +286,10 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
     int kk = 0;
     float sc = 0.f;
     if (lane < n) {
-      e = std::min<uint32_t>(pm[r0 + lane], (uint32_t)(nrows - 1));
-      const uint32_t gq = e / kp, pq = std::min(e - gq * kp, kh - 1);
-      kk = min(max(clamp_key(keys[(long long)gq * kh + pq], geo.S) - key0, 0), kBucket - 1);
-      const float2 st = rstep[eb + e];
+      const uint32_t ent = pm[r0 + lane];
+      e = std::min<uint32_t>(ent >> 5, (uint32_t)(nrows - 1));
+      kk = (int)(ent & 31u);
+      const float2 st = bstep[(eb + e) >> 4];   // the step of the row's 16-key block
       sc = half ? st.y : st.x;
     }
     for (int u0 = 0; u0 < n; u0 += U) {
@@ -275,11 +309,11 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
         float* a = acc + ku * D + FPL * lane;
         if constexpr (FPL == 2) {
           float2 w = *reinterpret_cast<float2*>(a);
-          w.x += su * (float)(int16_t)(x[u] & 0xffffu);
-          w.y += su * (float)(int16_t)(x[u] >> 16);
+          w.x += su * f16_lo(x[u]);
+          w.y += su * f16_hi(x[u]);
           *reinterpret_cast<float2*>(a) = w;
         } else {
-          a[0] += su * (float)(int16_t)x[u];
+          a[0] += su * f16_lo(x[u]);
         }
       }
     }
@@ -315,7 +349,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     const uint16_t* v, const uint16_t* __restrict__ o,   // prefetch stays ordered (see below)
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
     const int32_t* __restrict__ idx, float scale, float* __restrict__ dq, Chunk ch,
-    int16_t* __restrict__ cv, int16_t* __restrict__ ck, float2* __restrict__ rstep, Geom geo) {
+    uint16_t* __restrict__ cv, uint16_t* __restrict__ ck, float2* __restrict__ bstep, Geom geo) {
   constexpr int QBP = (QB + 1) & ~1;   // query blocks padded to whole 32-query k-steps
   constexpr int NM = QBP / 2;
   constexpr int KS = D / 32;
@@ -455,14 +489,12 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       for (int qb = QB; qb < QBP; ++qb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) pv[qb][j] = dsv_[qb][j] = 0.f;
-      // The dV and dK rows of this chunk's edges are staged as 16-bit integers times one fp32
-      // step per half. |dV[d]| <= sum_n P * max|dO| and |dK[d]| <= scale * sum_n |dS| * max|Q|
-      // bound every entry of the key's rows. The lane's key is 16kb + li: its P and dS are
-      // multiplied by sv, sk = kQLevels / (32767 * bound) rounded down to a power of two
-      // before they become bf16 MFMA operands (a power of two commutes with the bf16 rounding,
-      // so the operands are exactly the rounded P and dS, scaled), the products then lie in
-      // [-1, 1] and v_cvt_pknorm_i16_f32 quantizes two of them per instruction: the key's
-      // rows use between 16000 and 32000 of the 32767 levels, error <= step / 2 per entry.
+      // The dV and dK rows of this chunk's edges are staged in fp16 with one power-of-two
+      // scale per 16-key block (kb). |dV[d]| <= sum_n P * max|dO| and |dK[d]| <= scale *
+      // sum_n |dS| * max|Q| bound every entry of a key's rows; the block's largest bound sets
+      // sv, sk (pow2_scale). P and dS are multiplied by them before they become bf16 MFMA
+      // operands (a power of two commutes with the bf16 rounding, so the operands are
+      // exactly the rounded P and dS, scaled), and the products go to fp16 as they are.
       {
         float cp = 0.f, cd = 0.f;
 #pragma unroll
@@ -476,13 +508,18 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         cp = wave_xor_sum(cp, 32);
         cd = wave_xor_sum(cd, 16);
         cd = wave_xor_sum(cd, 32);
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {   // largest column bound of the 16 keys
+          cp = wave_xor_max(cp, m);
+          cd = wave_xor_max(cd, m);
+        }
         const float sv = pow2_scale(cp * max_do);
         const float sk = pow2_scale(cd * max_q);   // dK = scale * (sum dS q): scale in the step
-        // the four lanes of a key store the same value (an unconditional store)
-        // (sv, sk are powers of two, so their reciprocals are exact)
-        rstep[grow + cb + 16 * kb + li] =
-            make_float2(sv > 0.f ? __builtin_amdgcn_rcpf(sv) * (1.f / 32767.f) : 0.f,
-                        sk > 0.f ? __builtin_amdgcn_rcpf(sk) * (scale / 32767.f) : 0.f);
+        // every lane stores the block's step (one address: an unconditional store); sv, sk are
+        // powers of two, so their reciprocals are exact
+        bstep[(grow + cb) / 16 + kb] =
+            make_float2(sv > 0.f ? __builtin_amdgcn_rcpf(sv) : 0.f,
+                        sk > 0.f ? __builtin_amdgcn_rcpf(sk) * scale : 0.f);
         // B operands of dO^T P / Q^T dS: column li <-> key, slot (lg, e) <-> member
         // 16(2m + e/4) + 4lg + e%4
 #pragma unroll
@@ -568,12 +605,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       for (int kb = 0; kb < 2; ++kb) {
         // row cb + 16kb + li < padded_k: past the row end it is a (zero) padding row
         const long long off = (grow + cb + 16 * kb + li) * D + 16 * fb + 4 * lg;
-        const u32x2 wv = {
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(av[kb][0], av[kb][1])),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(av[kb][2], av[kb][3]))};
-        const u32x2 wk = {
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(ak[kb][0], ak[kb][1])),
-            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(ak[kb][2], ak[kb][3]))};
+        const u32x2 wv = {pack_f16(av[kb][0], av[kb][1]), pack_f16(av[kb][2], av[kb][3])};
+        const u32x2 wk = {pack_f16(ak[kb][0], ak[kb][1]), pack_f16(ak[kb][2], ak[kb][3])};
         *reinterpret_cast<u32x2*>(cv + off) = wv;
         *reinterpret_cast<u32x2*>(ck + off) = wk;
       }
@@ -678,7 +711,7 @@ __global__ __launch_bounds__(64) void attn_bwd_f32(
 
 // Workspace layout for a chunk capacity of `cs` slots and `e` staging rows:
 //   [rs: cs*NG*(nB+1) u32][tot: cs*(nB+1) u32][off: cs*(nB+1) u32][perm: e u32]
-//   [step: e float2][dV rows: e*d int16][dK rows: e*d int16], every region 256-byte aligned.
+//   [steps: e/16 float2][dV rows: e*d fp16][dK rows: e*d fp16], every region 256-byte aligned.
 struct WsLayout {
   size_t rs, tot, off, perm, step, cv, ck, total;
 };
@@ -691,9 +724,9 @@ static WsLayout ws_layout(const Geom& geo, long long cs, long long e) {
   L.off = L.tot + al(cs * (nb + 1) * 4);
   L.perm = L.off + al(cs * (nb + 1) * 4);
   L.step = L.perm + al((size_t)e * 4);
-  L.cv = L.step + al((size_t)e * 8);
-  L.ck = L.cv + al((size_t)e * geo.d * sizeof(int16_t));
-  L.total = L.ck + (size_t)e * geo.d * sizeof(int16_t);
+  L.cv = L.step + al((size_t)e / 16 * 8);
+  L.ck = L.cv + al((size_t)e * geo.d * sizeof(uint16_t));
+  L.total = L.ck + (size_t)e * geo.d * sizeof(uint16_t);
   return L;
 }
 
@@ -715,7 +748,7 @@ static void chunk_capacity(const Geom& geo, size_t ws_bytes, long long& cs, long
   cs = std::min<long long>(kMaxChunk, nslots);
   while (cs > 1 && ws_layout(geo, cs, e1).total > ws_bytes) --cs;
   ecap = e1;   // largest row capacity for this slot capacity
-  const size_t per_row = 4 + 8 + 2 * (size_t)geo.d * sizeof(int16_t);
+  const size_t per_row = 4 + 1 + 2 * (size_t)geo.d * sizeof(uint16_t);
   const size_t fixed = ws_layout(geo, cs, 0).total;
   if (ws_bytes > fixed) ecap = std::max<long long>(e1, (long long)((ws_bytes - fixed) / per_row) - 64);
   while (ecap > e1 && ws_layout(geo, cs, ecap).total > ws_bytes) ecap -= 64;
@@ -792,9 +825,9 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
   uint32_t* tot = reinterpret_cast<uint32_t*>(wsb + L.tot);
   uint32_t* off = reinterpret_cast<uint32_t*>(wsb + L.off);
   uint32_t* perm = reinterpret_cast<uint32_t*>(wsb + L.perm);
-  float2* rstep = reinterpret_cast<float2*>(wsb + L.step);
-  int16_t* cv = reinterpret_cast<int16_t*>(wsb + L.cv);
-  int16_t* ck = reinterpret_cast<int16_t*>(wsb + L.ck);
+  float2* bstep = reinterpret_cast<float2*>(wsb + L.step);
+  uint16_t* cv = reinterpret_cast<uint16_t*>(wsb + L.cv);
+  uint16_t* ck = reinterpret_cast<uint16_t*>(wsb + L.ck);
   const int nB = n_buckets(geo.S);
   const int QBn = geo.G / 16;
 
@@ -807,17 +840,18 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
                        rs, geo);
     hipLaunchKernelGGL(bucket_totals, dim3(ch.n * nB), dim3(64), 0, st, rs, tot, geo);
     hipLaunchKernelGGL(bucket_offsets, dim3(ch.n), dim3(256), 0, st, tot, off, geo);
-    hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64), 0, st, rs, off, ch, perm, geo);
+    hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64), 0, st, rs, off, idx, ch, perm,
+                       geo);
     mark(4 * c + 1);
 #define DSV_BWD16(DD, QQ)                                                                       \
   if (geo.d == DD && QBn == QQ) {                                                               \
     hipLaunchKernelGGL((attn_bwd_bf16<DD, QQ>), dim3(rows_waves), dim3(64), 0, st,              \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,              \
                        (const uint16_t*)o, (const uint16_t*)d_o, lse, idx, scale, dq, ch, cv,   \
-                       ck, rstep, geo);                                                         \
+                       ck, bstep, geo);                                                         \
     mark(4 * c + 2);                                                                            \
     hipLaunchKernelGGL((bucket_reduce<DD>), dim3(ch.n * nB * 2), dim3(64), 0, st, off, perm,    \
-                       idx, rstep, cv, ck, ch, dk, dv, geo);                                    \
+                       bstep, cv, ck, ch, dk, dv, geo);                                         \
     mark(4 * c + 3);                                                                            \
   } else
     DSV_BWD16(64, 1) DSV_BWD16(64, 2) DSV_BWD16(64, 3) DSV_BWD16(64, 4)

@@ -166,8 +166,8 @@ int dsv_validate(int op, const dsv_problem* p, const int32_t* k_per_head, int re
     int kmax = 0;
     for (int h = 0; h < geo.H; ++h) kmax = std::max(kmax, geo.k[h]);
     const long long rows = (long long)geo.NG * ((kmax + 31) & ~31);
-    if (rows >= (1LL << 31))
-      return fail(DSV_ERR_UNSUPPORTED, "backward: %lld staging rows per head exceed 2^31", rows);
+    if (rows >= (1LL << 27))
+      return fail(DSV_ERR_UNSUPPORTED, "backward: %lld staging rows per head exceed 2^27", rows);
   }
   const size_t need = op == DSV_OP_BWD ? bwd_workspace_bytes(geo) : 0;
   if (ws_bytes < need)

@@ -81,8 +81,8 @@ typedef struct {
 
 /* Minimum bytes of device workspace `op` needs for this problem. DSV_OP_TOPK and DSV_OP_FWD
  * need none (their ws may be NULL). DSV_OP_BWD on the bf16 path needs the per-edge dV|dK
- * staging rows of one (b,h) head (NG*k32*(4*d + 12) bytes, k32 = max k rounded up to a
- * multiple of 32, plus small per-bucket tables); a
+ * staging rows of one (b,h) head (about NG*k32*(4*d + 4.5) bytes, k32 = max k rounded up
+ * to a multiple of 32, plus small per-bucket tables); a
  * larger workspace lets one launch cover several heads. The fp32 path needs none.
  * Returns (size_t)-1 if the problem is invalid. */
 size_t dsv_workspace_bytes(int op, const dsv_problem* p, const int32_t* k_per_head);
@@ -132,11 +132,12 @@ int dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, cons
  *              (bf16 path); owned by the caller, contents on entry ignored, clobbered.
  * With P = exp(scale*q.k - LSE), Delta_n = dO_n.O_n, dS = P*(dO.v - Delta):
  *   dQ_n = scale*sum_m dS[n,m] k_m,  dK_m = scale*sum_n dS[n,m] q_n,  dV_m = sum_n P[n,m] dO_n.
- * bf16 path: each (group, selected key) edge writes its dV and dK rows to a fixed slot of the
- * key's 64-key bucket in ws, as 16-bit integers with one fp32 step per row half (the step is
- * an a-priori bound of the half / 32000); a second kernel sums each bucket's slots in a fixed
- * order. dK/dV are therefore bitwise reproducible from run to run. The stream is used for
- * several launches per call (heads are processed in chunks that fit ws). */
+ * bf16 path: each (group, selected key) edge writes its partial dV and dK rows to its own
+ * staging row in ws, in fp16 scaled by a power of two per (group, 16-key block) chosen from an
+ * a-priori bound (relative error <= 2^-11 per entry); a second kernel sums each 32-key
+ * bucket's rows in a fixed order. dK/dV are therefore bitwise reproducible from run to run.
+ * The stream is used for several launches per call (heads are processed in chunks that fit
+ * ws). Unsupported (DSV_ERR_UNSUPPORTED) when NG * k32 >= 2^27 staging rows per head. */
 int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,
                         const void* o, const void* d_o, const float* lse, const int32_t* idx,
                         const int32_t* k_per_head, float scale, float* dq, float* dk, float* dv,
