@@ -211,10 +211,13 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
     for (int t = 0; t < ntiles; ++t) {
       const int buf = t & 1;
       if (t + 1 < ntiles) load_tile(t + 1, regs);
-#pragma unroll 2
+      floatx4 accs[TK_TILE / 16];   // all sub-tiles' scores first: the LDS reads and MFMAs
+#pragma unroll                     // of the tile overlap instead of waiting one by one
+      for (int sub = 0; sub < TK_TILE / 16; ++sub) accs[sub] = tile_scores(buf, sub);
+#pragma unroll
       for (int sub = 0; sub < TK_TILE / 16; ++sub) {
         const int m = t * TK_TILE + sub * 16 + li;
-        const floatx4 acc = tile_scores(buf, sub);
+        const floatx4 acc = accs[sub];
         const bool mvalid = m < S;
         if (pass < 4) {
 #pragma unroll
