@@ -320,7 +320,12 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
   }
   __syncthreads();
   const int nk = min(kBucket, geo.S - key0);
-  float* out = (half ? dk : dv) + bh * geo.S * D + (long long)key0 * D + FPL * lane;
+  // staging position FPL*lane holds feature 32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4
+  // (position 32fp + 8lg + t); FPL consecutive positions stay consecutive features
+  const int pos = FPL * lane;
+  const int t8 = pos & 7;
+  const int feat = (pos & ~31) + 4 * ((pos >> 3) & 3) + (t8 < 4 ? t8 : 12 + t8);
+  float* out = (half ? dk : dv) + bh * geo.S * D + (long long)key0 * D + feat;
   for (int l = 0; l < nk; ++l) {
     if constexpr (FPL == 2)
       *reinterpret_cast<float2*>(out + (long long)l * D) =
@@ -462,6 +467,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     // ---- S = Q K^T, dP = dO V^T ; lane: key 16kb + li, members 16qb + 4lg + j. The A
     // operands (member 16qb + li, features 32ks + 8lg ..) are 16-byte LDS row reads.
     u32x4 pa[2][NM], dsa[2][NM];
+    float2 step[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const bool kvalid = cb + 16 * kb + li < kh;
@@ -515,11 +521,9 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         }
         const float sv = pow2_scale(cp * max_do);
         const float sk = pow2_scale(cd * max_q);   // dK = scale * (sum dS q): scale in the step
-        // every lane stores the block's step (one address: an unconditional store); sv, sk are
-        // powers of two, so their reciprocals are exact
-        bstep[(grow + cb) / 16 + kb] =
-            make_float2(sv > 0.f ? __builtin_amdgcn_rcpf(sv) : 0.f,
-                        sk > 0.f ? __builtin_amdgcn_rcpf(sk) * scale : 0.f);
+        // sv, sk are powers of two, so their reciprocals are exact
+        step[kb] = make_float2(sv > 0.f ? __builtin_amdgcn_rcpf(sv) : 0.f,
+                               sk > 0.f ? __builtin_amdgcn_rcpf(sk) * scale : 0.f);
         // B operands of dO^T P / Q^T dS: column li <-> key, slot (lg, e) <-> member
         // 16(2m + e/4) + 4lg + e%4
 #pragma unroll
@@ -543,6 +547,11 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
           lds.ds[(qb * 16 + 4 * lg + j) * 40 + 16 * kb + li] = (uint16_t)(w & 0xffffu);
         }
     }
+
+    // both blocks' steps in one 16-byte store by every lane (one address, unconditional);
+    // (grow + cb) is a multiple of 32, so the pair is 16-byte aligned
+    *reinterpret_cast<float4*>(&bstep[(grow + cb) / 16]) =
+        make_float4(step[0].x, step[0].y, step[1].x, step[1].y);
 
     // ---- dQ^T += K^T dS^T. The A operand K^T (row li <-> feature 16fb + li, slot (lg, e) <->
     // key 4lg + e for e < 4, 16 + 4lg + e - 4 for e >= 4) is made from the natural K rows
@@ -579,36 +588,46 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
 
     // ---- dV^T = dO^T P, dK^T = Q^T dS (pre-scaled, see above). A operands by transposed LDS
     // reads: row li <-> feature 16fb + li, slot (lg, e) <-> member 32m + 16(e/4) + 4lg + e%4.
-    // Lane: key 16kb + li, features 16fb + 4lg + j; each staging row gets 8 bytes per lane.
+    // Lane: key 16kb + li, features 16fb + 4lg + j. Feature blocks go in pairs (2fp, 2fp + 1)
+    // so that every lane stores 16 bytes: staging position 32fp + 8lg + t holds feature
+    // 32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4 (t >= 4); the reduce undoes this order.
 #pragma unroll
-    for (int fb = 0; fb < NDB; ++fb) {
-      floatx4 av[2], ak[2];
+    for (int fp = 0; fp < NDB / 2; ++fp) {
+      floatx4 av[2][2], ak[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) av[kb] = ak[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const int r1 = 32 * m + 4 * lg + (li >> 2);
-        const int col = 16 * fb + 4 * (li & 3);
-        const u32x2 d1 = lds_read_tr16(&lds.dn[swz<D>(r1, col)]);
-        const u32x2 d2 = lds_read_tr16(&lds.dn[swz<D>(r1 + 16, col)]);
-        const u32x2 q1 = lds_read_tr16(&lds.qn[swz<D>(r1, col)]);
-        const u32x2 q2 = lds_read_tr16(&lds.qn[swz<D>(r1 + 16, col)]);
-        const u32x4 adoT = {d1[0], d1[1], d2[0], d2[1]};
-        const u32x4 aqT = {q1[0], q1[1], q2[0], q2[1]};
+        for (int kb = 0; kb < 2; ++kb) av[h2][kb] = ak[h2][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          av[kb] = mfma_bf16(adoT, pa[kb][m], av[kb]);
-          ak[kb] = mfma_bf16(aqT, dsa[kb][m], ak[kb]);
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int fb = 2 * fp + h2;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const int r1 = 32 * m + 4 * lg + (li >> 2);
+          const int col = 16 * fb + 4 * (li & 3);
+          const u32x2 d1 = lds_read_tr16(&lds.dn[swz<D>(r1, col)]);
+          const u32x2 d2 = lds_read_tr16(&lds.dn[swz<D>(r1 + 16, col)]);
+          const u32x2 q1 = lds_read_tr16(&lds.qn[swz<D>(r1, col)]);
+          const u32x2 q2 = lds_read_tr16(&lds.qn[swz<D>(r1 + 16, col)]);
+          const u32x4 adoT = {d1[0], d1[1], d2[0], d2[1]};
+          const u32x4 aqT = {q1[0], q1[1], q2[0], q2[1]};
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            av[h2][kb] = mfma_bf16(adoT, pa[kb][m], av[h2][kb]);
+            ak[h2][kb] = mfma_bf16(aqT, dsa[kb][m], ak[h2][kb]);
+          }
         }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // row cb + 16kb + li < padded_k: past the row end it is a (zero) padding row
-        const long long off = (grow + cb + 16 * kb + li) * D + 16 * fb + 4 * lg;
-        const u32x2 wv = {pack_f16(av[kb][0], av[kb][1]), pack_f16(av[kb][2], av[kb][3])};
-        const u32x2 wk = {pack_f16(ak[kb][0], ak[kb][1]), pack_f16(ak[kb][2], ak[kb][3])};
-        *reinterpret_cast<u32x2*>(cv + off) = wv;
-        *reinterpret_cast<u32x2*>(ck + off) = wk;
+        const long long off = (grow + cb + 16 * kb + li) * D + 32 * fp + 8 * lg;
+        const u32x4 wv = {pack_f16(av[0][kb][0], av[0][kb][1]), pack_f16(av[0][kb][2], av[0][kb][3]),
+                          pack_f16(av[1][kb][0], av[1][kb][1]), pack_f16(av[1][kb][2], av[1][kb][3])};
+        const u32x4 wk = {pack_f16(ak[0][kb][0], ak[0][kb][1]), pack_f16(ak[0][kb][2], ak[0][kb][3]),
+                          pack_f16(ak[1][kb][0], ak[1][kb][1]), pack_f16(ak[1][kb][2], ak[1][kb][3])};
+        *reinterpret_cast<u32x4*>(cv + off) = wv;
+        *reinterpret_cast<u32x4*>(ck + off) = wk;
       }
     }
     wave_lds_fence();   // the next chunk overwrites the dS tile
