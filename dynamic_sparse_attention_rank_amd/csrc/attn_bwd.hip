@@ -343,7 +343,7 @@ template <int D>
 struct BwdLds {
   uint16_t qn[64 * D];
   uint16_t dn[64 * D];
-  uint16_t ds[64 * 40];   // dS tile [query][key], 32 keys + 8 pad per row
+  uint16_t ds[32 * 80];   // dS tile [key][member], 64 members + 16 pad per row (160 bytes)
   float lse2[64] __attribute__((aligned(16)));    // LSE * log2(e) per group member
   float delta[64] __attribute__((aligned(16)));   // Delta per group member
 };
@@ -464,31 +464,39 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
   // prefetched K/V rows at the top of the loop then leaves the previous chunk's stores in
   // flight instead of draining them.
   auto chunk = [&](const int cb) {
-    // ---- S = Q K^T, dP = dO V^T ; lane: key 16kb + li, members 16qb + 4lg + j. The A
-    // operands (member 16qb + li, features 32ks + 8lg ..) are 16-byte LDS row reads.
+    // ---- S = Q K^T, dP = dO V^T of 16-key block kb; lane: key 16kb + li, members 16qb +
+    // 4lg + j. The A operands (member 16qb + li, features 32ks + 8lg ..) are 16-byte LDS row
+    // reads.
+    auto s_dp = [&](const int kb, floatx4 (&s)[QB], floatx4 (&dp)[QB]) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        s[qb] = dp[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int off = swz<D>(qb * 16 + li, 32 * ks + 8 * lg);
+          s[qb] = mfma_bf16(*reinterpret_cast<const u32x4*>(&lds.qn[off]), kb_n[kb][ks], s[qb]);
+          dp[qb] =
+              mfma_bf16(*reinterpret_cast<const u32x4*>(&lds.dn[off]), vb_n[kb][ks], dp[qb]);
+        }
+      }
+    };
     u32x4 pa[2][NM], dsa[2][NM];
     float2 step[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    // ---- P, dS of block kb, their fp16 staging scales, the dV / dK operands and the dS tile
+    auto softmax = [&](const int kb, const floatx4 (&s)[QB], const floatx4 (&dp)[QB]) {
       const bool kvalid = cb + 16 * kb + li < kh;
       float pv[QBP][4], dsv_[QBP][4];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        floatx4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = swz<D>(qb * 16 + li, 32 * ks + 8 * lg);
-          s = mfma_bf16(*reinterpret_cast<const u32x4*>(&lds.qn[off]), kb_n[kb][ks], s);
-          dp = mfma_bf16(*reinterpret_cast<const u32x4*>(&lds.dn[off]), vb_n[kb][ks], dp);
-        }
         // LSE / Delta of the members this tile gives the lane: 16qb + 4lg + j
         const floatx4 l2 = *reinterpret_cast<const floatx4*>(&lds.lse2[qb * 16 + 4 * lg]);
         const floatx4 dl = *reinterpret_cast<const floatx4*>(&lds.delta[qb * 16 + 4 * lg]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = kvalid ? __builtin_amdgcn_exp2f(fmaf(s[j], c2, -l2[j])) : 0.f;
+          const float p =
+              kvalid ? __builtin_amdgcn_exp2f(fmaf(s[qb][j], c2, -l2[j])) : 0.f;
           pv[qb][j] = p;
-          dsv_[qb][j] = p * (dp[j] - dl[j]);
+          dsv_[qb][j] = p * (dp[qb][j] - dl[j]);
         }
       }
 #pragma unroll
@@ -510,15 +518,9 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
             cp += pv[qb][j];
             cd += fabsf(dsv_[qb][j]);
           }
-        cp = wave_xor_sum(cp, 16);
-        cp = wave_xor_sum(cp, 32);
-        cd = wave_xor_sum(cd, 16);
-        cd = wave_xor_sum(cd, 32);
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {   // largest column bound of the 16 keys
-          cp = wave_xor_max(cp, m);
-          cd = wave_xor_max(cd, m);
-        }
+        // column sums over the members, then the largest column bound of the 16 keys
+        cp = max_in_row16(sum_over_rows(cp));
+        cd = max_in_row16(sum_over_rows(cd));
         const float sv = pow2_scale(cp * max_do);
         const float sk = pow2_scale(cd * max_q);   // dK = scale * (sum dS q): scale in the step
         // sv, sk are powers of two, so their reciprocals are exact
@@ -538,53 +540,66 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
           dsa[kb][m][3] = pack_bf16(dsv_[2 * m + 1][2] * sk, dsv_[2 * m + 1][3] * sk);
         }
       }
-      // dS tile (unscaled) -> LDS as [member][key]
+      // dS tile (unscaled) -> LDS as [key][member]: the lane's 4 members are adjacent
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t w = pack_bf16(dsv_[qb][j], 0.f);
-          lds.ds[(qb * 16 + 4 * lg + j) * 40 + 16 * kb + li] = (uint16_t)(w & 0xffffu);
-        }
+        *reinterpret_cast<u32x2*>(&lds.ds[(16 * kb + li) * 80 + 16 * qb + 4 * lg]) =
+            u32x2{pack_bf16(dsv_[qb][0], dsv_[qb][1]), pack_bf16(dsv_[qb][2], dsv_[qb][3])};
+    };
+    {
+      floatx4 s0[QB], dp0[QB];
+      s_dp(0, s0, dp0);
+      softmax(0, s0, dp0);
     }
+    floatx4 s1[QB], dp1[QB];
+    s_dp(1, s1, dp1);
+    // ---- K^T operands of dQ^T += K^T dS^T (row li <-> feature 16fb + li, slot (lg, e) <->
+    // key 4lg + e for e < 4, 16 + 4lg + e - 4 for e >= 4), made from the natural K rows now:
+    // kb_n x sel moves feature block fb of each 16-key tile into the C layout (lane li <->
+    // feature, keys 4lg + j), which packed to bf16 is exactly that operand.
+    u32x4 kT[NDB];
+#pragma unroll
+    for (int fb = 0; fb < NDB; ++fb) {
+      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+      const floatx4 t0 = mfma_bf16(kb_n[0][fb >> 1], sel[fb & 1], z);
+      const floatx4 t1 = mfma_bf16(kb_n[1][fb >> 1], sel[fb & 1], z);
+      kT[fb] = u32x4{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]),
+                     pack_bf16(t1[2], t1[3])};
+    }
+    // The natural K/V registers are free again: request the next chunk's rows (past the end
+    // the clamped positions reload the last key) and the keys of the one after, so that the
+    // gathers have the rest of this chunk to arrive. The compiler barriers keep them after
+    // the MFMAs above and ahead of this chunk's stores.
+    asm volatile("" ::: "memory");
+    load_nat(nkey);
+    load_keys(cb + 64, nkey);
+    asm volatile("" ::: "memory");
+    softmax(1, s1, dp1);
 
     // both blocks' steps in one 16-byte store by every lane (one address, unconditional);
     // (grow + cb) is a multiple of 32, so the pair is 16-byte aligned
     *reinterpret_cast<float4*>(&bstep[(grow + cb) / 16]) =
         make_float4(step[0].x, step[0].y, step[1].x, step[1].y);
 
-    // ---- dQ^T += K^T dS^T. The A operand K^T (row li <-> feature 16fb + li, slot (lg, e) <->
-    // key 4lg + e for e < 4, 16 + 4lg + e - 4 for e >= 4) is made from the natural K rows
-    // already in registers: kb_n x sel moves feature block fb of each 16-key tile into the C
-    // layout (lane li <-> feature, keys 4lg + j), which packed to bf16 is exactly that
-    // operand. The B operand dS^T is read from the LDS tile with the same key order.
+    // ---- dQ^T += K^T dS^T; the B operand dS^T is read from the LDS tile in the key order
+    // of the K^T operands
     wave_lds_fence();   // dS tile complete
     {
       u32x4 bds[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(&lds.ds[(qb * 16 + li) * 40 + 4 * lg]);
-        const u32x2 hi =
-            *reinterpret_cast<const u32x2*>(&lds.ds[(qb * 16 + li) * 40 + 16 + 4 * lg]);
+        // transposed reads: lane li gets member 16qb + li of keys 4lg .. 4lg + 3 (lo) and
+        // 16 + 4lg .. 16 + 4lg + 3 (hi)
+        const int r = 4 * lg + (li >> 2), c = 16 * qb + 4 * (li & 3);
+        const u32x2 lo = lds_read_tr16(&lds.ds[r * 80 + c]);
+        const u32x2 hi = lds_read_tr16(&lds.ds[(r + 16) * 80 + c]);
         bds[qb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
 #pragma unroll
-      for (int fb = 0; fb < NDB; ++fb) {
-        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-        const floatx4 t0 = mfma_bf16(kb_n[0][fb >> 1], sel[fb & 1], z);
-        const floatx4 t1 = mfma_bf16(kb_n[1][fb >> 1], sel[fb & 1], z);
-        const u32x4 ka = {pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]),
-                          pack_bf16(t1[0], t1[1]), pack_bf16(t1[2], t1[3])};
+      for (int fb = 0; fb < NDB; ++fb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) dqacc[qb][fb] = mfma_bf16(ka, bds[qb], dqacc[qb][fb]);
-      }
+        for (int qb = 0; qb < QB; ++qb) dqacc[qb][fb] = mfma_bf16(kT[fb], bds[qb], dqacc[qb][fb]);
     }
-
-    // the natural K/V registers are free again: request the next chunk's rows now (past the
-    // end the clamped positions reload the last key) and the keys of the one after
-    load_nat(nkey);
-    load_keys(cb + 64, nkey);
-    asm volatile("" ::: "memory");   // keep these loads ahead of the stores below
 
     // ---- dV^T = dO^T P, dK^T = Q^T dS (pre-scaled, see above). A operands by transposed LDS
     // reads: row li <-> feature 16fb + li, slot (lg, e) <-> member 32m + 16(e/4) + 4lg + e%4.

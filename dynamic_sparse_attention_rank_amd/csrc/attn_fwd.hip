@@ -53,6 +53,7 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
   constexpr int KS = D / 32;    // contraction steps of S^T = K Q^T
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   __shared__ __attribute__((aligned(16))) uint16_t qn[16 * QB * D];
+  __shared__ __attribute__((aligned(16))) uint16_t kvs[2][32 * D];   // K, V rows of a chunk
   const int lane = threadIdx.x;
   const int lg = lane >> 4;
   const int li = lane & 15;
@@ -87,35 +88,67 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
     for (int f = 0; f < NDB; ++f) oacc[qb][f] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = scale * kLog2e;
-  u32x4 sel[2];
-  make_selection(lane, sel);
 
-  u32x4 kb_n[2][KS], vb_n[2][KS];   // K / V rows 16kb + li of the current chunk, features
-  int nkey[2];                      // 32ks + 8lg ..; keys of the chunk after the next one
-  auto load_keys = [&](int cb, int out[2]) {
+  // ---- K and V rows of a 32-key chunk go to LDS by direct-to-LDS loads that each cover
+  // whole rows (full cache lines: 16-byte pieces, GPR per row, RPI rows per load), about twice
+  // the gather rate of loads shaped like MFMA operands (16 rows x 64 bytes). Load i, lane l
+  // fills LDS row p = RPI i + l / GPR, stored piece l % GPR (the XOR swizzle swz, so that
+  // operand reads do not conflict). Row p holds the chunk's key NI (p % RPI) + p / RPI, which
+  // makes a lane's NI keys adjacent in the index row. The score tile's rows are LDS rows, and
+  // the V^T operands are transposed reads of the same rows, so P^T and V^T agree on the key
+  // order without knowing it; only the tail mask maps a row back to its key.
+  constexpr int GPR = D / 8;     // 16-byte pieces per row
+  constexpr int RPI = 64 / GPR;  // rows per load
+  constexpr int NI = 32 / RPI;   // loads per array and chunk
+  const int la = lane / GPR;
+  const int lp = lane % GPR;
+  int kq[NI];   // keys of the next chunk to fetch
+  auto load_keys = [&](int cb, int (&out)[NI]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) out[kb] = row[min(cb + 16 * kb + li, kh - 1)];
+    for (int i = 0; i < NI; ++i) out[i] = row[min(cb + NI * la + i, kh - 1)];
   };
-  auto load_nat = [&](const int keys[2]) {
+  auto fetch_rows = [&](const int (&keys)[NI]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = clamp_key(keys[kb], geo.S);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kb_n[kb][ks] = ld16(K + (long long)key * D + ks * 32 + 8 * lg);
-        vb_n[kb][ks] = ld16(V + (long long)key * D + ks * 32 + 8 * lg);
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int p = RPI * i + la;
+      const long long off = (long long)clamp_key(keys[i], geo.S) * D + 8 * (lp ^ (p % GPR));
+      global_load_lds16(K + off, &kvs[0][RPI * i * D]);
+      global_load_lds16(V + off, &kvs[1][RPI * i * D]);
     }
   };
   {
-    int k0[2];
+    int k0[NI];
     load_keys(0, k0);
-    load_nat(k0);
-    load_keys(32, nkey);
+    fetch_rows(k0);
+    load_keys(32, kq);
   }
 
   for (int cb = 0; cb < kh; cb += 32) {
-    // ---- S^T = K Q^T ; lane: query 16qb + li, keys 16kb + 4lg + j
+    // this chunk's rows have landed once only the NI key loads issued after them remain
+    wait_vmcnt<NI>();
+    // ---- operands: K rows 16kb + li (A of S^T = K Q^T, features 32ks + 8lg ..) and V^T
+    // (row li <-> feature 16fb + li, slot (lg, e) <-> LDS row 4lg + e (e < 4) or
+    // 16 + 4lg + e - 4 (e >= 4)) by transposed reads
+    u32x4 ka[2][KS], vT[NDB];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        ka[kb][ks] = *reinterpret_cast<const u32x4*>(&kvs[0][swz<D>(16 * kb + li, 32 * ks + 8 * lg)]);
+#pragma unroll
+    for (int fb = 0; fb < NDB; ++fb) {
+      const int r = 4 * lg + (li >> 2), c = 16 * fb + 4 * (li & 3);
+      const u32x2 lo = lds_read_tr16(&kvs[1][swz<D>(r, c)]);
+      const u32x2 hi = lds_read_tr16(&kvs[1][swz<D>(r + 16, c)]);
+      vT[fb] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+    // operands are in registers: refill the buffer with the next chunk (past the end the
+    // clamped positions reload the last key; never used) and fetch the keys after it
+    wave_lds_fence();
+    fetch_rows(kq);
+    load_keys(cb + 64, kq);
+
+    // ---- S^T = K Q^T ; lane: query 16qb + li, LDS rows (keys) 16kb + 4lg + j
     floatx4 s[2][QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -124,59 +157,56 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
       for (int ks = 0; ks < KS; ++ks) {
         const u32x4 qop = *reinterpret_cast<const u32x4*>(&qn[swz<D>(16 * qb + li, 32 * ks + 8 * lg)]);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb][qb] = mfma_bf16(kb_n[kb][ks], qop, s[kb][qb]);
+        for (int kb = 0; kb < 2; ++kb) s[kb][qb] = mfma_bf16(ka[kb][ks], qop, s[kb][qb]);
       }
     }
-    // ---- V^T operands: row li <-> feature 16fb + li, slot (lg, e) <-> key 4lg + e (e < 4),
-    // 16 + 4lg + e - 4 (e >= 4), from the V rows in registers (selection MFMA, exact)
-    u32x4 vT[NDB];
-#pragma unroll
-    for (int fb = 0; fb < NDB; ++fb) {
-      const floatx4 z = {0.f, 0.f, 0.f, 0.f};
-      const floatx4 t0 = mfma_bf16(vb_n[0][fb >> 1], sel[fb & 1], z);
-      const floatx4 t1 = mfma_bf16(vb_n[1][fb >> 1], sel[fb & 1], z);
-      vT[fb] = u32x4{pack_bf16(t0[0], t0[1]), pack_bf16(t0[2], t0[3]), pack_bf16(t1[0], t1[1]),
-                     pack_bf16(t1[2], t1[3])};
-    }
-    // K/V registers consumed: request the next chunk (past the end the clamped positions
-    // reload the last key; those loads are never used) and the keys of the one after. The
-    // compiler barrier keeps the loads after the MFMAs above, so the two K/V buffers are
-    // never live together.
-    asm volatile("" ::: "memory");
-    load_nat(nkey);
-    load_keys(cb + 64, nkey);
 
     const bool tail = cb + 32 > kh;
+    // scaled scores (log2 units) and each lane's maximum per query tile
+    float t[QB][2][4], lmax[QB];
+    bool raise = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float t[2][4];
-      float lmax = -INFINITY;
+      lmax[qb] = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float x = s[kb][qb][j] * c2;
-          if (tail && cb + 16 * kb + 4 * lg + j >= kh) x = -INFINITY;
-          t[kb][j] = x;
-          lmax = fmaxf(lmax, x);
+          const int p = 16 * kb + 4 * lg + j;   // LDS row -> chunk key NI (p % RPI) + p / RPI
+          if (tail && cb + NI * (p % RPI) + p / RPI >= kh) x = -INFINITY;
+          t[qb][kb][j] = x;
+          lmax[qb] = fmaxf(lmax[qb], x);
         }
-      if (__ballot(lmax > mrun[qb] + kRaise)) {
-        float cmax = wave_xor_max(lmax, 16);
-        cmax = wave_xor_max(cmax, 32);
-        const float mnew = fmaxf(mrun[qb], cmax);
-        const float alpha = exp2f(mrun[qb] - mnew);
-        mrun[qb] = mnew;
-        lrun[qb] *= alpha;
+      raise = raise || lmax[qb] > mrun[qb] + kRaise;
+    }
+    // Lazy rescaling: a query's running maximum moves only when a score exceeds it by more
+    // than kRaise (so exp2 of the shifted scores stays below 2^kRaise). One uniform branch
+    // per chunk keeps the exponentials and the P V^T products below in one basic block.
+    if (__ballot(raise)) {
 #pragma unroll
-        for (int f = 0; f < NDB; ++f) oacc[qb][f] *= alpha;
+      for (int qb = 0; qb < QB; ++qb) {
+        if (__ballot(lmax[qb] > mrun[qb] + kRaise)) {
+          float cmax = wave_xor_max(lmax[qb], 16);
+          cmax = wave_xor_max(cmax, 32);
+          const float mnew = fmaxf(mrun[qb], cmax);
+          const float alpha = exp2f(mrun[qb] - mnew);
+          mrun[qb] = mnew;
+          lrun[qb] *= alpha;
+#pragma unroll
+          for (int f = 0; f < NDB; ++f) oacc[qb][f] *= alpha;
+        }
       }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       float p[2][4];
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          p[kb][j] = __builtin_amdgcn_exp2f(t[kb][j] - mrun[qb]);
+          p[kb][j] = __builtin_amdgcn_exp2f(t[qb][kb][j] - mrun[qb]);
           psum += p[kb][j];
         }
       lrun[qb] += psum;

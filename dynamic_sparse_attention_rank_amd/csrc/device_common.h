@@ -95,6 +95,33 @@ __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
   return v + __shfl_xor(v, mask, 64);
 }
 
+// Sum over the four 16-lane rows: lane l gets v(l%16) + v(l%16 + 16) + v(l%16 + 32) +
+// v(l%16 + 48), paired as (r0 + r1) + (r2 + r3), the same in every lane. gfx950's row swaps
+// (v_permlane16_swap / v_permlane32_swap) move the data without an LDS round trip: with both
+// operands v, the two results of a swap hold the two rows of each pair.
+__device__ __forceinline__ float sum_over_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Maximum over each 16-lane row (every lane of the row gets it), by DPP: swaps inside quads,
+// then rotations by 4 and 8 lanes.
+__device__ __forceinline__ float max_in_row16(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf,
+                                                          false)));   // quad_perm 1,0,3,2
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf,
+                                                          false)));   // quad_perm 2,3,0,1
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xf, 0xf,
+                                                          false)));   // row_ror 4
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xf, 0xf,
+                                                          false)));   // row_ror 8
+  return v;
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -133,6 +160,20 @@ struct GroupGeom {
 template <int D>
 __device__ __forceinline__ int swz(int r, int col) {
   return r * D + ((((col >> 3) ^ r) & (D / 8 - 1)) << 3) + (col & 7);
+}
+
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4): lane l's bytes
+// land at lds_base + 16 l. lds_base must be the same in every lane. The transfer is counted by
+// vmcnt like any vector load; the data may be read from LDS once that count has drained.
+__device__ __forceinline__ void global_load_lds16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   0);
+}
+// Wait until at most N vector memory operations of this wave are outstanding (loads, stores
+// and direct-to-LDS loads retire in issue order), and keep memory accesses on their side.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // ds_read_b64_tr_b16: within each 16-lane block, lane j passes the address of 4 elements
