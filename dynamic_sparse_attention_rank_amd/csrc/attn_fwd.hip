@@ -8,17 +8,17 @@
 // bf16 path (gfx950 MFMA): one wave per group (G = 16..64 queries, d = 64 or 128).
 //   * The group's Q rows sit in LDS (one swizzled copy); S^T = K Q^T reads them as 16-byte B
 //     operands, so a 16x16 score tile gives a lane one query and 4 keys.
-//   * Keys are consumed in chunks of 32 from the ascending index row. K and V rows are both
-//     gathered in 16-byte pieces straight into MFMA operand registers (lane: one key, 8
-//     features). The V^T operand of O^T += V^T P^T is made from those registers by an MFMA
-//     against a 0/1 selection matrix (exact), with the key order chosen so that the P^T
-//     operand is exactly the score tile a lane already holds.
+//   * Keys are consumed in chunks of 32 from the ascending index row. The chunk's K and V rows
+//     are gathered into an LDS tile by direct-to-LDS loads that cover whole rows (full cache
+//     lines, about twice the gather rate of operand-shaped 64-byte pieces); K operands are
+//     swizzled row reads, the V^T operand of O^T += V^T P^T comes from transposed LDS reads of
+//     the same rows, so P^T and V^T share the tile's row order.
 //   * Online softmax in the log2 domain with an fp32 running max and sum; the max is only
 //     raised (and O rescaled) when a new score exceeds it by more than 2^8, which keeps exp2
 //     arguments <= 8 and makes rescaling rare. Results are exact regardless of when it is raised.
-//   * The next chunk's K/V rows are requested as soon as the current ones have been turned
-//     into operands, and the key indices one chunk further ahead; every load in the loop is
-//     unconditional (positions clamped), so the waits for them are exact.
+//   * The next chunk's rows are requested as soon as the current ones are in registers, and
+//     the key indices one chunk further ahead; every load in the loop is unconditional
+//     (positions clamped), so the waits for them are exact.
 // fp32 path: plain fp32 FMA per lane (one lane per query); it exists for fp32 inputs and is
 // not tuned.
 #include <math.h>
@@ -32,6 +32,11 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRaise = 8.0f;   // log2-domain slack before the running max is raised
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
 
 __device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, int& h, int& g) {
   const int per_head = geo.B * geo.NG;
@@ -102,30 +107,33 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
   constexpr int NI = 32 / RPI;   // loads per array and chunk
   const int la = lane / GPR;
   const int lp = lane % GPR;
-  int kq[NI];   // keys of the next chunk to fetch
-  auto load_keys = [&](int cb, int (&out)[NI]) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) out[i] = row[min(cb + NI * la + i, kh - 1)];
-  };
-  auto fetch_rows = [&](const int (&keys)[NI]) {
+  // key indices: lane l reads chunk position l % 32 (one load per chunk; positions past the
+  // row end read its last key) and the NI keys a lane's row loads need are picked from those
+  // lanes by ds_bpermute when the rows are requested
+  int kq;   // index-row entry (cb + lane % 32) of the next chunk to fetch
+  auto load_keys = [&](int cb) { return row[min(cb + (lane & 31), kh - 1)]; };
+  const char* Kb = reinterpret_cast<const char*>(K);
+  const char* Vb = reinterpret_cast<const char*>(V);
+  auto fetch_rows = [&](const int kraw) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int p = RPI * i + la;
-      const long long off = (long long)clamp_key(keys[i], geo.S) * D + 8 * (lp ^ (p % GPR));
-      global_load_lds16(K + off, &kvs[0][RPI * i * D]);
-      global_load_lds16(V + off, &kvs[1][RPI * i * D]);
+      const uint32_t key = min((uint32_t)__shfl(kraw, NI * la + i, 64), (uint32_t)geo.S - 1u);
+      const uint32_t off = key * (uint32_t)(2 * D) + (uint32_t)((lp ^ (p % GPR)) << 4);
+      global_load_lds16(Kb + off, &kvs[0][RPI * i * D]);
+      global_load_lds16(Vb + off, &kvs[1][RPI * i * D]);
     }
   };
-  {
-    int k0[NI];
-    load_keys(0, k0);
-    fetch_rows(k0);
-    load_keys(32, kq);
-  }
+  fetch_rows(load_keys(0));
+  kq = load_keys(32);
 
-  for (int cb = 0; cb < kh; cb += 32) {
-    // this chunk's rows have landed once only the NI key loads issued after them remain
-    wait_vmcnt<NI>();
+  // mrun is the running maximum of the raw scores q.k (c2 > 0 turns them into log2 units):
+  // P = exp2(c2 s - c2 mrun) is then one FMA and one exp2 per score
+  const float raise_s = kRaise / c2;
+  auto chunk = [&](const int cb, auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;
+    // this chunk's rows have landed once only the key load issued after them remains
+    wait_vmcnt<1>();
     // ---- operands: K rows 16kb + li (A of S^T = K Q^T, features 32ks + 8lg ..) and V^T
     // (row li <-> feature 16fb + li, slot (lg, e) <-> LDS row 4lg + e (e < 4) or
     // 16 + 4lg + e - 4 (e >= 4)) by transposed reads
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
     // clamped positions reload the last key; never used) and fetch the keys after it
     wave_lds_fence();
     fetch_rows(kq);
-    load_keys(cb + 64, kq);
+    kq = load_keys(cb + 64);
 
     // ---- S^T = K Q^T ; lane: query 16qb + li, LDS rows (keys) 16kb + 4lg + j
     floatx4 s[2][QB];
@@ -161,9 +169,9 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
       }
     }
 
-    const bool tail = cb + 32 > kh;
-    // scaled scores (log2 units) and each lane's maximum per query tile
-    float t[QB][2][4], lmax[QB];
+    // each lane's maximum raw score per query tile; in the last, partial chunk the rows past
+    // the end of the index row (LDS row p holds chunk key NI (p % RPI) + p / RPI) are -inf
+    float lmax[QB];
     bool raise = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -172,13 +180,13 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          float x = s[kb][qb][j] * c2;
-          const int p = 16 * kb + 4 * lg + j;   // LDS row -> chunk key NI (p % RPI) + p / RPI
-          if (tail && cb + NI * (p % RPI) + p / RPI >= kh) x = -INFINITY;
-          t[qb][kb][j] = x;
-          lmax[qb] = fmaxf(lmax[qb], x);
+          if constexpr (kTail) {
+            const int p = 16 * kb + 4 * lg + j;
+            if (cb + NI * (p % RPI) + p / RPI >= kh) s[kb][qb][j] = -INFINITY;
+          }
+          lmax[qb] = fmaxf(lmax[qb], s[kb][qb][j]);
         }
-      raise = raise || lmax[qb] > mrun[qb] + kRaise;
+      raise = raise || lmax[qb] > mrun[qb] + raise_s;
     }
     // Lazy rescaling: a query's running maximum moves only when a score exceeds it by more
     // than kRaise (so exp2 of the shifted scores stays below 2^kRaise). One uniform branch
@@ -186,11 +194,11 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
     if (__ballot(raise)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        if (__ballot(lmax[qb] > mrun[qb] + kRaise)) {
+        if (__ballot(lmax[qb] > mrun[qb] + raise_s)) {
           float cmax = wave_xor_max(lmax[qb], 16);
           cmax = wave_xor_max(cmax, 32);
           const float mnew = fmaxf(mrun[qb], cmax);
-          const float alpha = exp2f(mrun[qb] - mnew);
+          const float alpha = exp2f((mrun[qb] - mnew) * c2);
           mrun[qb] = mnew;
           lrun[qb] *= alpha;
 #pragma unroll
@@ -200,13 +208,14 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      const float nm = -mrun[qb] * c2;
       float p[2][4];
       float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          p[kb][j] = __builtin_amdgcn_exp2f(t[qb][kb][j] - mrun[qb]);
+          p[kb][j] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][j], c2, nm));
           psum += p[kb][j];
         }
       lrun[qb] += psum;
@@ -216,7 +225,10 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
 #pragma unroll
       for (int fb = 0; fb < NDB; ++fb) oacc[qb][fb] = mfma_bf16(vT[fb], pb, oacc[qb][fb]);
     }
-  }
+  };
+  int cb = 0;
+  for (; cb + 32 <= kh; cb += 32) chunk(cb, Flag<false>{});
+  if (cb < kh) chunk(cb, Flag<true>{});
 
   // finalise: full row sums, normalise, store O (bf16) and LSE (fp32). Lane: query
   // 16qb + li, features 16fb + 4lg + j.
@@ -233,7 +245,7 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
           u32x2{pack_bf16(oacc[qb][fb][0] * inv, oacc[qb][fb][1] * inv),
                 pack_bf16(oacc[qb][fb][2] * inv, oacc[qb][fb][3] * inv)};
     if (lg == 0)
-      lse[((long long)b * geo.H + h) * geo.S + n] = (mrun[qb] + log2f(l)) * kLn2;
+      lse[((long long)b * geo.H + h) * geo.S + n] = (mrun[qb] * c2 + log2f(l)) * kLn2;
   }
 }
 
