@@ -126,6 +126,14 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
   };
   fetch_rows(load_keys(0));
   kq = load_keys(32);
+  // the Q operands (B of S^T = K Q^T: query 16qb + li, features 32ks + 8lg ..) stay in
+  // registers for the whole row instead of being re-read from LDS every chunk
+  u32x4 qop[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qop[qb][ks] = *reinterpret_cast<const u32x4*>(&qn[swz<D>(16 * qb + li, 32 * ks + 8 * lg)]);
 
   // mrun is the running maximum of the raw scores q.k (c2 > 0 turns them into log2 units):
   // P = exp2(c2 s - c2 mrun) is then one FMA and one exp2 per score
@@ -162,11 +170,9 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
     for (int qb = 0; qb < QB; ++qb) {
       s[0][qb] = s[1][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const u32x4 qop = *reinterpret_cast<const u32x4*>(&qn[swz<D>(16 * qb + li, 32 * ks + 8 * lg)]);
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) s[kb][qb] = mfma_bf16(ka[kb][ks], qop, s[kb][qb]);
-      }
+        for (int kb = 0; kb < 2; ++kb) s[kb][qb] = mfma_bf16(ka[kb][ks], qop[qb][ks], s[kb][qb]);
     }
 
     // each lane's maximum raw score per query tile; in the last, partial chunk the rows past
