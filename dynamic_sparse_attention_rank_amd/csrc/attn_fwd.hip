@@ -33,10 +33,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRaise = 8.0f;   // log2-domain slack before the running max is raised
 
-template <bool B>
-struct Flag {
-  static constexpr bool value = B;
-};
 
 __device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, int& h, int& g) {
   const int per_head = geo.B * geo.NG;

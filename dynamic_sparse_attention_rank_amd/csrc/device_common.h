@@ -131,6 +131,12 @@ __device__ __forceinline__ u32x2 ld8(const void* p) {
 
 // Key indices come from caller memory: clamp them into [0, S) so that a bad list can never
 // address outside K/V (the result for such a list is unspecified, but memory-safe).
+// Compile-time switch passed to generic lambdas (e.g. the last, partial key chunk).
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
+
 __device__ __forceinline__ int clamp_key(int key, int S) { return min(max(key, 0), S - 1); }
 
 // Token index of member j of group g (groups are gt x gh x gw boxes of the T x Hh x W grid,
