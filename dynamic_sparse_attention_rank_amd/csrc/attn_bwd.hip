@@ -297,10 +297,12 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t eu = __builtin_amdgcn_readlane(e, u0 + u);
+        // staging rows are read once: non-temporal, so they do not displace other lines
         if constexpr (FPL == 2)
-          x[u] = *reinterpret_cast<const uint32_t*>(src + (long long)eu * D);
+          x[u] = __builtin_nontemporal_load(
+              reinterpret_cast<const uint32_t*>(src + (long long)eu * D));
         else
-          x[u] = (uint16_t)src[(long long)eu * D];
+          x[u] = (uint16_t)__builtin_nontemporal_load(src + (long long)eu * D);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -604,8 +606,12 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     // ---- dV^T = dO^T P, dK^T = Q^T dS (pre-scaled, see above). A operands by transposed LDS
     // reads: row li <-> feature 16fb + li, slot (lg, e) <-> member 32m + 16(e/4) + 4lg + e%4.
     // Lane: key 16kb + li, features 16fb + 4lg + j. Feature blocks go in pairs (2fp, 2fp + 1)
-    // so that every lane stores 16 bytes: staging position 32fp + 8lg + t holds feature
+    // so that every lane holds 16-byte granules: staging position 32fp + 8lg + t holds feature
     // 32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4 (t >= 4); the reduce undoes this order.
+    // The rows are written once and read back by the reduce long after, so the stores are
+    // non-temporal and cover whole 128-byte lines (half-line non-temporal stores are far
+    // slower); they are the bulk of this kernel's HBM traffic.
+    u32x4 xv[2], xk[2];   // granules of the even feature-block pair, held for the line swap
 #pragma unroll
     for (int fp = 0; fp < NDB / 2; ++fp) {
       floatx4 av[2][2], ak[2][2];
@@ -636,13 +642,34 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         // row cb + 16kb + li < padded_k: past the row end it is a (zero) padding row
-        const long long off = (grow + cb + 16 * kb + li) * D + 32 * fp + 8 * lg;
         const u32x4 wv = {pack_f16(av[0][kb][0], av[0][kb][1]), pack_f16(av[0][kb][2], av[0][kb][3]),
                           pack_f16(av[1][kb][0], av[1][kb][1]), pack_f16(av[1][kb][2], av[1][kb][3])};
         const u32x4 wk = {pack_f16(ak[0][kb][0], ak[0][kb][1]), pack_f16(ak[0][kb][2], ak[0][kb][3]),
                           pack_f16(ak[1][kb][0], ak[1][kb][1]), pack_f16(ak[1][kb][2], ak[1][kb][3])};
-        *reinterpret_cast<u32x4*>(cv + off) = wv;
-        *reinterpret_cast<u32x4*>(ck + off) = wk;
+        if ((fp & 1) == 0) {
+          xv[kb] = wv;
+          xk[kb] = wk;
+        } else {
+          // a lane holds granules 8p + lg (even fp) and 8p + 4 + lg (odd fp) of row li; after
+          // swapping with lane li ^ 8 every store writes 8 whole 128-byte lines: rows
+          // 16kb + (li & 7) (first) and 16kb + (li & 7) + 8 (second), granule 8p + 4(li / 8) + lg
+          // DPP row_ror:8 with a bank mask: lanes 8..15 of each row (banks 2, 3) take the
+          // odd granule of lane li - 8, lanes 0..7 (banks 0, 1) the even granule of lane li + 8
+          u32x4 av1, av2, ak1, ak2;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            av1[w] = __builtin_amdgcn_update_dpp(xv[kb][w], wv[w], 0x128, 0xf, 0xc, false);
+            av2[w] = __builtin_amdgcn_update_dpp(wv[w], xv[kb][w], 0x128, 0xf, 0x3, false);
+            ak1[w] = __builtin_amdgcn_update_dpp(xk[kb][w], wk[w], 0x128, 0xf, 0xc, false);
+            ak2[w] = __builtin_amdgcn_update_dpp(wk[w], xk[kb][w], 0x128, 0xf, 0x3, false);
+          }
+          const long long ra = grow + cb + 16 * kb + (li & 7);
+          const int gcol = 8 * (8 * (fp >> 1) + 4 * (li >> 3) + lg);
+          __builtin_nontemporal_store(av1, reinterpret_cast<u32x4*>(cv + ra * D + gcol));
+          __builtin_nontemporal_store(av2, reinterpret_cast<u32x4*>(cv + (ra + 8) * D + gcol));
+          __builtin_nontemporal_store(ak1, reinterpret_cast<u32x4*>(ck + ra * D + gcol));
+          __builtin_nontemporal_store(ak2, reinterpret_cast<u32x4*>(ck + (ra + 8) * D + gcol));
+        }
       }
     }
     wave_lds_fence();   // the next chunk overwrites the dS tile
