@@ -248,6 +248,7 @@ __global__ void fill_zero(float4* __restrict__ p, long long n4) {
 // then walks them one row per instruction, so no two lanes ever touch the same LDS word and
 // rows with equal keys are added in list order. 32 row loads are in flight per wave. Every
 // key row of the bucket is then written once (zero where no group selected the key).
+typedef float floatx2 __attribute__((ext_vector_type(2)));
 template <int D>
 __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__ off,
                                                    const uint32_t* __restrict__ perm,
@@ -330,8 +331,8 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
   float* out = (half ? dk : dv) + bh * geo.S * D + (long long)key0 * D + feat;
   for (int l = 0; l < nk; ++l) {
     if constexpr (FPL == 2)
-      *reinterpret_cast<float2*>(out + (long long)l * D) =
-          *reinterpret_cast<const float2*>(acc + l * D + FPL * lane);
+      __builtin_nontemporal_store(*reinterpret_cast<const floatx2*>(acc + l * D + FPL * lane),
+                                  reinterpret_cast<floatx2*>(out + (long long)l * D));
     else
       out[(long long)l * D] = acc[l * D + lane];
   }
