@@ -11,24 +11,23 @@
 //     dV_m = sum_n P[n,m] dO_n           (idem)
 //
 // bf16 path (gfx950 MFMA), one wave per group, keys in chunks of 32:
-//   * S = Q K^T and dP = dO V^T are computed with Q / dO as the A operand (registers) and K / V
-//     rows gathered straight into B operands. A lane then holds one key and 4 queries per
-//     16x16 tile, which is exactly the A operand of dV = P^T dO and dK = dS^T Q: no transpose
-//     of P or dS is needed there. Their B operands (dO and Q with queries contiguous per lane)
-//     are built once per group in LDS.
-//   * dQ^T += K^T dS^T needs dS with queries in lanes: dS goes through a 4 KB LDS tile; K rows
-//     are re-gathered one full row per 16 lanes and transposed in registers (v_perm_b32).
+//   * Q and dO rows of the group sit in LDS (one swizzled copy each). S = Q K^T and
+//     dP = dO V^T read them as 16-byte A operands, with K / V rows gathered straight into B
+//     operands; a lane then holds one key and 4 queries per 16x16 tile, which is exactly the
+//     B operand of dV^T = dO^T P and dK^T = Q^T dS. Their A operands (dO, Q with queries
+//     contiguous per lane) are transposed LDS reads (ds_read_b64_tr_b16).
+//   * dQ^T += K^T dS^T: K^T from the K registers by an MFMA against a 0/1 selection operand,
+//     dS^T from a [key][member] LDS tile read back transposed. dQ is written once.
 //   * dK/dV: each (group, selected key) edge yields one row of dV and one of dK, summed over
 //     all groups that selected the key. fp32 atomics on this chip sustain only ~0.33 T adds/s,
-//     so the rows are not added in place. The edge (g, p) owns staging row g*k + p, so each
-//     wave writes its rows contiguously, as 16-bit integers with one fp32 step per half (the
-//     step is an a-priori bound / 32000: |dV| <= sum P * max|dO|, |dK| <= scale * sum|dS| *
-//     max|Q|, so each entry is off by at most 1.6e-5 of that bound, far below the bf16
-//     rounding of the P and dS MFMA operands). Small pre-passes list, for every 32-key
-//     bucket, its edges in (group, position) order; a reduce kernel then sums each bucket's
-//     rows in LDS (one wave per bucket and half, one row per instruction, no atomics) and
-//     writes every dK/dV row of the bucket exactly once, so dK/dV are bitwise reproducible.
-//     Heads are processed in chunks sized to the caller's workspace.
+//     so the rows are not added in place. The edge (g, p) owns staging row g*padded_k + p:
+//     fp16 entries with one power-of-two scale per 16-key block from a-priori bounds
+//     (|dV| <= sum P * max|dO|, |dK| <= scale * sum|dS| * max|Q|), so each entry keeps a
+//     relative error <= 2^-11. The rows are written with whole-line non-temporal stores.
+//     Small pre-passes list, for every 32-key bucket, its edges in (group, position) order;
+//     a reduce kernel then sums each bucket's rows in LDS (one wave per bucket and half, one
+//     row per instruction, no atomics) and writes every dK/dV row exactly once, so dK/dV are
+//     bitwise reproducible. Heads are processed in chunks sized to the caller's workspace.
 // fp32 path: plain fp32 FMA (one lane per query, then one lane per feature for dK/dV); it
 // exists for fp32 inputs and is not tuned.
 #include <math.h>
