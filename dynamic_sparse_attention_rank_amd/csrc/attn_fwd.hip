@@ -231,6 +231,9 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
   int cb = 0;
   for (; cb + 32 <= kh; cb += 32) chunk(cb, Flag<false>{});
   if (cb < kh) chunk(cb, Flag<true>{});
+  // the last chunk requested rows past the end into the other buffer: they land before
+  // the workgroup ends and its LDS is handed to another
+  wait_vmcnt<0>();
 
   // finalise: full row sums, normalise, store O (bf16) and LSE (fp32). Lane: query
   // 16qb + li, features 16fb + 4lg + j.
