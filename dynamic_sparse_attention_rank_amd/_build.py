@@ -13,6 +13,10 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsv.so")
 SOURCES = ["dsv_api.cpp", "topk.hip", "attn_fwd.hip", "attn_bwd.hip"]
 ARCH = os.environ.get("DSV_OFFLOAD_ARCH", "gfx950")
+# The forward keeps its output accumulators in VGPRs (MFMA results written to VGPRs, not
+# AGPRs): its lazy rescale multiplies them with VALU ops, and with AGPR accumulators the
+# compiler copies all of them to VGPRs on every chunk, rescaled or not.
+EXTRA_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -38,7 +42,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
 
     def compile_one(src):
         obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *common_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+               "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         r = subprocess.run(cmd, capture_output=True, text=True)
