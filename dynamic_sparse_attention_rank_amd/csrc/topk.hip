@@ -9,71 +9,87 @@
 // tiles, each time the key stream is traversed.
 //
 // Design (gfx950):
-//   * Workgroup = 4 waves = 64 groups of one (b, h). Each wave owns 16 groups: the 16-row A
-//     operand of a v_mfma_f32_16x16x32_bf16 holds their group sums (split into two bf16 terms,
-//     hi + lo, so that the sums stay exact), the B operand holds 16 keys of K_lr staged in LDS.
-//     Each 16x16 output tile gives a lane one key and four groups.
+//   * Workgroup = TK_GW x TK_KW waves over 16 TK_GW groups of one (b, h). Wave (gw, kw) scores
+//     groups 16 gw .. 16 gw + 15 against keys 16 kw .. 16 kw + 15 of every TK_TILE-key tile, so
+//     the TK_KW waves of a group block split the key stream and share its LDS histograms. The
+//     16-row A operand of v_mfma_f32_16x16x32_bf16 holds the group sums (split into two bf16
+//     terms, hi + lo, so that the sums stay exact); the B operand (16 keys of K_lr) is loaded
+//     straight from memory into registers, one tile ahead. Each 16x16 output tile gives a lane
+//     one key and four groups.
 //   * Exact selection = radix select on an order-preserving 32-bit image of the fp32 score,
 //     8 bits per pass: pass p builds, per group, an LDS histogram of digit p over the keys whose
 //     higher digits match the prefix found so far; a wave scan then fixes the digit holding the
 //     k-th largest key. A group stops refining as soon as its whole current bin is needed.
+//     Lane li adds its four groups' counts in the rotated order (j + li) mod 4, so one LDS
+//     atomic instruction touches 16 different groups (at most 4 lanes per histogram) even when
+//     all scores fall into the same bin, as they do for the exponent byte of pass 0.
 //   * A final pass compacts, per group, the keys above the threshold plus the first `need` keys
-//     equal to it, in ascending key order (wave ballots give each lane its output slot).
-//   * K_lr tiles are staged once per workgroup in LDS (double-buffered) and read by all waves.
+//     equal to it, in ascending key order: wave ballots rank a lane's key inside its 16-key
+//     slice, and per-tile slice counts in LDS give each slice its offset.
+//   * Consecutive workgroups go to different XCDs; the block index is remapped so that the
+//     workgroups of one (b, h) share an XCD (and its L2) while they stream the same K_lr.
 #include "device_common.h"
 #include "dsv_internal.h"
 
 namespace dsv {
 namespace {
 
-constexpr int TK_WAVES = 4;
+constexpr int TK_GW = 2;                   // group waves per workgroup (16 groups each)
+constexpr int TK_KW = 4;                   // key slices per workgroup (16 keys of a tile each)
+constexpr int TK_WAVES = TK_GW * TK_KW;
 constexpr int TK_THREADS = 64 * TK_WAVES;
-constexpr int TK_GROUPS = 16 * TK_WAVES;   // groups per workgroup
-constexpr int TK_TILE = 64;                // keys per staged K_lr tile
+constexpr int TK_GROUPS = 16 * TK_GW;      // groups per workgroup
+constexpr int TK_TILE = 16 * TK_KW;        // keys per step of the workgroup
 constexpr int TK_HSTRIDE = 257;            // 256 bins + 1 pad word per group histogram
 
 // Order-preserving map float -> uint32 (larger score <=> larger key). -0 is folded onto +0.
 __device__ __forceinline__ uint32_t score_key(float s) {
-  if (s == 0.0f) s = 0.0f;
-  const uint32_t u = __float_as_uint(s);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(s + 0.0f);   // -0 + 0 = +0 (round to nearest)
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 template <bool F32, int R>
 struct TopkCfg {
   static constexpr int ES = F32 ? 4 : 2;             // bytes per element
   static constexpr int RB = R * ES;                  // bytes per K_lr row
-  static constexpr int TILE_BYTES = TK_TILE * RB;
-  static constexpr int CHUNKS = TILE_BYTES / 16;     // 16-byte chunks per tile
-  static constexpr int LD_PER_THREAD = (CHUNKS + TK_THREADS - 1) / TK_THREADS;
   static constexpr int KSTEPS = F32 ? R / 4 : (R + 31) / 32;   // MFMA contraction steps
 };
 
 template <bool F32, int R>
-__global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict__ qlr_,
+__global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void topk_kernel(const void* __restrict__ qlr_,
                                                           const void* __restrict__ klr_,
                                                           int32_t* __restrict__ idx, Geom geo) {
   using C = TopkCfg<F32, R>;
   __shared__ uint32_t hist[TK_GROUPS * TK_HSTRIDE];
-  __shared__ __attribute__((aligned(16))) unsigned char ktile[2][C::TILE_BYTES];
+  // compaction: per tile parity, group and key slice, the slice's count of keys above the
+  // threshold (bits 0..15) and equal to it (bits 16..31)
+  __shared__ __attribute__((aligned(16))) uint32_t tcnt[2][TK_GROUPS][TK_KW];
   __shared__ uint32_t st_prefix[TK_GROUPS];
   __shared__ int st_krem[TK_GROUPS];
   // Group state: -1 = no such group; 0..3 = still refining, that many digits known (and the
   // next histogram pass is that index); 16 + D = finished with D digits known.
   __shared__ int st_npass[TK_GROUPS];
-  __shared__ int st_active;
+  __shared__ int st_active[4];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int lg = lane >> 4;
   const int li = lane & 15;
+  const int gw = wave / TK_KW;
+  const int kw = wave - gw * TK_KW;
 
+  // block -> (b, h, group block): blocks x, x + 8, x + 16, .. run on XCD x % 8, and they get
+  // consecutive logical indices, so that one (b, h)'s blocks share an XCD
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int logical = xcd * (nblk >> 3) + min(xcd, nblk & 7) + (blockIdx.x >> 3);
   const int gblocks = (geo.NG + TK_GROUPS - 1) / TK_GROUPS;
-  const int bh = blockIdx.x / gblocks;
-  const int gblock = blockIdx.x - bh * gblocks;
-  const int b = bh / geo.H;
-  const int h = bh - b * geo.H;
+  const int slot = logical / gblocks;
+  const int gblock = logical - slot * gblocks;
+  const int b = slot / geo.H;
+  const int h = geo.order[slot - b * geo.H];
+  const int bh = b * geo.H + h;
   const int S = geo.S;
   const int kh = geo.k[h];
   const long long head_base = (long long)bh * S * R;   // element offset of (b,h) in Q_lr/K_lr
@@ -89,9 +105,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
   }
   for (int i = tid; i < TK_GROUPS * TK_HSTRIDE; i += TK_THREADS) hist[i] = 0;
 
-  // ---- group sums -> A operands (row li = group 16*wave + li)
+  // ---- group sums -> A operands (row li = group 16*gw + li); each key slice sums its own copy
   const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
-  const int my_group = gblock * TK_GROUPS + 16 * wave + li;
+  const int my_group = gblock * TK_GROUPS + 16 * gw + li;
   float ssum[C::KSTEPS * (F32 ? 1 : 8)];
 #pragma unroll
   for (int i = 0; i < C::KSTEPS * (F32 ? 1 : 8); ++i) ssum[i] = 0.0f;
@@ -134,47 +150,37 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
     }
   }
 
-  // ---- K_lr tile staging
-  const int ntiles = (S + TK_TILE - 1) / TK_TILE;
-  auto load_tile = [&](int t, u32x4* regs) {
+  // ---- B operands: key m = TK_TILE t + 16 kw + li of tile t (clamped to the last key; the
+  // scores of keys past the end are never counted), contraction slot lg
+  constexpr int NB = F32 ? R / 16 : C::KSTEPS;   // 16-byte loads per lane and tile
+  auto load_b = [&](int t, u32x4* bo) {
+    const int m = min(t * TK_TILE + 16 * kw + li, S - 1);
+    const unsigned char* krow = klr + (long long)m * C::RB;
 #pragma unroll
-    for (int c = 0; c < C::LD_PER_THREAD; ++c) {
-      const int chunk = tid + c * TK_THREADS;
-      regs[c] = u32x4{0, 0, 0, 0};
-      if (chunk < C::CHUNKS) {
-        const long long byte = (long long)t * C::TILE_BYTES + chunk * 16;
-        const int key = (int)(byte / C::RB);
-        if (key < S) regs[c] = ld16(klr + byte);
+    for (int i = 0; i < NB; ++i) {
+      if constexpr (F32) {
+        bo[i] = ld16(krow + (lg * (R / 4) + 4 * i) * 4);
+      } else {
+        bo[i] = (i * 32 + 8 * lg < R) ? ld16(krow + (i * 32 + 8 * lg) * 2) : u32x4{0, 0, 0, 0};
       }
     }
   };
-  auto store_tile = [&](int buf, const u32x4* regs) {
-#pragma unroll
-    for (int c = 0; c < C::LD_PER_THREAD; ++c) {
-      const int chunk = tid + c * TK_THREADS;
-      if (chunk < C::CHUNKS) *reinterpret_cast<u32x4*>(&ktile[buf][chunk * 16]) = regs[c];
-    }
-  };
-
-  // Scores of the 16 keys of sub-tile `sub` for this wave's 16 groups (lane: key li, rows 4lg+j).
-  auto tile_scores = [&](int buf, int sub) -> floatx4 {
+  // scores of the wave's 16 groups (rows 4 lg + j) against its key of the tile (column li)
+  auto scores = [&](const u32x4* bo) -> floatx4 {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    const unsigned char* krow = &ktile[buf][(sub * 16 + li) * C::RB];
-    if constexpr (F32) {
-      const float* kr = reinterpret_cast<const float*>(krow) + lg * (R / 4);
 #pragma unroll
-      for (int s = 0; s < R / 4; ++s) acc = mfma_f32(ssum[s], kr[s], acc);
-    } else {
+    for (int i = 0; i < NB; ++i) {
+      if constexpr (F32) {
 #pragma unroll
-      for (int ks = 0; ks < C::KSTEPS; ++ks) {
-        u32x4 bop = {0, 0, 0, 0};
-        if (ks * 32 + 8 * lg < R) bop = *reinterpret_cast<const u32x4*>(krow + (ks * 32 + 8 * lg) * 2);
-        acc = mfma_bf16(a_hi[ks], bop, acc);
-        acc = mfma_bf16(a_lo[ks], bop, acc);
+        for (int e = 0; e < 4; ++e) acc = mfma_f32(ssum[4 * i + e], __uint_as_float(bo[i][e]), acc);
+      } else {
+        acc = mfma_bf16(a_hi[i], bo[i], acc);
+        acc = mfma_bf16(a_lo[i], bo[i], acc);
       }
     }
     return acc;
   };
+  const int ntiles = (S + TK_TILE - 1) / TK_TILE;
 
   __syncthreads();
 
@@ -184,80 +190,106 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
       if (tid == 0) {
         int act = 0;
         for (int i = 0; i < TK_GROUPS; ++i) act |= (st_npass[i] == pass);
-        st_active = act;
+        st_active[pass] = act;
       }
       __syncthreads();
-      if (!st_active) continue;   // uniform: every group stopped refining earlier
+      if (!st_active[pass]) continue;   // uniform: every group stopped refining earlier
     }
-    // per-lane copies of the state of the lane's four groups (rows 4*lg + j of the wave block)
-    uint32_t pfx[4];
-    int gstate[4], need[4], shift[4];
-    long long rowoff[4];
-    int cnt[4] = {0, 0, 0, 0}, ties[4] = {0, 0, 0, 0};
+    const int dshift = 24 - 8 * pass;
+    const int pshift = 32 - 8 * pass;
+    u32x4 bcur[NB], bnxt[NB];
+    load_b(0, bcur);
+    if (pass < 4) {
+      // Histogram pass. Slot j of lane li is group 4 lg + (j + li) % 4 of the wave's block.
+      uint32_t rpfx[4];
+      int rstate[4];
+      uint32_t* rhist[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gl = 16 * wave + 4 * lg + j;
-      pfx[j] = st_prefix[gl];
-      gstate[j] = st_npass[gl];
-      need[j] = st_krem[gl];
-      shift[j] = 32 - 8 * (gstate[j] - 16);   // meaningful once finished (gstate >= 16)
-      rowoff[j] = (gstate[j] >= 0) ? geo.row_offset(b, h, gblock * TK_GROUPS + gl) : 0;
-    }
-
-    u32x4 regs[C::LD_PER_THREAD];
-    load_tile(0, regs);
-    store_tile(0, regs);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < ntiles) load_tile(t + 1, regs);
-      floatx4 accs[TK_TILE / 16];   // all sub-tiles' scores first: the LDS reads and MFMAs
-#pragma unroll                     // of the tile overlap instead of waiting one by one
-      for (int sub = 0; sub < TK_TILE / 16; ++sub) accs[sub] = tile_scores(buf, sub);
+      for (int j = 0; j < 4; ++j) {
+        const int gl = 16 * gw + 4 * lg + ((j + li) & 3);
+        rpfx[j] = st_prefix[gl];
+        rstate[j] = st_npass[gl];
+        rhist[j] = &hist[gl * TK_HSTRIDE];
+      }
+      for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) load_b(t + 1, bnxt);
+        const floatx4 acc = scores(bcur);
+        const bool mvalid = t * TK_TILE + 16 * kw + li < S;
 #pragma unroll
-      for (int sub = 0; sub < TK_TILE / 16; ++sub) {
-        const int m = t * TK_TILE + sub * 16 + li;
-        const floatx4 acc = accs[sub];
-        const bool mvalid = m < S;
-        if (pass < 4) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t key = score_key(acc[j]);
-            const bool take = mvalid && gstate[j] == pass &&
-                              (pass == 0 || (key >> (32 - 8 * pass)) == pfx[j]);
-            if (take) {
-              const int gl = 16 * wave + 4 * lg + j;
-              __hip_atomic_fetch_add(&hist[gl * TK_HSTRIDE + ((key >> (24 - 8 * pass)) & 255u)], 1u,
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-          }
-        } else {
-          const uint32_t below = (1u << li) - 1u;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t key = score_key(acc[j]);
-            const bool gvalid = gstate[j] >= 16;
-            const uint32_t v = key >> (shift[j] & 31);
-            const bool gt = mvalid && gvalid && v > pfx[j];
-            const bool eq = mvalid && gvalid && v == pfx[j];
-            const uint32_t eqbits = (uint32_t)(__ballot(eq) >> (16 * lg)) & 0xffffu;
-            const bool sel = gt || (eq && ties[j] + __popc(eqbits & below) < need[j]);
-            const uint32_t selbits = (uint32_t)(__ballot(sel) >> (16 * lg)) & 0xffffu;
-            const int pos = cnt[j] + __popc(selbits & below);
-            if (sel && pos < kh) idx[rowoff[j] + pos] = m;
-            cnt[j] += __popc(selbits);
-            ties[j] += __popc(eqbits);
-          }
+        for (int j = 0; j < 4; ++j) {
+          const int jr = (j + li) & 3;
+          const float sc = jr == 0 ? acc[0] : jr == 1 ? acc[1] : jr == 2 ? acc[2] : acc[3];
+          const uint32_t key = score_key(sc);
+          const bool take = mvalid && rstate[j] == pass &&
+                            (pass == 0 || (key >> (pshift & 31)) == rpfx[j]);
+          if (take)
+            __hip_atomic_fetch_add(&rhist[j][(key >> dshift) & 255u], 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
         }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) bcur[i] = bnxt[i];
       }
-      if (t + 1 < ntiles) store_tile(buf ^ 1, regs);
-      __syncthreads();
+    } else {
+      // Compaction. Lane: key m, groups 4 lg + j of the wave's block, all finished.
+      uint32_t pfx[4];
+      int shift[4], cnt[4], left[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int gl = 16 * gw + 4 * lg + j;
+        const int gs = st_npass[gl];
+        pfx[j] = gs >= 16 ? st_prefix[gl] : 0xffffffffu;
+        shift[j] = gs >= 16 ? 32 - 8 * (gs - 16) : 0;   // no key exceeds an all-ones image
+        left[j] = gs >= 16 ? st_krem[gl] : 0;            // equal keys still to take
+        cnt[j] = 0;
+      }
+      // rows of groups 4 lg + j are consecutive (k_h entries each); groups past NG select nothing
+      int32_t* const orow = idx + geo.row_offset(b, h, gblock * TK_GROUPS + 16 * gw + 4 * lg);
+      const uint32_t below = (1u << li) - 1u;
+      for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) load_b(t + 1, bnxt);
+        const floatx4 acc = scores(bcur);
+        const int m = t * TK_TILE + 16 * kw + li;
+        const bool mvalid = m < S;
+        uint32_t ge[4];   // this slice's ballots of the key's group j: above (bits 0..15), equal
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t v = score_key(acc[j]) >> (shift[j] & 31);
+          const uint32_t gtb = (uint32_t)(__ballot(mvalid && v > pfx[j]) >> (16 * lg)) & 0xffffu;
+          const uint32_t eqb = (uint32_t)(__ballot(mvalid && v == pfx[j]) >> (16 * lg)) & 0xffffu;
+          ge[j] = gtb | (eqb << 16);
+          if (li == 0)
+            tcnt[t & 1][16 * gw + 4 * lg + j][kw] = __popc(gtb) | (__popc(eqb) << 16);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 c = *reinterpret_cast<const u32x4*>(&tcnt[t & 1][16 * gw + 4 * lg + j][0]);
+          uint32_t pre = 0, tot = 0;   // (above, equal) counts of the earlier slices / all slices
+#pragma unroll
+          for (int w = 0; w < TK_KW; ++w) {
+            if (w < kw) pre += c[w];
+            tot += c[w];
+          }
+          const int pre_gt = (int)(pre & 0xffffu), pre_eq = (int)(pre >> 16);
+          const int lft = max(left[j], 0);
+          const bool sel = ((ge[j] >> li) & 1u) ||
+                           (((ge[j] >> (16 + li)) & 1u) &&
+                            pre_eq + __popc((ge[j] >> 16) & below) < lft);
+          const uint32_t selbits = (uint32_t)(__ballot(sel) >> (16 * lg)) & 0xffffu;
+          const int pos = cnt[j] + pre_gt + min(lft, pre_eq) + __popc(selbits & below);
+          if (sel && pos < kh) orow[j * kh + pos] = m;
+          cnt[j] += (int)(tot & 0xffffu) + min(lft, (int)(tot >> 16));
+          left[j] -= (int)(tot >> 16);
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) bcur[i] = bnxt[i];
+      }
     }
 
     if (pass < 4) {
-      // Each wave resolves digit `pass` for its own 16 groups and clears their histograms.
-      for (int gi = 0; gi < 16; ++gi) {
-        const int gl = 16 * wave + gi;
+      __syncthreads();
+      // Each wave resolves digit `pass` for some of the groups and clears their histograms.
+      for (int gl = wave; gl < TK_GROUPS; gl += TK_WAVES) {
         if (st_npass[gl] != pass) continue;   // uniform across the wave
         uint32_t* hrow = &hist[gl * TK_HSTRIDE];
         uint32_t c[4];
