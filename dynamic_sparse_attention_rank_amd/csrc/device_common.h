@@ -29,6 +29,18 @@ __device__ __forceinline__ floatx4 mfma_f32(float a, float b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// 32 x 32 tiles: A (32 x 16) lane l holds row l % 32, 8 contraction elements of slot l / 32;
+// B likewise for column l % 32; C element 4i + j of lane l is row 8i + 4(l / 32) + j, column
+// l % 32. The fp32 form contracts one element per slot.
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ floatx16 mfma32_bf16(const u32x4& a, const u32x4& b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ floatx16 mfma32_f32(float a, float b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
 // Two floats -> packed bf16 pair (round to nearest even), `lo` in bits 0..15.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

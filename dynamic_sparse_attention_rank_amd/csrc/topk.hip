@@ -9,23 +9,23 @@
 // tiles, each time the key stream is traversed.
 //
 // Design (gfx950):
-//   * Workgroup = TK_GW x TK_KW waves over 16 TK_GW groups of one (b, h). Wave (gw, kw) scores
-//     groups 16 gw .. 16 gw + 15 against keys 16 kw .. 16 kw + 15 of every TK_TILE-key tile, so
-//     the TK_KW waves of a group block split the key stream and share its LDS histograms. The
-//     16-row A operand of v_mfma_f32_16x16x32_bf16 holds the group sums (split into two bf16
-//     terms, hi + lo, so that the sums stay exact); the B operand (16 keys of K_lr) is loaded
-//     straight from memory into registers, one tile ahead. Each 16x16 output tile gives a lane
-//     one key and four groups.
+//   * Workgroup = TK_KW waves over 32 groups of one (b, h). Scores come in 32 x 32 MFMA tiles
+//     (v_mfma_f32_32x32x16_bf16) with keys as rows and groups as columns: A is 32 rows of K_lr,
+//     loaded straight from memory into registers, and B holds the group sums (each split into
+//     two bf16 terms, hi + lo, so that the sums stay exact). Lane l then owns group l % 32 and
+//     16 of the 32 keys (rows 8i + 4(l / 32) + j); its partner lane l ^ 32 owns the other 16.
+//     Wave kw scores keys 32 kw .. 32 kw + 31 of every TK_TILE-key tile, so the waves split
+//     the key stream and share the workgroup's LDS histograms.
 //   * Exact selection = radix select on an order-preserving 32-bit image of the fp32 score,
 //     8 bits per pass: pass p builds, per group, an LDS histogram of digit p over the keys whose
 //     higher digits match the prefix found so far; a wave scan then fixes the digit holding the
-//     k-th largest key. A group stops refining as soon as its whole current bin is needed.
-//     Lane li adds its four groups' counts in the rotated order (j + li) mod 4, so one LDS
-//     atomic instruction touches 16 different groups (at most 4 lanes per histogram) even when
-//     all scores fall into the same bin, as they do for the exponent byte of pass 0.
+//     k-th largest key. A group stops refining as soon as its whole current bin is needed, or
+//     when every key counted in the pass had zero bits below the digit (then the bin's keys are
+//     all equal). One LDS atomic instruction touches 32 different groups' histograms.
 //   * A final pass compacts, per group, the keys above the threshold plus the first `need` keys
-//     equal to it, in ascending key order: wave ballots rank a lane's key inside its 16-key
-//     slice, and per-tile slice counts in LDS give each slice its offset.
+//     equal to it, in ascending key order. A lane keeps bit masks of its 16 keys that are above
+//     or equal; bit counts of its own and its partner's masks rank a key inside the wave's
+//     32-key slice, and per-tile slice counts in LDS give each slice its offset.
 //   * Consecutive workgroups go to different XCDs; the block index is remapped so that the
 //     workgroups of one (b, h) share an XCD (and its L2) while they stream the same K_lr.
 #include "device_common.h"
@@ -34,13 +34,12 @@
 namespace dsv {
 namespace {
 
-constexpr int TK_GW = 2;                   // group waves per workgroup (16 groups each)
-constexpr int TK_KW = 4;                   // key slices per workgroup (16 keys of a tile each)
-constexpr int TK_WAVES = TK_GW * TK_KW;
-constexpr int TK_THREADS = 64 * TK_WAVES;
-constexpr int TK_GROUPS = 16 * TK_GW;      // groups per workgroup
-constexpr int TK_TILE = 16 * TK_KW;        // keys per step of the workgroup
+constexpr int TK_GROUPS = 32;              // groups per workgroup (a lane pair each)
+constexpr int TK_KW = 16;                  // waves = key slices per workgroup
+constexpr int TK_THREADS = 64 * TK_KW;
+constexpr int TK_TILE = 32 * TK_KW;        // keys per step of the workgroup
 constexpr int TK_HSTRIDE = 257;            // 256 bins + 1 pad word per group histogram
+constexpr int TK_SUMW = 4;                 // waves that sum the groups' Q_lr rows
 
 // Order-preserving map float -> uint32 (larger score <=> larger key). -0 is folded onto +0.
 __device__ __forceinline__ uint32_t score_key(float s) {
@@ -48,19 +47,26 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
+// Contraction layout. bf16: k-step i covers features 16i .. 16i + 15, lane slot h = l / 32 holds
+// 16i + 8h .. 16i + 8h + 7 (one 16-byte load). fp32: slot h holds features h R/2 .. h R/2 + R/2 - 1,
+// one per v_mfma_f32_32x32x2f32 step (R/8 16-byte loads). A lane's own feature f (< R/2) is
+// element f of its loads in both cases.
 template <bool F32, int R>
 struct TopkCfg {
   static constexpr int ES = F32 ? 4 : 2;             // bytes per element
-  static constexpr int RB = R * ES;                  // bytes per K_lr row
-  static constexpr int KSTEPS = F32 ? R / 4 : (R + 31) / 32;   // MFMA contraction steps
+  static constexpr int RB = R * ES;                  // bytes per row
+  static constexpr int NB = F32 ? R / 8 : R / 16;    // 16-byte loads per lane and row
+  static constexpr int NF = R / 2;                   // features per lane
+  __device__ static int off(int i, int h) { return F32 ? 2 * h * R + 16 * i : 32 * i + 16 * h; }
 };
 
 template <bool F32, int R>
-__global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(6))) void topk_kernel(const void* __restrict__ qlr_,
+__global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict__ qlr_,
                                                           const void* __restrict__ klr_,
                                                           int32_t* __restrict__ idx, Geom geo) {
   using C = TopkCfg<F32, R>;
-  __shared__ uint32_t hist[TK_GROUPS * TK_HSTRIDE];
+  static_assert(TK_SUMW * 64 * C::NF <= TK_GROUPS * TK_HSTRIDE, "partial sums overflow");
+  __shared__ uint32_t hist[TK_GROUPS * TK_HSTRIDE];   // also the group sums' partials, first
   // compaction: per tile parity, group and key slice, the slice's count of keys above the
   // threshold (bits 0..15) and equal to it (bits 16..31)
   __shared__ __attribute__((aligned(16))) uint32_t tcnt[2][TK_GROUPS][TK_KW];
@@ -70,14 +76,14 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   // next histogram pass is that index); 16 + D = finished with D digits known.
   __shared__ int st_npass[TK_GROUPS];
   __shared__ int st_active[4];
+  // per group: set when a key counted in the current pass has a nonzero bit below the digit
+  __shared__ uint32_t st_lowbits[TK_GROUPS];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int kw = tid >> 6;       // wave = key slice
   const int lane = tid & 63;
-  const int lg = lane >> 4;
-  const int li = lane & 15;
-  const int gw = wave / TK_KW;
-  const int kw = wave - gw * TK_KW;
+  const int g = lane & 31;       // group of the workgroup
+  const int hh = lane >> 5;      // contraction slot / key half
 
   // block -> (b, h, group block): blocks x, x + 8, x + 16, .. run on XCD x % 8, and they get
   // consecutive logical indices, so that one (b, h)'s blocks share an XCD
@@ -93,98 +99,124 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
   const int S = geo.S;
   const int kh = geo.k[h];
   const long long head_base = (long long)bh * S * R;   // element offset of (b,h) in Q_lr/K_lr
-
   const unsigned char* klr = static_cast<const unsigned char*>(klr_) + head_base * C::ES;
   const unsigned char* qlr = static_cast<const unsigned char*>(qlr_) + head_base * C::ES;
+  const int my_group = gblock * TK_GROUPS + g;
 
-  // ---- group state
-  for (int i = tid; i < TK_GROUPS; i += TK_THREADS) {
-    st_prefix[i] = 0;
-    st_krem[i] = kh;
-    st_npass[i] = (gblock * TK_GROUPS + i < geo.NG) ? 0 : -1;   // -1: no such group
-  }
-  for (int i = tid; i < TK_GROUPS * TK_HSTRIDE; i += TK_THREADS) hist[i] = 0;
-
-  // ---- group sums -> A operands (row li = group 16*gw + li); each key slice sums its own copy
-  const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
-  const int my_group = gblock * TK_GROUPS + 16 * gw + li;
-  float ssum[C::KSTEPS * (F32 ? 1 : 8)];
+  // ---- group sums: waves 0 .. TK_SUMW-1 sum every TK_SUMW-th member row of the lane's group
+  // into LDS partials; every wave then adds the partials in the same order (deterministic)
+  float* part = reinterpret_cast<float*>(hist);
+  if (kw < TK_SUMW) {
+    float ps[C::NF];
 #pragma unroll
-  for (int i = 0; i < C::KSTEPS * (F32 ? 1 : 8); ++i) ssum[i] = 0.0f;
-  if (my_group < geo.NG) {
-    for (int j = 0; j < geo.G; ++j) {
-      const int n = gg.token(my_group, j);
-      const unsigned char* row = qlr + (long long)n * C::RB;
-      if constexpr (F32) {
-        const float* fr = reinterpret_cast<const float*>(row) + lg * (R / 4);
+    for (int f = 0; f < C::NF; ++f) ps[f] = 0.0f;
+    if (my_group < geo.NG) {
+      const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
+      for (int j = kw; j < geo.G; j += TK_SUMW) {
+        const unsigned char* row = qlr + (long long)gg.token(my_group, j) * C::RB;
 #pragma unroll
-        for (int s = 0; s < R / 4; ++s) ssum[s] += fr[s];
-      } else {
+        for (int i = 0; i < C::NB; ++i) {
+          const u32x4 v = ld16(row + C::off(i, hh));
+          if constexpr (F32) {
 #pragma unroll
-        for (int ks = 0; ks < C::KSTEPS; ++ks) {
-          if (ks * 32 + 8 * lg < R) {
-            const u32x4 v = ld16(row + (ks * 32 + 8 * lg) * 2);
+            for (int e = 0; e < 4; ++e) ps[4 * i + e] += __uint_as_float(v[e]);
+          } else {
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              ssum[ks * 8 + 2 * e2] += bf16_lo(v[e2]);
-              ssum[ks * 8 + 2 * e2 + 1] += bf16_hi(v[e2]);
+            for (int e = 0; e < 4; ++e) {
+              ps[8 * i + 2 * e] += bf16_lo(v[e]);
+              ps[8 * i + 2 * e + 1] += bf16_hi(v[e]);
             }
           }
         }
       }
     }
+#pragma unroll
+    for (int f = 0; f < C::NF; ++f) part[(kw * C::NF + f) * 64 + lane] = ps[f];
   }
-  // bf16 path: s = hi + lo with hi = bf16(s), lo = bf16(s - hi); exact while |s| < 2^16 for
-  // integer sums, and products with bf16 K_lr entries are exact in the fp32 accumulator.
-  u32x4 a_hi[F32 ? 1 : C::KSTEPS], a_lo[F32 ? 1 : C::KSTEPS];
+  __syncthreads();
+  float ssum[C::NF];
+#pragma unroll
+  for (int f = 0; f < C::NF; ++f) {
+    ssum[f] = part[f * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < TK_SUMW; ++w) ssum[f] += part[(w * C::NF + f) * 64 + lane];
+  }
+  // bf16 B operands: s = hi + lo with hi = bf16(s), lo = bf16(s - hi); exact while |s| < 2^16
+  // for integer sums, and products with bf16 K_lr entries are exact in the fp32 accumulator.
+  u32x4 b_hi[F32 ? 1 : C::NB], b_lo[F32 ? 1 : C::NB];
   if constexpr (!F32) {
 #pragma unroll
-    for (int ks = 0; ks < C::KSTEPS; ++ks) {
+    for (int i = 0; i < C::NB; ++i) {
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const float s0 = ssum[ks * 8 + 2 * e2], s1 = ssum[ks * 8 + 2 * e2 + 1];
+      for (int e = 0; e < 4; ++e) {
+        const float s0 = ssum[8 * i + 2 * e], s1 = ssum[8 * i + 2 * e + 1];
         const float h0 = bf16_round(s0), h1 = bf16_round(s1);
-        a_hi[ks][e2] = pack_bf16(h0, h1);
-        a_lo[ks][e2] = pack_bf16(s0 - h0, s1 - h1);
+        b_hi[i][e] = pack_bf16(h0, h1);
+        b_lo[i][e] = pack_bf16(s0 - h0, s1 - h1);
       }
     }
   }
+  __syncthreads();   // partials read: the histograms take their place
 
-  // ---- B operands: key m = TK_TILE t + 16 kw + li of tile t (clamped to the last key; the
-  // scores of keys past the end are never counted), contraction slot lg
-  constexpr int NB = F32 ? R / 16 : C::KSTEPS;   // 16-byte loads per lane and tile
-  auto load_b = [&](int t, u32x4* bo) {
-    const int m = min(t * TK_TILE + 16 * kw + li, S - 1);
+  for (int i = tid; i < TK_GROUPS; i += TK_THREADS) {
+    st_prefix[i] = 0;
+    st_lowbits[i] = 0;
+    st_krem[i] = kh;
+    st_npass[i] = (gblock * TK_GROUPS + i < geo.NG) ? 0 : -1;   // -1: no such group
+  }
+  for (int i = tid; i < TK_GROUPS * TK_HSTRIDE; i += TK_THREADS) hist[i] = 0;
+
+  // ---- A operands: key row TK_TILE t + 32 kw + lane % 32 of tile t (clamped to the last key;
+  // the scores of keys past the end are never counted)
+  auto load_a = [&](int t, u32x4* a) {
+    const int m = min(t * TK_TILE + 32 * kw + g, S - 1);
     const unsigned char* krow = klr + (long long)m * C::RB;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      if constexpr (F32) {
-        bo[i] = ld16(krow + (lg * (R / 4) + 4 * i) * 4);
-      } else {
-        bo[i] = (i * 32 + 8 * lg < R) ? ld16(krow + (i * 32 + 8 * lg) * 2) : u32x4{0, 0, 0, 0};
-      }
-    }
+    for (int i = 0; i < C::NB; ++i) a[i] = ld16(krow + C::off(i, hh));
   };
-  // scores of the wave's 16 groups (rows 4 lg + j) against its key of the tile (column li)
-  auto scores = [&](const u32x4* bo) -> floatx4 {
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  // scores of the tile's 32 keys (rows) for the 32 groups (columns)
+  auto scores = [&](const u32x4* a) -> floatx16 {
+    floatx16 acc;
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) {
       if constexpr (F32) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mfma_f32(ssum[4 * i + e], __uint_as_float(bo[i][e]), acc);
+        for (int e = 0; e < 4; ++e) acc = mfma32_f32(__uint_as_float(a[i][e]), ssum[4 * i + e], acc);
       } else {
-        acc = mfma_bf16(a_hi[i], bo[i], acc);
-        acc = mfma_bf16(a_lo[i], bo[i], acc);
+        acc = mfma32_bf16(a[i], b_hi[i], acc);
+        acc = mfma32_bf16(a[i], b_lo[i], acc);
       }
     }
     return acc;
   };
-  const int ntiles = (S + TK_TILE - 1) / TK_TILE;
+  const int nfull = S / TK_TILE;   // tiles without keys past the end
+  // Walks the key tiles in order, calling body(scores, t, Flag<partial>): operands are loaded
+  // two tiles ahead and scored one tile ahead, so neither the loads nor the MFMAs wait in line.
+  auto walk = [&](auto&& body) {
+    u32x4 a0[C::NB], a1[C::NB];
+    load_a(0, a0);
+    load_a(1, a1);
+    floatx16 acc = scores(a0);
+    for (int t = 0; t < nfull; t += 2) {
+      load_a(t + 2, a0);
+      floatx16 nxt = scores(a1);
+      body(acc, t, Flag<false>{});
+      acc = nxt;
+      if (t + 1 >= nfull) break;
+      load_a(t + 3, a1);
+      nxt = scores(a0);
+      body(acc, t + 1, Flag<false>{});
+      acc = nxt;
+    }
+    if (nfull * TK_TILE < S) body(acc, nfull, Flag<true>{});   // acc holds tile nfull
+  };
 
   __syncthreads();
 
-  // ---- radix passes (pass 4 = compaction)
+  // ---- radix passes (pass 4 = compaction). Element 4i + j of a lane's scores is key
+  // TK_TILE t + 32 kw + 8i + 4 hh + j.
   for (int pass = 0; pass <= 4; ++pass) {
     if (pass < 4) {
       if (tid == 0) {
@@ -195,108 +227,109 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
       __syncthreads();
       if (!st_active[pass]) continue;   // uniform: every group stopped refining earlier
     }
-    const int dshift = 24 - 8 * pass;
-    const int pshift = 32 - 8 * pass;
-    u32x4 bcur[NB], bnxt[NB];
-    load_b(0, bcur);
     if (pass < 4) {
-      // Histogram pass. Slot j of lane li is group 4 lg + (j + li) % 4 of the wave's block.
-      uint32_t rpfx[4];
-      int rstate[4];
-      uint32_t* rhist[4];
+      // Histogram pass. The lane also ORs the bits below the digit over the keys it counts.
+      const int dshift = 24 - 8 * pass;
+      const int pshift = 32 - 8 * pass;
+      const uint32_t pfx = st_prefix[g];
+      const bool act = st_npass[g] == pass;
+      const bool p0 = pass == 0;
+      uint32_t* const hrow = &hist[g * TK_HSTRIDE];
+      uint32_t lowor = 0;
+      auto count = [&](const floatx16& acc, int t, auto tail_tag, auto first_tag) {
+        constexpr bool kTail = decltype(tail_tag)::value;
+        constexpr bool kFirst = decltype(first_tag)::value;
+        const int mb = t * TK_TILE + 32 * kw + 4 * hh;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gl = 16 * gw + 4 * lg + ((j + li) & 3);
-        rpfx[j] = st_prefix[gl];
-        rstate[j] = st_npass[gl];
-        rhist[j] = &hist[gl * TK_HSTRIDE];
-      }
-      for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) load_b(t + 1, bnxt);
-        const floatx4 acc = scores(bcur);
-        const bool mvalid = t * TK_TILE + 16 * kw + li < S;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int jr = (j + li) & 3;
-          const float sc = jr == 0 ? acc[0] : jr == 1 ? acc[1] : jr == 2 ? acc[2] : acc[3];
-          const uint32_t key = score_key(sc);
-          const bool take = mvalid && rstate[j] == pass &&
-                            (pass == 0 || (key >> (pshift & 31)) == rpfx[j]);
-          if (take)
-            __hip_atomic_fetch_add(&rhist[j][(key >> dshift) & 255u], 1u, __ATOMIC_RELAXED,
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t key = score_key(acc[e]);
+          bool take = act;
+          if constexpr (kTail) take = take && mb + 8 * (e >> 2) + (e & 3) < S;
+          if constexpr (!kFirst) take = take && (key >> (pshift & 31)) == pfx;
+          if (take) {
+            __hip_atomic_fetch_add(&hrow[(key >> dshift) & 255u], 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
+            if constexpr (!kFirst) lowor |= key;
+          }
         }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) bcur[i] = bnxt[i];
+      };
+      if (p0) {   // every key of an active group counts; its low bits are not tracked
+        walk([&](const floatx16& acc, int t, auto tail) { count(acc, t, tail, Flag<true>{}); });
+        lowor = 1u;
+      } else {
+        walk([&](const floatx16& acc, int t, auto tail) { count(acc, t, tail, Flag<false>{}); });
       }
+      if ((lowor & ((1u << dshift) - 1u)) != 0) st_lowbits[g] = 1u;   // any lane: not zero
     } else {
-      // Compaction. Lane: key m, groups 4 lg + j of the wave's block, all finished.
-      uint32_t pfx[4];
-      int shift[4], cnt[4], left[4];
+      // Compaction. Both lanes of a group keep the same running state.
+      const int gs = st_npass[g];
+      const uint32_t pfx = gs >= 16 ? st_prefix[g] : 0xffffffffu;
+      const int shift = gs >= 16 ? 32 - 8 * (gs - 16) : 0;   // no key exceeds all-ones
+      int left = gs >= 16 ? st_krem[g] : 0;                    // equal keys still to take
+      int cnt = 0;
+      int32_t* const orow = idx + geo.row_offset(b, h, gs >= 0 ? my_group : 0);
+      walk([&](const floatx16& acc, int t, auto tail_tag) {
+        constexpr bool kTail = decltype(tail_tag)::value;
+        const int mb = t * TK_TILE + 32 * kw + 4 * hh;
+        uint32_t gtm = 0, eqm = 0;   // bit e: element e above / equal
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int gl = 16 * gw + 4 * lg + j;
-        const int gs = st_npass[gl];
-        pfx[j] = gs >= 16 ? st_prefix[gl] : 0xffffffffu;
-        shift[j] = gs >= 16 ? 32 - 8 * (gs - 16) : 0;   // no key exceeds an all-ones image
-        left[j] = gs >= 16 ? st_krem[gl] : 0;            // equal keys still to take
-        cnt[j] = 0;
-      }
-      // rows of groups 4 lg + j are consecutive (k_h entries each); groups past NG select nothing
-      int32_t* const orow = idx + geo.row_offset(b, h, gblock * TK_GROUPS + 16 * gw + 4 * lg);
-      const uint32_t below = (1u << li) - 1u;
-      for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) load_b(t + 1, bnxt);
-        const floatx4 acc = scores(bcur);
-        const int m = t * TK_TILE + 16 * kw + li;
-        const bool mvalid = m < S;
-        uint32_t ge[4];   // this slice's ballots of the key's group j: above (bits 0..15), equal
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t v = score_key(acc[j]) >> (shift[j] & 31);
-          const uint32_t gtb = (uint32_t)(__ballot(mvalid && v > pfx[j]) >> (16 * lg)) & 0xffffu;
-          const uint32_t eqb = (uint32_t)(__ballot(mvalid && v == pfx[j]) >> (16 * lg)) & 0xffffu;
-          ge[j] = gtb | (eqb << 16);
-          if (li == 0)
-            tcnt[t & 1][16 * gw + 4 * lg + j][kw] = __popc(gtb) | (__popc(eqb) << 16);
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t v = score_key(acc[e]) >> (shift & 31);
+          bool valid = true;
+          if constexpr (kTail) valid = mb + 8 * (e >> 2) + (e & 3) < S;
+          gtm |= (uint32_t)(valid & (v > pfx)) << e;
+          eqm |= (uint32_t)(valid & (v == pfx)) << e;
         }
+        const uint32_t both = gtm | (eqm << 16);
+        const uint32_t pboth = (uint32_t)__shfl_xor((int)both, 32, 64);
+        const uint32_t pgtm = pboth & 0xffffu, peqm = pboth >> 16;
+        tcnt[t & 1][g][kw] = (uint32_t)(__popc(gtm) + __popc(pgtm)) |
+                             ((uint32_t)(__popc(eqm) + __popc(peqm)) << 16);
         __syncthreads();
+        uint32_t pre = 0, tot = 0;   // (above, equal) counts of the earlier slices / all slices
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4 c = *reinterpret_cast<const u32x4*>(&tcnt[t & 1][16 * gw + 4 * lg + j][0]);
-          uint32_t pre = 0, tot = 0;   // (above, equal) counts of the earlier slices / all slices
+        for (int w4 = 0; w4 < TK_KW; w4 += 4) {
+          const u32x4 c = *reinterpret_cast<const u32x4*>(&tcnt[t & 1][g][w4]);
 #pragma unroll
-          for (int w = 0; w < TK_KW; ++w) {
-            if (w < kw) pre += c[w];
+          for (int w = 0; w < 4; ++w) {
+            if (w4 + w < kw) pre += c[w];
             tot += c[w];
           }
-          const int pre_gt = (int)(pre & 0xffffu), pre_eq = (int)(pre >> 16);
-          const int lft = max(left[j], 0);
-          const bool sel = ((ge[j] >> li) & 1u) ||
-                           (((ge[j] >> (16 + li)) & 1u) &&
-                            pre_eq + __popc((ge[j] >> 16) & below) < lft);
-          const uint32_t selbits = (uint32_t)(__ballot(sel) >> (16 * lg)) & 0xffffu;
-          const int pos = cnt[j] + pre_gt + min(lft, pre_eq) + __popc(selbits & below);
-          if (sel && pos < kh) orow[j * kh + pos] = m;
-          cnt[j] += (int)(tot & 0xffffu) + min(lft, (int)(tot >> 16));
-          left[j] -= (int)(tot >> 16);
         }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) bcur[i] = bnxt[i];
-      }
+        const int pre_gt = (int)(pre & 0xffffu), pre_eq = (int)(pre >> 16);
+        const int lft = max(left, 0);
+        const int base = cnt + pre_gt + min(lft, pre_eq);
+        // the lane's selected keys, one at a time (about 10 % of them); eqm is zero in most tiles
+        const int lr = max(lft - pre_eq, 0);   // equal keys this slice may still take
+        uint32_t todo = gtm | eqm;
+        while (todo != 0u) {
+          const int e = __builtin_ctz(todo);
+          todo &= todo - 1u;
+          const int i = e >> 2;
+          const uint32_t own = (1u << e) - 1u;
+          const uint32_t par = (1u << (4 * i + 4 * hh)) - 1u;   // partner blocks before e
+          const int gtb = __popc(gtm & own) + __popc(pgtm & par);
+          const int eqb = __popc(eqm & own) + __popc(peqm & par);
+          const bool sel = ((gtm >> e) & 1u) || eqb < lr;
+          const int pos = base + gtb + min(lr, eqb);
+          if (sel && pos < kh) orow[pos] = mb + 8 * i + (e & 3);
+        }
+        cnt += (int)(tot & 0xffffu) + min(lft, (int)(tot >> 16));
+        left -= (int)(tot >> 16);
+      });
     }
 
     if (pass < 4) {
       __syncthreads();
       // Each wave resolves digit `pass` for some of the groups and clears their histograms.
-      for (int gl = wave; gl < TK_GROUPS; gl += TK_WAVES) {
+      for (int gl = kw; gl < TK_GROUPS; gl += TK_KW) {
         if (st_npass[gl] != pass) continue;   // uniform across the wave
-        uint32_t* hrow = &hist[gl * TK_HSTRIDE];
+        uint32_t* hr = &hist[gl * TK_HSTRIDE];
         uint32_t c[4];
         uint32_t lsum = 0;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-          c[tt] = hrow[255 - (4 * lane + tt)];
+          c[tt] = hr[255 - (4 * lane + tt)];
           lsum += c[tt];
         }
         uint32_t incl = lsum;
@@ -315,14 +348,16 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(6)))
               const uint32_t left = krem - excl;   // keys still needed inside `bin`
               st_prefix[gl] = (pass == 0) ? bin : ((st_prefix[gl] << 8) | bin);
               st_krem[gl] = (int)left;
-              st_npass[gl] = (left == c[tt] || pass == 3) ? 16 + pass + 1 : pass + 1;
+              st_npass[gl] = (left == c[tt] || pass == 3 || st_lowbits[gl] == 0)
+                                 ? 16 + pass + 1 : pass + 1;
               break;
             }
             excl += c[tt];
           }
         }
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) hrow[4 * lane + tt] = 0;
+        for (int tt = 0; tt < 4; ++tt) hr[4 * lane + tt] = 0;
+        st_lowbits[gl] = 0;
       }
       __syncthreads();
     }
