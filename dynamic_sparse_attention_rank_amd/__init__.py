@@ -26,13 +26,18 @@ STATUS = {0: "DSV_OK", 1: "DSV_ERR_NULL", 2: "DSV_ERR_SHAPE", 3: "DSV_ERR_K",
 EXPORTED = ("dsv_workspace_bytes", "dsv_idx_elems", "dsv_idx_row_offset", "dsv_lowrank_topk",
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd", "dsv_bwd_chunks",
             "dsv_sparse_attn_bwd_profiled", "dsv_validate", "dsv_status_string",
-            "dsv_last_error", "dsv_version")
+            "dsv_last_error", "dsv_version", "dsv_plan_heads", "dsv_default_cost_model",
+            "dsv_dispatch_k")
 
 
 class DsvError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{STATUS.get(status, status)}: {message}")
         self.status = status
+
+
+class CostModel(ctypes.Structure):
+    _fields_ = [("topk_ns_per_score", ctypes.c_double), ("attn_ns_per_edge", ctypes.c_double)]
 
 
 class Problem(ctypes.Structure):
@@ -95,12 +100,18 @@ def lib() -> ctypes.CDLL:
         L.dsv_bwd_chunks.restype = ctypes.c_int
         L.dsv_validate.argtypes = [ctypes.c_int, P, i32p, ctypes.c_int,
                                    ctypes.POINTER(vp), ctypes.c_int, sz]
+        dp = ctypes.POINTER(ctypes.c_double)
+        L.dsv_plan_heads.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                                     ctypes.c_double, i32p, dp, dp]
+        L.dsv_default_cost_model.argtypes = [P, ctypes.c_int, ctypes.POINTER(CostModel)]
+        L.dsv_dispatch_k.argtypes = [P, i32p, ctypes.POINTER(CostModel), i32p, i32p]
         L.dsv_status_string.restype = ctypes.c_char_p
         L.dsv_status_string.argtypes = [ctypes.c_int]
         L.dsv_last_error.restype = ctypes.c_char_p
         L.dsv_version.restype = ctypes.c_char_p
         for fn in ("dsv_lowrank_topk", "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd",
-                   "dsv_sparse_attn_bwd_profiled", "dsv_validate"):
+                   "dsv_sparse_attn_bwd_profiled", "dsv_validate", "dsv_plan_heads",
+                   "dsv_default_cost_model", "dsv_dispatch_k"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -142,6 +153,37 @@ def validate(op: int, p: Problem, k_per_head: Sequence[int], ptrs: Sequence[int]
     arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
     return int(lib().dsv_validate(op, ctypes.byref(p), _kph(k_per_head), reduce, arr,
                                   len(ptrs), ws_bytes))
+
+
+def plan_heads(k_per_head: Sequence[int], n_parts: int, fixed_cost: float = 0.0,
+               cost_per_k: float = 1.0) -> Tuple[List[int], List[float], float]:
+    """(part of each head, load of each part, rho_s) of the longest-processing-time placement
+    of heads with cost fixed_cost + cost_per_k * k_h over n_parts devices."""
+    H = len(k_per_head)
+    part = (ctypes.c_int32 * max(H, 1))()
+    load = (ctypes.c_double * max(n_parts, 1))()
+    rho = ctypes.c_double()
+    _check(lib().dsv_plan_heads(_kph(k_per_head), H, n_parts, float(fixed_cost),
+                                float(cost_per_k), part, load, ctypes.byref(rho)))
+    return list(part)[:H], list(load)[:n_parts], rho.value
+
+
+def default_cost_model(p: Problem, with_backward: bool = True) -> CostModel:
+    """Measured MI355X per-unit costs of this library's kernels, scaled to the problem."""
+    cm = CostModel()
+    _check(lib().dsv_default_cost_model(ctypes.byref(p), int(with_backward), ctypes.byref(cm)))
+    return cm
+
+
+def dispatch_k(p: Problem, k_per_head: Sequence[int],
+               cost_model: Optional[CostModel] = None) -> Tuple[List[int], int]:
+    """(k per head after the dense-versus-sparse choice, number of dense heads)."""
+    cm = cost_model if cost_model is not None else default_cost_model(p)
+    out = (ctypes.c_int32 * p.heads)()
+    nd = ctypes.c_int32()
+    _check(lib().dsv_dispatch_k(ctypes.byref(p), _kph(k_per_head), ctypes.byref(cm), out,
+                                ctypes.byref(nd)))
+    return list(out), nd.value
 
 
 # ----------------------------------------------------------------------------- torch layer

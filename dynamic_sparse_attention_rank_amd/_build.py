@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libdsv.so")
-SOURCES = ["dsv_api.cpp", "topk.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["dsv_api.cpp", "dsv_plan.cpp", "topk.hip", "attn_fwd.hip", "attn_bwd.hip"]
 ARCH = os.environ.get("DSV_OFFLOAD_ARCH", "gfx950")
 # The forward keeps its output accumulators in VGPRs (MFMA results written to VGPRs, not
 # AGPRs): its lazy rescale multiplies them with VALU ops, and with AGPR accumulators the

@@ -103,6 +103,14 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
   const unsigned char* qlr = static_cast<const unsigned char*>(qlr_) + head_base * C::ES;
   const int my_group = gblock * TK_GROUPS + g;
 
+  if (kh == S) {   // dense head: every key, in order, without scoring
+    for (int gi = 0; gi < TK_GROUPS && gblock * TK_GROUPS + gi < geo.NG; ++gi) {
+      int32_t* row = idx + geo.row_offset(b, h, gblock * TK_GROUPS + gi);
+      for (int m = tid; m < S; m += TK_THREADS) row[m] = m;
+    }
+    return;
+  }
+
   // ---- group sums: waves 0 .. TK_SUMW-1 sum every TK_SUMW-th member row of the lane's group
   // into LDS partials; every wave then adds the partials in the same order (deterministic)
   float* part = reinterpret_cast<float*>(hist);

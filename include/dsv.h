@@ -160,6 +160,50 @@ int dsv_sparse_attn_bwd_profiled(const dsv_problem* p, const void* q, const void
                                  float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
                                  void* stream, void* const* events, int n_events);
 
+/* ---- Planning (host only; no HIP call, nothing enqueued) ---------------------------------- */
+
+/* Head placement over n_parts devices (DSV summaries: zh §2.3 "Head-wise CP Re-balancing",
+ * pt §2C, fr §2C, ko §2다: heads are assigned to GPUs by their sparsity so the compute load
+ * balances; db-SP summary, "核心方法" (core method): a head-level greedy, and the sparse
+ * imbalance ratio rho_s = max load / mean load from its "关键观察" (key observations)).
+ *   k_per_head   : host [heads], each >= 1.
+ *   fixed_cost, cost_per_k : cost of head h = fixed_cost + cost_per_k * k_h (any unit, >= 0,
+ *                  not both 0), e.g. the estimator's time per head and the attention time per
+ *                  unit of k (dsv_default_cost_model gives measured MI355X figures).
+ *   part_of_head : host [heads], written: the part (0 .. n_parts-1) each head goes to.
+ *   part_load    : host [n_parts] or NULL, written: the summed cost of each part.
+ *   rho          : host or NULL, written: max part load / mean part load (>= 1).
+ * Longest-processing-time greedy: heads in decreasing cost (equal costs: lower head index
+ * first), each to the part with the least load so far (equal loads: lower part index). The
+ * largest load is at most (4/3 - 1/(3 n_parts)) times the optimum. The kernels launch the heads
+ * of one device in this same decreasing-cost order. */
+int dsv_plan_heads(const int32_t* k_per_head, int32_t heads, int32_t n_parts, double fixed_cost,
+                   double cost_per_k, int32_t* part_of_head, double* part_load, double* rho);
+
+/* Per-unit costs of this library's kernels on one MI355X, for planning and dispatch. */
+typedef struct {
+  double topk_ns_per_score;  /* critical-KV estimation, per (group, key) score */
+  double attn_ns_per_edge;   /* sparse attention, per (group, selected key) edge */
+} dsv_cost_model;
+
+/* Fills `cm` with figures measured on MI355X (the S=64K workload, scaled to the problem's
+ * rank, head_dim and group size in proportion to the work per unit): forward only
+ * (with_backward = 0) or forward + backward (1). */
+int dsv_default_cost_model(const dsv_problem* p, int with_backward, dsv_cost_model* cm);
+
+/* Dense-versus-sparse choice per head (DSV summaries: zh §2.1 stage two, the OP Dispatcher
+ * decides per block from its sparsity whether sparse attention runs). Per (b, h) the sparse
+ * path costs NG*S*topk_ns_per_score + NG*k_h*attn_ns_per_edge and dense attention
+ * NG*S*attn_ns_per_edge; a head goes dense when that is not more, i.e. when
+ * k_h >= S * (1 - topk_ns_per_score / attn_ns_per_edge).
+ *   k_in      : host [heads], the sparse k_h.
+ *   k_out     : host [heads], written: S for a dense head, else k_in[h]. Dense heads run
+ *               through the same kernels (dsv_lowrank_topk writes the full ascending row for
+ *               k_h = S without scoring).
+ *   n_dense   : host or NULL, written: the number of dense heads. */
+int dsv_dispatch_k(const dsv_problem* p, const int32_t* k_in, const dsv_cost_model* cm,
+                   int32_t* k_out, int32_t* n_dense);
+
 /* Validation only: returns the status the corresponding call would return for these
  * arguments before enqueueing anything (no HIP call is made). Pointers are checked for NULL
  * and 16-byte alignment; pass any non-NULL aligned values to check shapes alone. */

@@ -16,9 +16,12 @@ gist.science/{zh,pt,fr,ko}/paper/2502.07590):
   * attention - exact softmax attention restricted to each group's selected keys (zh §2.1
                 "sparse computation": full attention on the critical KV pairs only), forward
                 and backward, in a dense masked form and in a gathered form.
+  * planning  - head placement over devices by a longest-processing-time greedy and its
+                imbalance ratio (zh §2.3, db-SP summary), and the dense-versus-sparse choice
+                per head (zh §2.1 "OP Dispatcher").
 Readings the pages leave open (group reduction = SUM, ties -> lower key index, ascending
 rows, scale = 1/sqrt(d), natural-log LSE, no gradient through the selection) are stated in
 each function. Every function here is pinned by the CPU tests (see tests/test_oracle_*.py);
 the SUM reduction itself is pinned only to this definition, not to the paper's kernel.
 """
-from . import geometry, topk, attention  # noqa: F401
+from . import geometry, topk, attention, planning  # noqa: F401

@@ -45,6 +45,11 @@ TOPK_CASES = [
                       dtype="fp32"), [19, 64]),
     ("fp32-r48", dict(heads=1, frames=4, height=8, width=8, group=(1, 4, 4), rank=48,
                       dtype="fp32"), [100]),
+    # dense heads (k = S: every key, no scoring) next to sparse ones in one call
+    ("mixed-dense", dict(heads=3, frames=4, height=8, width=8, group=(2, 2, 4), rank=32),
+     [256, 40, 256]),
+    ("fp32-dense", dict(heads=2, frames=4, height=8, width=8, group=(2, 2, 4), rank=16,
+                        dtype="fp32"), [3, 256]),
 ]
 
 
