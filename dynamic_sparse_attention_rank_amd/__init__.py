@@ -27,7 +27,7 @@ EXPORTED = ("dsv_workspace_bytes", "dsv_idx_elems", "dsv_idx_row_offset", "dsv_l
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd", "dsv_bwd_chunks",
             "dsv_sparse_attn_bwd_profiled", "dsv_validate", "dsv_status_string",
             "dsv_last_error", "dsv_version", "dsv_plan_heads", "dsv_default_cost_model",
-            "dsv_dispatch_k")
+            "dsv_dispatch_k", "dsv_adaptive_k")
 
 
 class DsvError(RuntimeError):
@@ -105,13 +105,14 @@ def lib() -> ctypes.CDLL:
                                      ctypes.c_double, i32p, dp, dp]
         L.dsv_default_cost_model.argtypes = [P, ctypes.c_int, ctypes.POINTER(CostModel)]
         L.dsv_dispatch_k.argtypes = [P, i32p, ctypes.POINTER(CostModel), i32p, i32p]
+        L.dsv_adaptive_k.argtypes = [P, vp, vp, f, ctypes.c_double, vp, vp, vp]
         L.dsv_status_string.restype = ctypes.c_char_p
         L.dsv_status_string.argtypes = [ctypes.c_int]
         L.dsv_last_error.restype = ctypes.c_char_p
         L.dsv_version.restype = ctypes.c_char_p
         for fn in ("dsv_lowrank_topk", "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd",
                    "dsv_sparse_attn_bwd_profiled", "dsv_validate", "dsv_plan_heads",
-                   "dsv_default_cost_model", "dsv_dispatch_k"):
+                   "dsv_default_cost_model", "dsv_dispatch_k", "dsv_adaptive_k"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -233,6 +234,28 @@ def lowrank_topk(p: Problem, q_lr, k_lr, k_per_head: Sequence[int], idx=None,
     _check(lib().dsv_lowrank_topk(ctypes.byref(p), qp, kp, _kph(k_per_head), reduce, ip,
                                   None, 0, _stream_ptr(stream)))
     return idx
+
+
+def adaptive_k(p: Problem, q_lr, k_lr, mass: float = 0.9, logit_scale: Optional[float] = None,
+               k_group=None, stream=None):
+    """(k_head [H], k_group [B, H, NG]) int32 device tensors: per group, the keys that carry
+    `mass` of the estimated attention (see include/dsv.h); logit_scale defaults to
+    1 / (sqrt(d) * G), the mean member logit."""
+    torch = _torch()
+    dt = _storage_dtype(p)
+    shp = (p.batch, p.heads, p.seq, p.rank)
+    qp = _dev(q_lr, "q_lr", dt, shp)
+    kp = _dev(k_lr, "k_lr", dt, shp)
+    if logit_scale is None:
+        logit_scale = 1.0 / (math.sqrt(p.head_dim) * p.group_size)
+    if k_group is None:
+        k_group = torch.empty((p.batch, p.heads, p.n_groups), dtype=torch.int32,
+                              device=q_lr.device)
+    gp = _dev(k_group, "k_group", torch.int32, (p.batch, p.heads, p.n_groups))
+    k_head = torch.empty(p.heads, dtype=torch.int32, device=q_lr.device)
+    _check(lib().dsv_adaptive_k(ctypes.byref(p), qp, kp, float(logit_scale), float(mass), gp,
+                                k_head.data_ptr(), _stream_ptr(stream)))
+    return k_head, k_group
 
 
 def sparse_attn_fwd(p: Problem, q, k, v, idx, k_per_head: Sequence[int],

@@ -2,12 +2,14 @@
 //
 // Every check runs before anything is enqueued, so a non-OK status leaves the stream and the
 // outputs untouched.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
 
 #include <algorithm>
 #include <numeric>
+#include <vector>
 
 #include "dsv_internal.h"
 
@@ -187,6 +189,30 @@ int dsv_lowrank_topk(const dsv_problem* p, const void* q_lr, const void* k_lr,
   validate_problem(p, k_per_head, &geo);
   int e = launch_topk(geo, q_lr, k_lr, idx, stream);
   if (e) return fail(DSV_ERR_HIP, "top-k launch failed (hipError %d)", e);
+  return DSV_OK;
+}
+
+int dsv_adaptive_k(const dsv_problem* p, const void* q_lr, const void* k_lr, float logit_scale,
+                   double mass, int32_t* k_group, int32_t* k_head, void* stream) {
+  std::vector<int32_t> ones(p && p->heads > 0 ? p->heads : 1, 1);
+  Geom geo;
+  int st = validate_problem(p, ones.data(), &geo);
+  if (st != DSV_OK) return st;
+  if ((st = check_ptr(q_lr, "q_lr", 16)) || (st = check_ptr(k_lr, "k_lr", 16)) ||
+      (st = check_ptr(k_head, "k_head", 4)))
+    return st;
+  if (k_group && reinterpret_cast<uintptr_t>(k_group) % 4)
+    return fail(DSV_ERR_ALIGN, "k_group is not 4-byte aligned");
+  if (!(logit_scale > 0.0f) || !isfinite(logit_scale))
+    return fail(DSV_ERR_SHAPE, "logit_scale must be positive and finite");
+  if (!(mass > 0.0 && mass <= 1.0)) return fail(DSV_ERR_SHAPE, "mass must be in (0, 1]");
+  AdaptiveParams ap;
+  for (int b = 0; b < AK_BINS - 1; ++b) ap.w[b] = exp(-((double)b + 0.5) / AK_BINS_PER_NAT);
+  ap.w[AK_BINS - 1] = exp(-(double)(AK_BINS - 1) / AK_BINS_PER_NAT);
+  ap.mass = mass;
+  ap.tau_r = logit_scale * (float)AK_BINS_PER_NAT;
+  const int e = launch_adaptive_k(geo, q_lr, k_lr, ap, k_group, k_head, stream);
+  if (e) return fail(DSV_ERR_HIP, "adaptive-k launch failed (hipError %d)", e);
   return DSV_OK;
 }
 

@@ -35,8 +35,19 @@ struct Geom {
 int validate_problem(const dsv_problem* p, const int32_t* k_per_head, Geom* geo);
 void set_error(const char* fmt, ...);
 
+// Adaptive k: bins of the estimated logit below a group's maximum, and their softmax weights.
+constexpr int AK_BINS = 128;
+constexpr int AK_BINS_PER_NAT = 4;
+struct AdaptiveParams {
+  double w[AK_BINS];   // weight of bin b: exp(-(b + 1/2) / 4), the last bin exp(-(AK_BINS-1)/4)
+  double mass;         // share of the mass the group's k keys must carry, in (0, 1]
+  float tau_r;         // logit_scale * AK_BINS_PER_NAT, rounded to fp32
+};
+
 // Kernel launchers (one per translation unit). Return 0 or a hipError_t value.
 int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int32_t* idx, void* stream);
+int launch_adaptive_k(const Geom& geo, const void* q_lr, const void* k_lr,
+                      const AdaptiveParams& ap, int32_t* k_group, int32_t* k_head, void* stream);
 int launch_attn_fwd(const Geom& geo, const void* q, const void* k, const void* v,
                     const int32_t* idx, float scale, void* o, float* lse, void* stream);
 // `events` (may be NULL): 4 hipEvent_t per head chunk, recorded around the chunk's stages.

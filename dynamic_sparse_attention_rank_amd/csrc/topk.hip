@@ -60,6 +60,145 @@ struct TopkCfg {
   __device__ static int off(int i, int h) { return F32 ? 2 * h * R + 16 * i : 32 * i + 16 * h; }
 };
 
+// Block index -> (b, h, group block). Blocks x, x + 8, x + 16, .. run on XCD x % 8; they get
+// consecutive logical indices, so that one (b, h)'s blocks share an XCD (and its L2) while they
+// stream the same K_lr. Heads go heaviest first.
+__device__ __forceinline__ void decode_block(const Geom& geo, int& b, int& h, int& gblock) {
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int logical = xcd * (nblk >> 3) + min(xcd, nblk & 7) + (blockIdx.x >> 3);
+  const int gblocks = (geo.NG + TK_GROUPS - 1) / TK_GROUPS;
+  const int slot = logical / gblocks;
+  gblock = logical - slot * gblocks;
+  b = slot / geo.H;
+  h = geo.order[slot - b * geo.H];
+}
+
+// The score stream of one workgroup: group sums of its 32 groups as B operands, and a walk over
+// the key tiles that hands each lane the 16 scores of its group for its keys of every tile.
+// Element 4i + j of a lane's scores is key TK_TILE t + 32 kw + 8i + 4 hh + j (lane = 32 hh + g).
+template <bool F32, int R>
+struct ScoreStream {
+  using C = TopkCfg<F32, R>;
+  const unsigned char* klr;
+  int S, kw, g, hh;
+  float ssum[C::NF];
+  u32x4 b_hi[F32 ? 1 : C::NB], b_lo[F32 ? 1 : C::NB];
+
+  // Sums the group members' Q_lr rows: waves 0 .. TK_SUMW-1 sum every TK_SUMW-th member of the
+  // lane's group into the LDS partials `part`; every wave then adds the partials in the same
+  // order (deterministic). Contains two workgroup barriers: every thread calls it.
+  __device__ __forceinline__ void init(const Geom& geo, const void* qlr_, const void* klr_, int bh,
+                                       int my_group, float* part) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    kw = tid >> 6;
+    g = lane & 31;
+    hh = lane >> 5;
+    S = geo.S;
+    const long long head_base = (long long)bh * S * R;   // element offset of (b,h)
+    klr = static_cast<const unsigned char*>(klr_) + head_base * C::ES;
+    const unsigned char* qlr = static_cast<const unsigned char*>(qlr_) + head_base * C::ES;
+    if (kw < TK_SUMW) {
+      float ps[C::NF];
+#pragma unroll
+      for (int f = 0; f < C::NF; ++f) ps[f] = 0.0f;
+      if (my_group < geo.NG) {
+        const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
+        for (int j = kw; j < geo.G; j += TK_SUMW) {
+          const unsigned char* row = qlr + (long long)gg.token(my_group, j) * C::RB;
+#pragma unroll
+          for (int i = 0; i < C::NB; ++i) {
+            const u32x4 v = ld16(row + C::off(i, hh));
+            if constexpr (F32) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ps[4 * i + e] += __uint_as_float(v[e]);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                ps[8 * i + 2 * e] += bf16_lo(v[e]);
+                ps[8 * i + 2 * e + 1] += bf16_hi(v[e]);
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int f = 0; f < C::NF; ++f) part[(kw * C::NF + f) * 64 + lane] = ps[f];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < C::NF; ++f) {
+      ssum[f] = part[f * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < TK_SUMW; ++w) ssum[f] += part[(w * C::NF + f) * 64 + lane];
+    }
+    // bf16 B operands: s = hi + lo with hi = bf16(s), lo = bf16(s - hi); exact while |s| < 2^16
+    // for integer sums, and products with bf16 K_lr entries are exact in the fp32 accumulator.
+    if constexpr (!F32) {
+#pragma unroll
+      for (int i = 0; i < C::NB; ++i) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float s0 = ssum[8 * i + 2 * e], s1 = ssum[8 * i + 2 * e + 1];
+          const float h0 = bf16_round(s0), h1 = bf16_round(s1);
+          b_hi[i][e] = pack_bf16(h0, h1);
+          b_lo[i][e] = pack_bf16(s0 - h0, s1 - h1);
+        }
+      }
+    }
+    __syncthreads();   // partials read: the caller may reuse their LDS
+  }
+
+  // A operands: key row TK_TILE t + 32 kw + g of tile t (clamped to the last key; the scores
+  // of keys past the end are never used)
+  __device__ __forceinline__ void load_a(int t, u32x4* a) const {
+    const int m = min(t * TK_TILE + 32 * kw + g, S - 1);
+    const unsigned char* krow = klr + (long long)m * C::RB;
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) a[i] = ld16(krow + C::off(i, hh));
+  }
+  // scores of the tile's 32 keys (rows) for the 32 groups (columns)
+  __device__ __forceinline__ floatx16 scores(const u32x4* a) const {
+    floatx16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) {
+      if constexpr (F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = mfma32_f32(__uint_as_float(a[i][e]), ssum[4 * i + e], acc);
+      } else {
+        acc = mfma32_bf16(a[i], b_hi[i], acc);
+        acc = mfma32_bf16(a[i], b_lo[i], acc);
+      }
+    }
+    return acc;
+  }
+  // Walks the key tiles in order, calling body(scores, t, Flag<partial>): operands are loaded
+  // two tiles ahead and scored one tile ahead, so neither the loads nor the MFMAs wait in line.
+  template <class Body>
+  __device__ __forceinline__ void walk(Body&& body) const {
+    const int nfull = S / TK_TILE;   // tiles without keys past the end
+    u32x4 a0[C::NB], a1[C::NB];
+    load_a(0, a0);
+    load_a(1, a1);
+    floatx16 acc = scores(a0);
+    for (int t = 0; t < nfull; t += 2) {
+      load_a(t + 2, a0);
+      floatx16 nxt = scores(a1);
+      body(acc, t, Flag<false>{});
+      acc = nxt;
+      if (t + 1 >= nfull) break;
+      load_a(t + 3, a1);
+      nxt = scores(a0);
+      body(acc, t + 1, Flag<false>{});
+      acc = nxt;
+    }
+    if (nfull * TK_TILE < S) body(acc, nfull, Flag<true>{});   // acc holds tile nfull
+  }
+};
+
 template <bool F32, int R>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict__ qlr_,
                                                           const void* __restrict__ klr_,
@@ -85,22 +224,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
   const int g = lane & 31;       // group of the workgroup
   const int hh = lane >> 5;      // contraction slot / key half
 
-  // block -> (b, h, group block): blocks x, x + 8, x + 16, .. run on XCD x % 8, and they get
-  // consecutive logical indices, so that one (b, h)'s blocks share an XCD
-  const int nblk = gridDim.x;
-  const int xcd = blockIdx.x & 7;
-  const int logical = xcd * (nblk >> 3) + min(xcd, nblk & 7) + (blockIdx.x >> 3);
-  const int gblocks = (geo.NG + TK_GROUPS - 1) / TK_GROUPS;
-  const int slot = logical / gblocks;
-  const int gblock = logical - slot * gblocks;
-  const int b = slot / geo.H;
-  const int h = geo.order[slot - b * geo.H];
+  int b, h, gblock;
+  decode_block(geo, b, h, gblock);
   const int bh = b * geo.H + h;
   const int S = geo.S;
   const int kh = geo.k[h];
-  const long long head_base = (long long)bh * S * R;   // element offset of (b,h) in Q_lr/K_lr
-  const unsigned char* klr = static_cast<const unsigned char*>(klr_) + head_base * C::ES;
-  const unsigned char* qlr = static_cast<const unsigned char*>(qlr_) + head_base * C::ES;
   const int my_group = gblock * TK_GROUPS + g;
 
   if (kh == S) {   // dense head: every key, in order, without scoring
@@ -111,60 +239,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
     return;
   }
 
-  // ---- group sums: waves 0 .. TK_SUMW-1 sum every TK_SUMW-th member row of the lane's group
-  // into LDS partials; every wave then adds the partials in the same order (deterministic)
-  float* part = reinterpret_cast<float*>(hist);
-  if (kw < TK_SUMW) {
-    float ps[C::NF];
-#pragma unroll
-    for (int f = 0; f < C::NF; ++f) ps[f] = 0.0f;
-    if (my_group < geo.NG) {
-      const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
-      for (int j = kw; j < geo.G; j += TK_SUMW) {
-        const unsigned char* row = qlr + (long long)gg.token(my_group, j) * C::RB;
-#pragma unroll
-        for (int i = 0; i < C::NB; ++i) {
-          const u32x4 v = ld16(row + C::off(i, hh));
-          if constexpr (F32) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ps[4 * i + e] += __uint_as_float(v[e]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              ps[8 * i + 2 * e] += bf16_lo(v[e]);
-              ps[8 * i + 2 * e + 1] += bf16_hi(v[e]);
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int f = 0; f < C::NF; ++f) part[(kw * C::NF + f) * 64 + lane] = ps[f];
-  }
-  __syncthreads();
-  float ssum[C::NF];
-#pragma unroll
-  for (int f = 0; f < C::NF; ++f) {
-    ssum[f] = part[f * 64 + lane];
-#pragma unroll
-    for (int w = 1; w < TK_SUMW; ++w) ssum[f] += part[(w * C::NF + f) * 64 + lane];
-  }
-  // bf16 B operands: s = hi + lo with hi = bf16(s), lo = bf16(s - hi); exact while |s| < 2^16
-  // for integer sums, and products with bf16 K_lr entries are exact in the fp32 accumulator.
-  u32x4 b_hi[F32 ? 1 : C::NB], b_lo[F32 ? 1 : C::NB];
-  if constexpr (!F32) {
-#pragma unroll
-    for (int i = 0; i < C::NB; ++i) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float s0 = ssum[8 * i + 2 * e], s1 = ssum[8 * i + 2 * e + 1];
-        const float h0 = bf16_round(s0), h1 = bf16_round(s1);
-        b_hi[i][e] = pack_bf16(h0, h1);
-        b_lo[i][e] = pack_bf16(s0 - h0, s1 - h1);
-      }
-    }
-  }
-  __syncthreads();   // partials read: the histograms take their place
+  ScoreStream<F32, R> ss;
+  ss.init(geo, qlr_, klr_, bh, my_group, reinterpret_cast<float*>(hist));
 
   for (int i = tid; i < TK_GROUPS; i += TK_THREADS) {
     st_prefix[i] = 0;
@@ -174,57 +250,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
   }
   for (int i = tid; i < TK_GROUPS * TK_HSTRIDE; i += TK_THREADS) hist[i] = 0;
 
-  // ---- A operands: key row TK_TILE t + 32 kw + lane % 32 of tile t (clamped to the last key;
-  // the scores of keys past the end are never counted)
-  auto load_a = [&](int t, u32x4* a) {
-    const int m = min(t * TK_TILE + 32 * kw + g, S - 1);
-    const unsigned char* krow = klr + (long long)m * C::RB;
-#pragma unroll
-    for (int i = 0; i < C::NB; ++i) a[i] = ld16(krow + C::off(i, hh));
-  };
-  // scores of the tile's 32 keys (rows) for the 32 groups (columns)
-  auto scores = [&](const u32x4* a) -> floatx16 {
-    floatx16 acc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < C::NB; ++i) {
-      if constexpr (F32) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc = mfma32_f32(__uint_as_float(a[i][e]), ssum[4 * i + e], acc);
-      } else {
-        acc = mfma32_bf16(a[i], b_hi[i], acc);
-        acc = mfma32_bf16(a[i], b_lo[i], acc);
-      }
-    }
-    return acc;
-  };
-  const int nfull = S / TK_TILE;   // tiles without keys past the end
-  // Walks the key tiles in order, calling body(scores, t, Flag<partial>): operands are loaded
-  // two tiles ahead and scored one tile ahead, so neither the loads nor the MFMAs wait in line.
-  auto walk = [&](auto&& body) {
-    u32x4 a0[C::NB], a1[C::NB];
-    load_a(0, a0);
-    load_a(1, a1);
-    floatx16 acc = scores(a0);
-    for (int t = 0; t < nfull; t += 2) {
-      load_a(t + 2, a0);
-      floatx16 nxt = scores(a1);
-      body(acc, t, Flag<false>{});
-      acc = nxt;
-      if (t + 1 >= nfull) break;
-      load_a(t + 3, a1);
-      nxt = scores(a0);
-      body(acc, t + 1, Flag<false>{});
-      acc = nxt;
-    }
-    if (nfull * TK_TILE < S) body(acc, nfull, Flag<true>{});   // acc holds tile nfull
-  };
-
   __syncthreads();
 
-  // ---- radix passes (pass 4 = compaction). Element 4i + j of a lane's scores is key
-  // TK_TILE t + 32 kw + 8i + 4 hh + j.
+  // ---- radix passes (pass 4 = compaction)
   for (int pass = 0; pass <= 4; ++pass) {
     if (pass < 4) {
       if (tid == 0) {
@@ -262,10 +290,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
         }
       };
       if (p0) {   // every key of an active group counts; its low bits are not tracked
-        walk([&](const floatx16& acc, int t, auto tail) { count(acc, t, tail, Flag<true>{}); });
+        ss.walk([&](const floatx16& acc, int t, auto tail) { count(acc, t, tail, Flag<true>{}); });
         lowor = 1u;
       } else {
-        walk([&](const floatx16& acc, int t, auto tail) { count(acc, t, tail, Flag<false>{}); });
+        ss.walk([&](const floatx16& acc, int t, auto tail) { count(acc, t, tail, Flag<false>{}); });
       }
       if ((lowor & ((1u << dshift) - 1u)) != 0) st_lowbits[g] = 1u;   // any lane: not zero
     } else {
@@ -276,7 +304,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
       int left = gs >= 16 ? st_krem[g] : 0;                    // equal keys still to take
       int cnt = 0;
       int32_t* const orow = idx + geo.row_offset(b, h, gs >= 0 ? my_group : 0);
-      walk([&](const floatx16& acc, int t, auto tail_tag) {
+      ss.walk([&](const floatx16& acc, int t, auto tail_tag) {
         constexpr bool kTail = decltype(tail_tag)::value;
         const int mb = t * TK_TILE + 32 * kw + 4 * hh;
         uint32_t gtm = 0, eqm = 0;   // bit e: element e above / equal
@@ -372,6 +400,110 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
   }
 }
 
+// ---- adaptive k (the "critical KV pairs carry a given share of the attention mass" rule)
+//
+// Per group: the group scores' maximum M, then a histogram of its keys over AK_BINS bins of the
+// estimated logit below the maximum, bin = floor((M - sigma) * tau_r) (fp32, clamped to the last
+// bin), where tau_r = logit_scale * bins per nat. One lane per group then accumulates, in bin
+// order and in fp64, the softmax weights count[b] * w[b] (w from the host) and finds the first
+// bin at which the running mass reaches `mass` times the total; k is the keys of the earlier
+// bins plus the number of that bin's keys (at weight w[b]) still needed, at least 1.
+template <bool F32, int R>
+__global__ __launch_bounds__(TK_THREADS) void adaptive_k_kernel(const void* __restrict__ qlr_,
+                                                                const void* __restrict__ klr_,
+                                                                AdaptiveParams ap,
+                                                                int32_t* __restrict__ k_group,
+                                                                int32_t* __restrict__ k_head,
+                                                                Geom geo) {
+  using C = TopkCfg<F32, R>;
+  static_assert(TK_SUMW * 64 * C::NF <= TK_GROUPS * TK_HSTRIDE, "partial sums overflow");
+  static_assert(AK_BINS + 1 <= TK_HSTRIDE, "bins overflow");
+  __shared__ uint32_t hist[TK_GROUPS * TK_HSTRIDE];   // also the group sums' partials, first
+  __shared__ uint32_t st_max[TK_GROUPS];               // order-preserving image of the maximum
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = lane & 31;
+  int b, h, gblock;
+  decode_block(geo, b, h, gblock);
+  const int my_group = gblock * TK_GROUPS + g;
+  const int S = geo.S;
+
+  ScoreStream<F32, R> ss;
+  ss.init(geo, qlr_, klr_, b * geo.H + h, my_group, reinterpret_cast<float*>(hist));
+  for (int i = tid; i < TK_GROUPS * TK_HSTRIDE; i += TK_THREADS) hist[i] = 0;
+  for (int i = tid; i < TK_GROUPS; i += TK_THREADS) st_max[i] = 0;
+  __syncthreads();
+
+  // ---- the maximum of every group's scores
+  float mx = -INFINITY;
+  ss.walk([&](const floatx16& acc, int t, auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;
+    const int mb = t * TK_TILE + 32 * ss.kw + 4 * ss.hh;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if constexpr (kTail) {
+        if (mb + 8 * (e >> 2) + (e & 3) < S) mx = fmaxf(mx, acc[e]);
+      } else {
+        mx = fmaxf(mx, acc[e]);
+      }
+    }
+  });
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  __hip_atomic_fetch_max(&st_max[g], score_key(mx), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
+  __syncthreads();
+  const uint32_t mk = st_max[g];
+  const float M = __uint_as_float(mk ^ ((mk & 0x80000000u) ? 0x80000000u : 0xffffffffu));
+
+  // ---- histogram of the logit gap below the maximum
+  uint32_t* const hrow = &hist[g * TK_HSTRIDE];
+  const float tau_r = ap.tau_r;
+  ss.walk([&](const floatx16& acc, int t, auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;
+    const int mb = t * TK_TILE + 32 * ss.kw + 4 * ss.hh;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float x = __fmul_rn(__fsub_rn(M, acc[e]), tau_r);
+      const uint32_t bin = x < (float)(AK_BINS - 1) ? (uint32_t)x : (uint32_t)(AK_BINS - 1);
+      bool take = true;
+      if constexpr (kTail) take = mb + 8 * (e >> 2) + (e & 3) < S;
+      if (take)
+        __hip_atomic_fetch_add(&hrow[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  });
+  __syncthreads();
+
+  // ---- one lane per group: softmax-weighted cumulative mass in bin order (fp64, no fusion)
+  if (tid < TK_GROUPS && my_group < geo.NG) {
+    double z = 0.0;
+    for (int bb = 0; bb < AK_BINS; ++bb) z = __dadd_rn(z, __dmul_rn((double)hrow[bb], ap.w[bb]));
+    const double target = __dmul_rn(ap.mass, z);
+    double cum = 0.0;
+    long long n = 0;
+    long long k = S;
+    for (int bb = 0; bb < AK_BINS; ++bb) {
+      const double c = __dmul_rn((double)hrow[bb], ap.w[bb]);
+      const double nxt = __dadd_rn(cum, c);
+      if (hrow[bb] != 0u && nxt >= target) {
+        const double need = ceil(__ddiv_rn(__dsub_rn(target, cum), ap.w[bb]));
+        k = n + (long long)fmin(need, (double)hrow[bb]);
+        break;
+      }
+      cum = nxt;
+      n += hrow[bb];
+    }
+    const int kg = (int)max(k, 1LL);
+    if (k_group) k_group[((long long)b * geo.H + h) * geo.NG + my_group] = kg;
+    atomicMax(&k_head[h], kg);
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
 }  // namespace
 
 int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int32_t* idx, void* stream) {
@@ -394,6 +526,36 @@ int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int32_t* id
   DSV_TOPK_CASE(true, 48)
   DSV_TOPK_CASE(true, 64)
 #undef DSV_TOPK_CASE
+  return (int)hipErrorInvalidValue;
+}
+
+}  // namespace dsv
+
+namespace dsv {
+
+int launch_adaptive_k(const Geom& geo, const void* q_lr, const void* k_lr,
+                      const AdaptiveParams& ap, int32_t* k_group, int32_t* k_head, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((geo.H + 255) / 256), dim3(256), 0, st, k_head, geo.H,
+                     0);
+  const int gblocks = (geo.NG + TK_GROUPS - 1) / TK_GROUPS;
+  const dim3 grid(geo.B * geo.H * gblocks);
+  const bool f32 = geo.dtype == DSV_FP32;
+#define DSV_AK_CASE(F, RR)                                                                     \
+  if (f32 == F && geo.r == RR) {                                                               \
+    hipLaunchKernelGGL((adaptive_k_kernel<F, RR>), grid, dim3(TK_THREADS), 0, st, q_lr, k_lr, \
+                       ap, k_group, k_head, geo);                                              \
+    return (int)hipGetLastError();                                                             \
+  }
+  DSV_AK_CASE(false, 16)
+  DSV_AK_CASE(false, 32)
+  DSV_AK_CASE(false, 48)
+  DSV_AK_CASE(false, 64)
+  DSV_AK_CASE(true, 16)
+  DSV_AK_CASE(true, 32)
+  DSV_AK_CASE(true, 48)
+  DSV_AK_CASE(true, 64)
+#undef DSV_AK_CASE
   return (int)hipErrorInvalidValue;
 }
 

@@ -111,6 +111,28 @@ int dsv_lowrank_topk(const dsv_problem* p, const void* q_lr, const void* k_lr,
                      const int32_t* k_per_head, int reduce, int32_t* idx, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* Adaptive k: the number of keys per group that carry a given share of the group's estimated
+ * attention mass. (DSV summaries: zh §2.1 stage two, "critical KV estimation": the low-rank
+ * estimate of QK^T identifies the KV pairs that contribute more than 90% of the attention
+ * score; pt §2A, fr §2A, ko §2가.)
+ *   q_lr, k_lr  : as for dsv_lowrank_topk (group scores sigma[g][m], SUM reduction).
+ *   logit_scale : > 0; the estimated logit of key m for group g is logit_scale * sigma[g][m]
+ *                 (scale / G makes it the mean of the members' scaled low-rank logits).
+ *   mass        : in (0, 1], e.g. 0.9.
+ *   k_group     : device int32 [B][H][NG] or NULL, written: k of every group.
+ *   k_head      : device int32 [H], written: the largest k of the head's groups over the batch,
+ *                 i.e. a k_per_head for which every group's keys carry at least `mass`.
+ * Per group, from a histogram rather than a sort: with M the largest group score, key m falls
+ * in bin b = min(floor(fp32((M - sigma[m]) * fp32(4 * logit_scale))), 127), i.e. bins of a
+ * quarter of a logit unit below the maximum (the last bin holds the rest). Bin b carries the
+ * softmax weight w_b = exp(-(b + 1/2)/4) per key (the last bin exp(-127/4)). In fp64 and in
+ * bin order: Z = sum_b count_b w_b; the first non-empty bin b* at which the running sum reaches
+ * mass * Z gives k = (keys in bins < b*) + min(count_b*, ceil((mass * Z - running sum before
+ * b*) / w_b*)), at least 1. Counts are exact and the fp64 sums run in a fixed order, so the
+ * result is reproducible bit for bit. Launches on `stream`; no workspace. */
+int dsv_adaptive_k(const dsv_problem* p, const void* q_lr, const void* k_lr, float logit_scale,
+                   double mass, int32_t* k_group, int32_t* k_head, void* stream);
+
 /* Query-grouped sparse attention, forward.
  * (DSV summaries: zh §2.1 "sparse computation" bullet and §2.2 "Query Grouping".)
  *   q,k,v : [B][H][S][d] device, dtype p->dtype.   idx, k_per_head: as above.

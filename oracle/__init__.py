@@ -16,6 +16,8 @@ gist.science/{zh,pt,fr,ko}/paper/2502.07590):
   * attention - exact softmax attention restricted to each group's selected keys (zh §2.1
                 "sparse computation": full attention on the critical KV pairs only), forward
                 and backward, in a dense masked form and in a gathered form.
+  * adaptive  - per-group k from the share of the estimated attention mass its keys carry
+                (zh §2.1 "critical KV estimation": more than 90 % of the attention score).
   * planning  - head placement over devices by a longest-processing-time greedy and its
                 imbalance ratio (zh §2.3, db-SP summary), and the dense-versus-sparse choice
                 per head (zh §2.1 "OP Dispatcher").
@@ -24,4 +26,4 @@ rows, scale = 1/sqrt(d), natural-log LSE, no gradient through the selection) are
 each function. Every function here is pinned by the CPU tests (see tests/test_oracle_*.py);
 the SUM reduction itself is pinned only to this definition, not to the paper's kernel.
 """
-from . import geometry, topk, attention, planning  # noqa: F401
+from . import geometry, topk, attention, planning, adaptive  # noqa: F401
