@@ -338,6 +338,30 @@ def main():
     }
     log(f"timed: {ms_step:.3f} ms/step (top-k {mean(t_topk):.3f}, fwd {mean(t_fwd):.3f}, "
         f"bwd {mean(t_bwd):.3f} ms)")
+    # outside the step (its k is fixed by the workload): the adaptive-k estimator on the same
+    # inputs, and the head placement / dispatch the cost model gives for this workload
+    kg = torch.empty((cfg.batch, cfg.heads, p.n_groups), dtype=torch.int32, device=dev)
+    for _ in range(2):
+        dsv.adaptive_k(p, x["q_lr"], x["k_lr"], mass=0.9, k_group=kg, stream=stream)
+    ak_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ak_ev[0].record(stream)
+    for _ in range(5):
+        kh_t, _ = dsv.adaptive_k(p, x["q_lr"], x["k_lr"], mass=0.9, k_group=kg, stream=stream)
+    ak_ev[1].record(stream)
+    torch.cuda.synchronize()
+    ak_ms = ak_ev[0].elapsed_time(ak_ev[1]) / 5
+    cm = dsv.default_cost_model(p, with_backward=True)
+    part, load, rho = dsv.plan_heads(ks, 8, cfg.seq * p.n_groups * cm.topk_ns_per_score * 1e-6,
+                                     p.n_groups * cm.attn_ns_per_edge * 1e-6)
+    kd_out, n_dense = dsv.dispatch_k(p, ks, cm)
+    extras = {"adaptive_k": {"ms": ak_ms, "mass": 0.9,
+                             "scores_per_s": scores / (ak_ms * 1e-3),
+                             "k_head_min_max": [int(kh_t.min()), int(kh_t.max())]},
+              "head_plan_8": {"rho_s": rho, "max_load_ms": max(load)},
+              "dispatch": {"dense_heads": n_dense,
+                           "break_even_k_over_S": 1 - cm.topk_ns_per_score / cm.attn_ns_per_edge}}
+    log(f"adaptive k: {ak_ms:.3f} ms")
+    out["extras"] = extras
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)

@@ -133,3 +133,27 @@ def test_training_steps():
         say(f"   step {step} ok")
         del x, idx, o, lse, dq, dk, dv
         torch.cuda.empty_cache()
+
+
+def test_mid_adaptive_k_sampled_groups():
+    """Adaptive k at S=65536: sampled groups of three heads bit-exact against the oracle; the
+    head k is the largest group k."""
+    import math
+    from oracle import adaptive as oad
+    cfg = workload("mid")
+    say("[full] mid: adaptive k, mass 0.9")
+    x = gpu_inputs(cfg, backward=False)
+    p = dsv.problem_for(cfg)
+    kh, kg = dsv.adaptive_k(p, x["q_lr"], x["k_lr"], mass=0.9)
+    torch.cuda.synchronize()
+    kg = kg.cpu().numpy()
+    assert np.array_equal(kh.cpu().numpy(), kg.max(axis=(0, 2)))
+    ls32 = float(np.float32(1.0 / (math.sqrt(cfg.head_dim) * p.group_size)))
+    mem = members(cfg)
+    w = oad.bin_weights()
+    for h in (0, 7, 23):
+        for g in _sampled_groups(cfg.n_groups, 4, 200 + h):
+            sig = otopk.group_scores_sum_first(f64(x["q_lr"][0, h]), f64(x["k_lr"][0, h]),
+                                               mem[g:g + 1])[0]
+            ref = oad.k_from_counts(oad.group_bin_counts(sig, ls32), 0.9, w)
+            assert kg[0, h, g] == ref, (h, g, kg[0, h, g], ref)
