@@ -111,13 +111,18 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
   const char* Kb = reinterpret_cast<const char*>(K);
   const char* Vb = reinterpret_cast<const char*>(V);
   auto fetch_rows = [&](const int kraw) {
+    // all the lane's keys first (the ds_bpermute round trips overlap), then the row loads
+    uint32_t off[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int p = RPI * i + la;
       const uint32_t key = min((uint32_t)__shfl(kraw, NI * la + i, 64), (uint32_t)geo.S - 1u);
-      const uint32_t off = key * (uint32_t)(2 * D) + (uint32_t)((lp ^ (p % GPR)) << 4);
-      global_load_lds16(Kb + off, &kvs[0][RPI * i * D]);
-      global_load_lds16(Vb + off, &kvs[1][RPI * i * D]);
+      off[i] = key * (uint32_t)(2 * D) + (uint32_t)((lp ^ (p % GPR)) << 4);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      global_load_lds16(Kb + off[i], &kvs[0][RPI * i * D]);
+      global_load_lds16(Vb + off[i], &kvs[1][RPI * i * D]);
     }
   };
   fetch_rows(load_keys(0));
