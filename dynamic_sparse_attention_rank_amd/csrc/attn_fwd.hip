@@ -103,26 +103,26 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
   constexpr int NI = 32 / RPI;   // loads per array and chunk
   const int la = lane / GPR;
   const int lp = lane % GPR;
-  // key indices: lane l reads chunk position l % 32 (one load per chunk; positions past the
-  // row end read its last key) and the NI keys a lane's row loads need are picked from those
-  // lanes by ds_bpermute when the rows are requested
-  int kq;   // index-row entry (cb + lane % 32) of the next chunk to fetch
-  auto load_keys = [&](int cb) { return row[min(cb + (lane & 31), kh - 1)]; };
+  // key indices: the NI keys of a lane's row loads (chunk positions NI la + i, adjacent in the
+  // index row; positions past the row end read its last key) are loaded a chunk ahead
+  struct Keys { uint32_t k[NI]; };
+  auto load_keys = [&](int cb) {
+    Keys r;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) r.k[i] = (uint32_t)row[min(cb + NI * la + i, kh - 1)];
+    return r;
+  };
+  Keys kq;   // keys of the next chunk to fetch
   const char* Kb = reinterpret_cast<const char*>(K);
   const char* Vb = reinterpret_cast<const char*>(V);
-  auto fetch_rows = [&](const int kraw) {
-    // all the lane's keys first (the ds_bpermute round trips overlap), then the row loads
-    uint32_t off[NI];
+  auto fetch_rows = [&](const Keys& kr) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int p = RPI * i + la;
-      const uint32_t key = min((uint32_t)__shfl(kraw, NI * la + i, 64), (uint32_t)geo.S - 1u);
-      off[i] = key * (uint32_t)(2 * D) + (uint32_t)((lp ^ (p % GPR)) << 4);
-    }
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      global_load_lds16(Kb + off[i], &kvs[0][RPI * i * D]);
-      global_load_lds16(Vb + off[i], &kvs[1][RPI * i * D]);
+      const uint32_t off = min(kr.k[i], (uint32_t)geo.S - 1u) * (uint32_t)(2 * D) +
+                           (uint32_t)((lp ^ (p % GPR)) << 4);
+      global_load_lds16(Kb + off, &kvs[0][RPI * i * D]);
+      global_load_lds16(Vb + off, &kvs[1][RPI * i * D]);
     }
   };
   fetch_rows(load_keys(0));
@@ -141,8 +141,8 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
   const float raise_s = kRaise / c2;
   auto chunk = [&](const int cb, auto tail_tag) {
     constexpr bool kTail = decltype(tail_tag)::value;
-    // this chunk's rows have landed once only the key load issued after them remains
-    wait_vmcnt<1>();
+    // this chunk's rows have landed once only the key loads issued after them remain
+    wait_vmcnt<NI>();
     // ---- operands: K rows 16kb + li (A of S^T = K Q^T, features 32ks + 8lg ..) and V^T
     // (row li <-> feature 16fb + li, slot (lg, e) <-> LDS row 4lg + e (e < 4) or
     // 16 + 4lg + e - 4 (e >= 4)) by transposed reads
