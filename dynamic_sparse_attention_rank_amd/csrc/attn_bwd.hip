@@ -128,22 +128,46 @@ __global__ __launch_bounds__(256) void row_bucket_starts(const int32_t* __restri
   for (int j = jl + 1 + lane; j <= nB; j += 64) r[j] = (uint32_t)kh;
 }
 
+// rs [slot][g][j] -> rsT [slot][j][g] through 64 x 64 LDS tiles, so that the per-bucket
+// passes below read a bucket's entry points of consecutive groups from consecutive words.
+__global__ __launch_bounds__(256) void transpose_rs(const uint32_t* __restrict__ rs,
+                                                    uint32_t* __restrict__ rsT, Geom geo) {
+  __shared__ uint32_t t[64][65];
+  const int nB1 = n_buckets(geo.S) + 1;
+  const int tj = (nB1 + 63) / 64, tg = (geo.NG + 63) / 64;
+  int bid = blockIdx.x;
+  const int sl = bid / (tj * tg);
+  bid -= sl * tj * tg;
+  const int j0 = (bid % tj) * 64, g0 = (bid / tj) * 64;
+  const uint32_t* src = rs + (long long)sl * geo.NG * nB1;
+  uint32_t* dst = rsT + (long long)sl * geo.NG * nB1;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int g = g0 + r, j = j0 + tx;
+    if (g < geo.NG && j < nB1) t[r][tx] = src[(long long)g * nB1 + j];
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int j = j0 + r, g = g0 + tx;
+    if (g < geo.NG && j < nB1) dst[(long long)j * geo.NG + g] = t[tx][r];
+  }
+}
+
 // Row-run length of bucket j in row g: the entry points lie in [0, k] whatever the row holds
 // (every j is written), but only an ascending row makes them non-decreasing; a decreasing pair
 // counts as an empty run so that a malformed row cannot produce a negative length.
 __device__ __forceinline__ uint32_t run_len(uint32_t a, uint32_t b) { return b > a ? b - a : 0u; }
 
 // tot[j] = staging rows whose key lies in bucket j (all groups of the slot). One wave per
-// (slot, bucket), lanes over groups.
-__global__ __launch_bounds__(64) void bucket_totals(const uint32_t* __restrict__ rs,
+// (slot, bucket), lanes over groups; entry points from the transposed table rsT.
+__global__ __launch_bounds__(64) void bucket_totals(const uint32_t* __restrict__ rsT,
                                                     uint32_t* __restrict__ tot, Geom geo) {
   const int nB = n_buckets(geo.S);
   const int sl = blockIdx.x / nB;
   const int j = blockIdx.x - sl * nB;
-  const uint32_t* r = rs + (long long)sl * geo.NG * (nB + 1);
+  const uint32_t* r = rsT + (long long)sl * geo.NG * (nB + 1) + (long long)j * geo.NG;
   uint32_t run = 0;
-  for (int g = threadIdx.x; g < geo.NG; g += 64)
-    run += run_len(r[(long long)g * (nB + 1) + j], r[(long long)g * (nB + 1) + j + 1]);
+  for (int g = threadIdx.x; g < geo.NG; g += 64) run += run_len(r[g], r[geo.NG + g]);
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) run += __shfl_xor(run, m, 64);
   if (threadIdx.x == 0) tot[(long long)sl * (nB + 1) + j] = run;
@@ -180,7 +204,7 @@ __global__ __launch_bounds__(256) void bucket_offsets(const uint32_t* __restrict
 // lies in bucket j, ordered by group, then by position, each as (slot-relative staging row
 // g*padded_k + p) << 5 | (key - 32 j). One wave per (slot, bucket); 64 groups per step,
 // positions from a wave scan; the keys of a step's runs are read 8 per lane at a time.
-__global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ rs,
+__global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ rsT,
                                                   const uint32_t* __restrict__ off,
                                                   const int32_t* __restrict__ idx, Chunk ch,
                                                   uint32_t* __restrict__ perm, Geom geo) {
@@ -193,7 +217,7 @@ __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ r
   const uint32_t kh = (uint32_t)geo.k[h];
   const uint32_t kp = (uint32_t)padded_k(geo.k[h]);
   const uint32_t slot_rows = (uint32_t)(ch.edge_base[sl + 1] - ch.edge_base[sl]);
-  const uint32_t* r = rs + (long long)sl * geo.NG * (nB + 1);
+  const uint32_t* r = rsT + (long long)sl * geo.NG * (nB + 1) + (long long)j * geo.NG;
   const int32_t* keys = idx + geo.row_offset(b, h, 0);   // row of group g: keys + g*k
   uint32_t* pm = perm + ch.edge_base[sl];
   const int key0 = j * kBucket;
@@ -202,8 +226,8 @@ __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ r
     const int g = g0 + lane;
     uint32_t a = 0, len = 0;
     if (g < geo.NG) {
-      a = r[(long long)g * (nB + 1) + j];
-      len = run_len(a, r[(long long)g * (nB + 1) + j + 1]);
+      a = r[g];
+      len = run_len(a, r[geo.NG + g]);
     }
     uint32_t incl = len;   // inclusive prefix over lanes
 #pragma unroll
@@ -771,17 +795,19 @@ __global__ __launch_bounds__(64) void attn_bwd_f32(
 }  // namespace
 
 // Workspace layout for a chunk capacity of `cs` slots and `e` staging rows:
-//   [rs: cs*NG*(nB+1) u32][tot: cs*(nB+1) u32][off: cs*(nB+1) u32][perm: e u32]
-//   [steps: e/16 float2][dV rows: e*d fp16][dK rows: e*d fp16], every region 256-byte aligned.
+//   [rs: cs*NG*(nB+1) u32][rsT: cs*NG*(nB+1) u32][tot: cs*(nB+1) u32][off: cs*(nB+1) u32]
+//   [perm: e u32][steps: e/16 float2][dV rows: e*d fp16][dK rows: e*d fp16], every region
+//   256-byte aligned.
 struct WsLayout {
-  size_t rs, tot, off, perm, step, cv, ck, total;
+  size_t rs, rst, tot, off, perm, step, cv, ck, total;
 };
 static WsLayout ws_layout(const Geom& geo, long long cs, long long e) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t nb = (size_t)n_buckets(geo.S);
   WsLayout L;
   L.rs = 0;
-  L.tot = L.rs + al(cs * geo.NG * (nb + 1) * 4);
+  L.rst = L.rs + al(cs * geo.NG * (nb + 1) * 4);
+  L.tot = L.rst + al(cs * geo.NG * (nb + 1) * 4);
   L.off = L.tot + al(cs * (nb + 1) * 4);
   L.perm = L.off + al(cs * (nb + 1) * 4);
   L.step = L.perm + al((size_t)e * 4);
@@ -883,6 +909,7 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
   const WsLayout L = ws_layout(geo, cs, ecap);
   char* wsb = static_cast<char*>(ws);
   uint32_t* rs = reinterpret_cast<uint32_t*>(wsb + L.rs);
+  uint32_t* rsT = reinterpret_cast<uint32_t*>(wsb + L.rst);
   uint32_t* tot = reinterpret_cast<uint32_t*>(wsb + L.tot);
   uint32_t* off = reinterpret_cast<uint32_t*>(wsb + L.off);
   uint32_t* perm = reinterpret_cast<uint32_t*>(wsb + L.perm);
@@ -899,9 +926,11 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
     mark(4 * c);
     hipLaunchKernelGGL(row_bucket_starts, dim3((rows_waves + 3) / 4), dim3(256), 0, st, idx, ch,
                        rs, geo);
-    hipLaunchKernelGGL(bucket_totals, dim3(ch.n * nB), dim3(64), 0, st, rs, tot, geo);
+    const int ttiles = ch.n * ((nB + 64) / 64) * ((geo.NG + 63) / 64);
+    hipLaunchKernelGGL(transpose_rs, dim3(ttiles), dim3(256), 0, st, rs, rsT, geo);
+    hipLaunchKernelGGL(bucket_totals, dim3(ch.n * nB), dim3(64), 0, st, rsT, tot, geo);
     hipLaunchKernelGGL(bucket_offsets, dim3(ch.n), dim3(256), 0, st, tot, off, geo);
-    hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64), 0, st, rs, off, idx, ch, perm,
+    hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64), 0, st, rsT, off, idx, ch, perm,
                        geo);
     mark(4 * c + 1);
 #define DSV_BWD16(DD, QQ)                                                                       \

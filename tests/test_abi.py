@@ -104,15 +104,15 @@ def test_workspace_and_idx_layout_agree_with_oracle():
     ks = [5, 17, 3]
     for op in (dsv.DSV_OP_TOPK, dsv.DSV_OP_FWD):
         assert dsv.workspace_bytes(op, p, ks) == 0
-    # backward (bf16), for one (b, h) slot: per-row bucket entry points NG x (nB+1) u32,
-    # bucket totals and offsets (nB+1) u32 each, then per staging row of the heaviest slot
+    # backward (bf16), for one (b, h) slot: per-row bucket entry points NG x (nB+1) u32 and
+    # their transpose, bucket totals and offsets (nB+1) u32 each, then per staging row of the heaviest slot
     # (NG * max k rounded up to 32): a bucket-list entry (u32), a d-entry fp16 dV row and a
     # d-entry fp16 dK row, plus two fp32 scales per 16 rows
     al = lambda x: -(-x // 256) * 256
     nb = -(-p.seq // 32)
     NG = p.n_groups
     e = NG * (-(-max(ks) // 32) * 32)
-    need = (al(NG * (nb + 1) * 4) + 2 * al((nb + 1) * 4) + al(e * 4) + al(e // 16 * 8)
+    need = (2 * al(NG * (nb + 1) * 4) + 2 * al((nb + 1) * 4) + al(e * 4) + al(e // 16 * 8)
             + al(e * 64 * 2) + e * 64 * 2)
     assert dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks) == need
     pf = dsv.problem(2, 3, 4, 8, 8, 64, 16, (2, 2, 4), "fp32")
