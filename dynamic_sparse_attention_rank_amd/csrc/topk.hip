@@ -47,6 +47,23 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
+// Float bounds of a key interval, so that a score is tested against a digit prefix with one
+// compare instead of building its key. For finite s: s >= key_lower_bound(k) <=> key(s) >= k,
+// and s < key_upper_bound(k) <=> key(s) < k (k up to 2^32; NaN bounds compare false).
+__device__ __forceinline__ float key_float(uint32_t key) {   // the float whose key is `key`
+  return __uint_as_float(key ^ ((key & 0x80000000u) ? 0x80000000u : 0xffffffffu));
+}
+__device__ __forceinline__ float key_lower_bound(unsigned long long k) {
+  if (k <= 0x007fffffull) return -INFINITY;                 // at or below the key of -inf
+  if (k > 0xff800000ull) return __builtin_nanf("");         // above the key of +inf: none
+  return key_float((uint32_t)k);
+}
+__device__ __forceinline__ float key_upper_bound(unsigned long long k) {
+  if (k > 0xff800000ull) return INFINITY;                   // every finite score
+  if (k <= 0x007fffffull) return -INFINITY;                 // no finite score
+  return key_float((uint32_t)k);
+}
+
 // Contraction layout. bf16: k-step i covers features 16i .. 16i + 15, lane slot h = l / 32 holds
 // 16i + 8h .. 16i + 8h + 7 (one 16-byte load). fp32: slot h holds features h R/2 .. h R/2 + R/2 - 1,
 // one per v_mfma_f32_32x32x2f32 step (R/8 16-byte loads). A lane's own feature f (< R/2) is
@@ -267,22 +284,25 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
       // Histogram pass. The lane also ORs the bits below the digit over the keys it counts.
       const int dshift = 24 - 8 * pass;
       const int pshift = 32 - 8 * pass;
-      const uint32_t pfx = st_prefix[g];
+      const unsigned long long pfx = st_prefix[g];
       const bool act = st_npass[g] == pass;
       const bool p0 = pass == 0;
       uint32_t* const hrow = &hist[g * TK_HSTRIDE];
       uint32_t lowor = 0;
+      // after pass 0: the scores whose keys carry the prefix are those in [lo, hi)
+      const float lo = key_lower_bound(pfx << (pshift & 31));
+      const float hi = key_upper_bound((pfx + 1) << (pshift & 31));
       auto count = [&](const floatx16& acc, int t, auto tail_tag, auto first_tag) {
         constexpr bool kTail = decltype(tail_tag)::value;
         constexpr bool kFirst = decltype(first_tag)::value;
         const int mb = t * TK_TILE + 32 * kw + 4 * hh;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const uint32_t key = score_key(acc[e]);
           bool take = act;
           if constexpr (kTail) take = take && mb + 8 * (e >> 2) + (e & 3) < S;
-          if constexpr (!kFirst) take = take && (key >> (pshift & 31)) == pfx;
+          if constexpr (!kFirst) take = take && acc[e] >= lo && acc[e] < hi;
           if (take) {
+            const uint32_t key = score_key(acc[e]);
             __hip_atomic_fetch_add(&hrow[(key >> dshift) & 255u], 1u, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_WORKGROUP);
             if constexpr (!kFirst) lowor |= key;
@@ -299,8 +319,12 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
     } else {
       // Compaction. Both lanes of a group keep the same running state.
       const int gs = st_npass[g];
-      const uint32_t pfx = gs >= 16 ? st_prefix[g] : 0xffffffffu;
+      const unsigned long long pfx = gs >= 16 ? st_prefix[g] : 0xffffffffull;
       const int shift = gs >= 16 ? 32 - 8 * (gs - 16) : 0;   // no key exceeds all-ones
+      // keys above the threshold prefix: key >= khi; equal to it: klo <= key < khi
+      const float f_hi = key_lower_bound((pfx + 1) << shift);
+      const float f_hi_u = key_upper_bound((pfx + 1) << shift);
+      const float f_lo = key_lower_bound(pfx << shift);
       int left = gs >= 16 ? st_krem[g] : 0;                    // equal keys still to take
       int cnt = 0;
       int32_t* const orow = idx + geo.row_offset(b, h, gs >= 0 ? my_group : 0);
@@ -310,11 +334,10 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
         uint32_t gtm = 0, eqm = 0;   // bit e: element e above / equal
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const uint32_t v = score_key(acc[e]) >> (shift & 31);
           bool valid = true;
           if constexpr (kTail) valid = mb + 8 * (e >> 2) + (e & 3) < S;
-          gtm |= (uint32_t)(valid & (v > pfx)) << e;
-          eqm |= (uint32_t)(valid & (v == pfx)) << e;
+          gtm |= (uint32_t)(valid & (acc[e] >= f_hi)) << e;
+          eqm |= (uint32_t)(valid & (acc[e] >= f_lo) & (acc[e] < f_hi_u)) << e;
         }
         const uint32_t both = gtm | (eqm << 16);
         const uint32_t pboth = (uint32_t)__shfl_xor((int)both, 32, 64);
