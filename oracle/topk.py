@@ -7,8 +7,9 @@ DSV summaries (gist.science/{zh,pt,fr,ko}/paper/2502.07590):
     fused operation that never stores the S x S scores; adjacent queries form a group that
     shares one list of critical KV indices.
 Readings (the pages are silent): a group's score for key m is the SUM over its queries of the
-per-query low-rank scores; the row keeps the k keys with the largest group score, equal scores
-ranked by the lower key index; the row is written in ascending key order.
+per-query low-rank scores (the MAX over them is the other reading, `group_scores_max_*`); the
+row keeps the k keys with the largest group score, equal scores ranked by the lower key index;
+the row is written in ascending key order.
 
 Everything is float64 (exact for integer-valued factors below 2^53) or int64.
 """
@@ -43,6 +44,22 @@ def group_scores_sum_first(q_lr: np.ndarray, k_lr: np.ndarray, members: np.ndarr
     q = np.asarray(q_lr, dtype=np.float64)
     s = q[members].sum(axis=1)          # [NG, r]
     return s @ np.asarray(k_lr, dtype=np.float64).T
+
+
+def group_scores_max_bruteforce(q_lr: np.ndarray, k_lr: np.ndarray,
+                                members: np.ndarray) -> np.ndarray:
+    """MAX reduction: sigma[g, m] = max_{n in g} u[n, m], u the per-query scores ([NG, S]).
+
+    The other reading of how a group's members combine into one score (the pages only say
+    that a group shares its critical indices): the key counts for the group as much as for the
+    member that attends to it most. Computed group by group from the G x S per-query block."""
+    q = np.asarray(q_lr, dtype=np.float64)
+    kt = np.asarray(k_lr, dtype=np.float64).T
+    NG = members.shape[0]
+    sigma = np.empty((NG, kt.shape[1]), dtype=np.float64)
+    for g in range(NG):
+        sigma[g] = (q[members[g]] @ kt).max(axis=0)
+    return sigma
 
 
 def topk_rows_by_sort(sigma: np.ndarray, k: int) -> np.ndarray:
@@ -91,10 +108,12 @@ def idx_row_offsets(B: int, H: int, NG: int, k_per_head) -> np.ndarray:
 
 
 def lowrank_topk(q_lr: np.ndarray, k_lr: np.ndarray, k_per_head, members: np.ndarray,
-                 heads_subset=None) -> np.ndarray:
-    """Packed int32 idx for inputs [B, H, S, r]: brute-force group scores, then a full sort.
+                 heads_subset=None, reduce: str = "sum") -> np.ndarray:
+    """Packed int32 idx for inputs [B, H, S, r]: brute-force group scores (SUM or MAX over the
+    members), then a full sort.
 
     `heads_subset` (list of (b, h)) limits the work to those heads; other rows are left -1."""
+    scores = {"sum": group_scores_bruteforce, "max": group_scores_max_bruteforce}[reduce]
     B, H, S, _ = q_lr.shape
     NG = members.shape[0]
     k = [int(x) for x in k_per_head]
@@ -102,7 +121,7 @@ def lowrank_topk(q_lr: np.ndarray, k_lr: np.ndarray, k_per_head, members: np.nda
     out = np.full(B * NG * sum(k), -1, dtype=np.int64)
     todo = heads_subset if heads_subset is not None else [(b, h) for b in range(B) for h in range(H)]
     for b, h in todo:
-        sigma = group_scores_bruteforce(q_lr[b, h], k_lr[b, h], members)
+        sigma = scores(q_lr[b, h], k_lr[b, h], members)
         rows = topk_rows_by_sort(sigma, k[h])
         o = offs[b, h]
         out[o:o + NG * k[h]] = rows.reshape(-1)

@@ -172,3 +172,41 @@ def test_packed_layout_offsets_heterogeneous_k():
     for (s0, e0), (s1, _) in zip(spans, spans[1:]):
         assert e0 == s1
     assert spans[-1][1] == B * NG * sum(kph)
+
+
+# ---------------------------------------------------------------- MAX group reduction
+def test_max_scores_hand_worked():
+    # two members (1, 0) and (0, 2) against keys (3, 1), (-1, 1), (0, 0): per-member scores
+    # (3, -1, 0) and (2, 2, 0) -> max (3, 2, 0), sum (5, 1, 0)
+    q = np.array([[1.0, 0.0], [0.0, 2.0]])
+    k = np.array([[3.0, 1.0], [-1.0, 1.0], [0.0, 0.0]])
+    mem = np.array([[0, 1]])
+    assert np.array_equal(topk.group_scores_max_bruteforce(q, k, mem), [[3.0, 2.0, 0.0]])
+    assert np.array_equal(topk.group_scores_bruteforce(q, k, mem), [[5.0, 1.0, 0.0]])
+    # the two readings select differently at k = 1 ... and agree at k = 2
+    smax = topk.group_scores_max_bruteforce(q, k, mem)
+    assert topk.topk_rows_by_sort(smax, 1).tolist() == [[0]]
+    assert topk.topk_rows_by_sort(smax, 2).tolist() == [[0, 1]]
+
+
+def test_max_scores_against_python_loops_and_invariants():
+    rng = np.random.default_rng(7)
+    q = rng.integers(-7, 8, size=(32, 4)).astype(np.float64)
+    k = rng.integers(-7, 8, size=(24, 4)).astype(np.float64)
+    mem = geometry.group_members(2, 4, 4, 1, 2, 2)   # 8 groups of 4
+    smax = topk.group_scores_max_bruteforce(q, k, mem)
+    for g in range(mem.shape[0]):
+        for m in range(k.shape[0]):
+            ref = max(sum(q[n, c] * k[m, c] for c in range(4)) for n in mem[g])
+            assert smax[g, m] == ref
+    ssum = topk.group_scores_bruteforce(q, k, mem)
+    G = mem.shape[1]
+    assert np.all(smax * G >= ssum)                  # max >= mean
+    # members in any order give the same scores
+    perm = mem[:, ::-1].copy()
+    assert np.array_equal(topk.group_scores_max_bruteforce(q, k, perm), smax)
+    # groups of identical members: MAX is the per-query score, SUM is G times it
+    q2 = np.repeat(q[:8], 4, axis=0)
+    mem2 = np.arange(32).reshape(8, 4)
+    assert np.array_equal(topk.group_scores_max_bruteforce(q2, k, mem2) * 4,
+                          topk.group_scores_bruteforce(q2, k, mem2))
