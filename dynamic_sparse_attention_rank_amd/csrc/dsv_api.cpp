@@ -153,9 +153,8 @@ int dsv_validate(int op, const dsv_problem* p, const int32_t* k_per_head, int re
   int n;
   switch (op) {
     case DSV_OP_TOPK:
-      if (reduce == DSV_GROUP_MAX)
-        return fail(DSV_ERR_UNSUPPORTED, "DSV_GROUP_MAX is not implemented");
-      if (reduce != DSV_GROUP_SUM) return fail(DSV_ERR_UNSUPPORTED, "unknown reduce %d", reduce);
+      if (reduce != DSV_GROUP_SUM && reduce != DSV_GROUP_MAX)
+        return fail(DSV_ERR_UNSUPPORTED, "unknown reduce %d", reduce);
       names = topk_names; aligns = topk_align; n = 3; break;
     case DSV_OP_FWD: names = fwd_names; aligns = fwd_align; n = 6; break;
     case DSV_OP_BWD: names = bwd_names; aligns = bwd_align; n = 10; break;
@@ -187,7 +186,7 @@ int dsv_lowrank_topk(const dsv_problem* p, const void* q_lr, const void* k_lr,
   if (st != DSV_OK) return st;
   Geom geo;
   validate_problem(p, k_per_head, &geo);
-  int e = launch_topk(geo, q_lr, k_lr, idx, stream);
+  int e = launch_topk(geo, q_lr, k_lr, reduce, idx, stream);
   if (e) return fail(DSV_ERR_HIP, "top-k launch failed (hipError %d)", e);
   return DSV_OK;
 }

@@ -45,7 +45,8 @@ struct AdaptiveParams {
 };
 
 // Kernel launchers (one per translation unit). Return 0 or a hipError_t value.
-int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int32_t* idx, void* stream);
+int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int reduce, int32_t* idx,
+                void* stream);
 int launch_adaptive_k(const Geom& geo, const void* q_lr, const void* k_lr,
                       const AdaptiveParams& ap, int32_t* k_group, int32_t* k_head, void* stream);
 int launch_attn_fwd(const Geom& geo, const void* q, const void* k, const void* v,

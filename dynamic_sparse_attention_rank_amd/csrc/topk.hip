@@ -522,6 +522,270 @@ __global__ __launch_bounds__(TK_THREADS) void adaptive_k_kernel(const void* __re
   }
 }
 
+// ---- MAX group reduction: sigma[g][m] = max over the members n of g of Q_lr[n] . K_lr[m]
+//
+// The per-member scores are the literal S x S x r product: one wave owns two groups and keeps
+// their members' Q_lr rows as MFMA operands in registers (rows = members, 32 per tile), the
+// key rows are the other operand (columns = keys), so a lane holds one key and 16 members:
+// the group maximum is an in-lane max and one swap with the partner lane. A wave then runs
+// the same exact radix select and ordered compaction as the SUM path on its own two groups
+// (lanes 0..31: the first group, 32..63: the second; lane c holds key 32t + c of block t),
+// with no workgroup barriers: its histograms and state are its own. Equal bins of one
+// instruction are folded by ballots in the first pass, where nearly all keys share a few bins.
+constexpr int TM_WAVES = 4;
+constexpr int TM_THREADS = 64 * TM_WAVES;
+constexpr int TM_GROUPS = 2 * TM_WAVES;   // groups per workgroup
+
+template <bool F32, int R>
+__global__ __launch_bounds__(TM_THREADS) void topk_max_kernel(const void* __restrict__ qlr_,
+                                                              const void* __restrict__ klr_,
+                                                              int32_t* __restrict__ idx,
+                                                              Geom geo) {
+  using C = TopkCfg<F32, R>;
+  __shared__ uint32_t hist[TM_GROUPS * TK_HSTRIDE];
+  __shared__ uint32_t st_prefix[TM_GROUPS];
+  __shared__ int st_krem[TM_GROUPS];
+  __shared__ int st_npass[TM_GROUPS];   // as in topk_kernel
+  __shared__ uint32_t st_lowbits[TM_GROUPS];
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int c32 = lane & 31;
+  const int hh = lane >> 5;
+  // block -> (b, h, group block), one (b, h)'s blocks on one XCD, heavy heads first
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int logical = xcd * (nblk >> 3) + min(xcd, nblk & 7) + (blockIdx.x >> 3);
+  const int gblocks = (geo.NG + TM_GROUPS - 1) / TM_GROUPS;
+  const int slot = logical / gblocks;
+  const int gblock = logical - slot * gblocks;
+  const int b = slot / geo.H;
+  const int h = geo.order[slot - b * geo.H];
+  const int S = geo.S;
+  const int kh = geo.k[h];
+  const int g0 = gblock * TM_GROUPS + 2 * w;   // the wave's groups g0, g0 + 1
+  if (g0 >= geo.NG) return;                    // the whole wave; there are no barriers
+  const int gl = 2 * w + hh;                   // the lane's group, local index
+  const int my_g = g0 + hh;
+  const bool gvalid = my_g < geo.NG;
+  const long long head_base = ((long long)b * geo.H + h) * S * R;
+  const unsigned char* klr = static_cast<const unsigned char*>(klr_) + head_base * C::ES;
+  const unsigned char* qlr = static_cast<const unsigned char*>(qlr_) + head_base * C::ES;
+
+  if (kh == S) {   // dense head: every key, in order, without scoring
+    for (int gi = 0; gi < 2 && g0 + gi < geo.NG; ++gi) {
+      int32_t* row = idx + geo.row_offset(b, h, g0 + gi);
+      for (int m = lane; m < S; m += 64) row[m] = m;
+    }
+    return;
+  }
+
+  // ---- member operands: tile qt of group g0 + gw holds members 32 qt + c32 (rows); members
+  // past G are zero rows whose scores are masked below
+  const int G = geo.G;
+  const int nqt = (G + 31) >> 5;
+  u32x4 qa[2][2][C::NB];
+  const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
+#pragma unroll
+  for (int gw = 0; gw < 2; ++gw)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const int j = 32 * qt + c32;
+      const bool ok = g0 + gw < geo.NG && j < G;
+      const unsigned char* row = qlr + (long long)(ok ? gg.token(g0 + gw, j) : 0) * C::RB;
+#pragma unroll
+      for (int i = 0; i < C::NB; ++i)
+        qa[gw][qt][i] = ok ? ld16(row + C::off(i, hh)) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+  // ---- key operands of block t (key 32t + c32, clamped) and the block's group maxima:
+  // lane c of half hh gets sigma[g0 + hh][32t + c]
+  auto load_k = [&](int t, u32x4* kb) {
+    const int m = min(32 * t + c32, S - 1);
+    const unsigned char* krow = klr + (long long)m * C::RB;
+#pragma unroll
+    for (int i = 0; i < C::NB; ++i) kb[i] = ld16(krow + C::off(i, hh));
+  };
+  auto block_max = [&](const u32x4* kb) -> float {
+    float mx[2];
+#pragma unroll
+    for (int gw = 0; gw < 2; ++gw) {
+      mx[gw] = -INFINITY;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        if (qt >= nqt) break;   // uniform: G <= 32 has one member tile
+        floatx16 acc;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < C::NB; ++i) {
+          if constexpr (F32) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc = mfma32_f32(__uint_as_float(qa[gw][qt][i][e]), __uint_as_float(kb[i][e]), acc);
+          } else {
+            acc = mfma32_bf16(qa[gw][qt][i], kb[i], acc);
+          }
+        }
+        if (32 * qt + 32 > G) {   // uniform: rows (members) 32 qt + 8i + 4hh + j past G
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (32 * qt + 8 * (e >> 2) + 4 * hh + (e & 3) >= G) acc[e] = -INFINITY;
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx[gw] = fmaxf(mx[gw], acc[e]);
+      }
+    }
+    const float m0 = fmaxf(mx[0], __shfl_xor(mx[0], 32, 64));
+    const float m1 = fmaxf(mx[1], __shfl_xor(mx[1], 32, 64));
+    return hh ? m1 : m0;
+  };
+  const int nblocks = (S + 31) >> 5;
+  // body(score, t): loads two blocks ahead, scores one block ahead
+  auto walk = [&](auto&& body) {
+    u32x4 k0[C::NB], k1[C::NB];
+    load_k(0, k0);
+    load_k(1, k1);
+    float sc = block_max(k0);
+    for (int t = 0; t < nblocks; t += 2) {
+      load_k(t + 2, k0);
+      float nx = block_max(k1);
+      body(sc, t);
+      sc = nx;
+      if (t + 1 >= nblocks) break;
+      load_k(t + 3, k1);
+      nx = block_max(k0);
+      body(sc, t + 1);
+      sc = nx;
+    }
+  };
+
+  if (c32 == 0) {
+    st_prefix[gl] = 0;
+    st_lowbits[gl] = 0;
+    st_krem[gl] = kh;
+    st_npass[gl] = gvalid ? 0 : -1;
+  }
+  for (int i = lane; i < 2 * TK_HSTRIDE; i += 64) hist[2 * w * TK_HSTRIDE + i] = 0;
+  wave_lds_fence();
+  uint32_t* const hrow = &hist[gl * TK_HSTRIDE];
+
+  for (int pass = 0; pass < 4; ++pass) {
+    const bool act = st_npass[gl] == pass;
+    if (__ballot(act) == 0) continue;   // uniform: neither group refines in this pass
+    const int dshift = 24 - 8 * pass;
+    const int pshift = 32 - 8 * pass;
+    const unsigned long long pfx = st_prefix[gl];
+    const float lo = key_lower_bound(pfx << (pshift & 31));
+    const float hi = key_upper_bound((pfx + 1) << (pshift & 31));
+    uint32_t lowor = 0;
+    if (pass == 0) {
+      // nearly every key falls into a few bins: one atomic per distinct (group, bin)
+      walk([&](const float sc, const int t) {
+        const bool take = act && 32 * t + c32 < S;
+        const uint32_t bin = score_key(sc) >> 24;
+        unsigned long long todo = __ballot(take);
+        while (todo) {
+          const int l0 = __builtin_ctzll(todo);
+          const uint32_t b0 = __builtin_amdgcn_readlane(bin, l0);
+          const unsigned long long m = __ballot(take && bin == b0 && hh == (l0 >> 5));
+          if (lane == l0)
+            __hip_atomic_fetch_add(&hist[(2 * w + (l0 >> 5)) * TK_HSTRIDE + b0],
+                                   (uint32_t)__popcll(m), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+          todo &= ~m;
+        }
+      });
+      lowor = 1u;   // not tracked in the first pass
+    } else {
+      walk([&](const float sc, const int t) {
+        if (act && 32 * t + c32 < S && sc >= lo && sc < hi) {
+          const uint32_t key = score_key(sc);
+          __hip_atomic_fetch_add(&hrow[(key >> dshift) & 255u], 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+          lowor |= key;
+        }
+      });
+    }
+    uint32_t o = lowor & ((1u << dshift) - 1u);
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) o |= __shfl_xor(o, off, 64);
+    if (c32 == 0 && o != 0) st_lowbits[gl] = 1u;
+    wave_lds_fence();
+    // resolve digit `pass` of each of the wave's groups that refined in it
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int glr = 2 * w + gi;
+      if (st_npass[glr] != pass) continue;   // uniform
+      uint32_t* hr = &hist[glr * TK_HSTRIDE];
+      uint32_t c[4];
+      uint32_t lsum = 0;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        c[tt] = hr[255 - (4 * lane + tt)];
+        lsum += c[tt];
+      }
+      uint32_t incl = lsum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t x = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += x;
+      }
+      const uint32_t krem = (uint32_t)st_krem[glr];
+      uint32_t excl = incl - lsum;
+      wave_lds_fence();   // every lane has read the state before one lane rewrites it
+      if (excl < krem && krem <= incl) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (excl + c[tt] >= krem) {
+            const uint32_t bin = 255u - (4u * lane + tt);
+            const uint32_t left = krem - excl;
+            st_prefix[glr] = (pass == 0) ? bin : ((st_prefix[glr] << 8) | bin);
+            st_krem[glr] = (int)left;
+            st_npass[glr] = (left == c[tt] || pass == 3 || st_lowbits[glr] == 0)
+                                ? 16 + pass + 1 : pass + 1;
+            break;
+          }
+          excl += c[tt];
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) hr[4 * lane + tt] = 0;
+      wave_lds_fence();
+      if (lane == 0) st_lowbits[glr] = 0;
+      wave_lds_fence();
+    }
+  }
+
+  // ---- compaction: keys above the threshold plus the first `left` equal to it, in key order
+  const int gs = st_npass[gl];
+  const unsigned long long pfx = gs >= 16 ? st_prefix[gl] : 0xffffffffull;
+  const int shift = gs >= 16 ? 32 - 8 * (gs - 16) : 0;
+  const float f_hi = key_lower_bound((pfx + 1) << shift);
+  const float f_hi_u = key_upper_bound((pfx + 1) << shift);
+  const float f_lo = key_lower_bound(pfx << shift);
+  int left = gs >= 16 ? st_krem[gl] : 0;
+  int cnt = 0;
+  int32_t* const orow = idx + geo.row_offset(b, h, gvalid ? my_g : g0);
+  const uint32_t below = (1u << c32) - 1u;
+  walk([&](const float sc, const int t) {
+    const int m = 32 * t + c32;
+    const bool valid = m < S;
+    const bool gt = valid && sc >= f_hi;
+    const bool eq = valid && sc >= f_lo && sc < f_hi_u;
+    const uint32_t gth = (uint32_t)(__ballot(gt) >> (32 * hh));
+    const uint32_t eqh = (uint32_t)(__ballot(eq) >> (32 * hh));
+    const int lft = max(left, 0);
+    const int eqb = __popc(eqh & below);
+    const bool sel = gt || (eq && eqb < lft);
+    const int pos = cnt + __popc(gth & below) + min(lft, eqb);
+    if (sel && gvalid && pos < kh) orow[pos] = m;
+    cnt += __popc(gth) + min(lft, __popc(eqh));
+    left -= __popc(eqh);
+  });
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -529,16 +793,23 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
 
 }  // namespace
 
-int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int32_t* idx, void* stream) {
-  const int gblocks = (geo.NG + TK_GROUPS - 1) / TK_GROUPS;
+int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int reduce, int32_t* idx,
+                void* stream) {
+  const bool mx = reduce == DSV_GROUP_MAX;
+  const int gpb = mx ? TM_GROUPS : TK_GROUPS;
+  const int gblocks = (geo.NG + gpb - 1) / gpb;
   const dim3 grid(geo.B * geo.H * gblocks);
-  const dim3 block(TK_THREADS);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool f32 = geo.dtype == DSV_FP32;
-#define DSV_TOPK_CASE(F, RR)                                                               \
-  if (f32 == F && geo.r == RR) {                                                           \
-    hipLaunchKernelGGL((topk_kernel<F, RR>), grid, block, 0, st, q_lr, k_lr, idx, geo);    \
-    return (int)hipGetLastError();                                                         \
+#define DSV_TOPK_CASE(F, RR)                                                                    \
+  if (f32 == F && geo.r == RR) {                                                                \
+    if (mx)                                                                                     \
+      hipLaunchKernelGGL((topk_max_kernel<F, RR>), grid, dim3(TM_THREADS), 0, st, q_lr, k_lr,   \
+                         idx, geo);                                                             \
+    else                                                                                        \
+      hipLaunchKernelGGL((topk_kernel<F, RR>), grid, dim3(TK_THREADS), 0, st, q_lr, k_lr, idx,  \
+                         geo);                                                                  \
+    return (int)hipGetLastError();                                                              \
   }
   DSV_TOPK_CASE(false, 16)
   DSV_TOPK_CASE(false, 32)

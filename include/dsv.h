@@ -53,8 +53,9 @@ extern "C" {
 typedef enum { DSV_FP32 = 0, DSV_BF16 = 1 } dsv_dtype;
 
 /* How the per-query low-rank scores of a group are combined into one group score.
- * SUM: sigma[g][m] = sum_{n in g} Q_lr[n].K_lr[m] (MEAN ranks identically). MAX is not
- * implemented and returns DSV_ERR_UNSUPPORTED. */
+ * SUM: sigma[g][m] = sum_{n in g} Q_lr[n].K_lr[m] (MEAN ranks identically).
+ * MAX: sigma[g][m] = max_{n in g} Q_lr[n].K_lr[m] (the per-query S x S scores, never stored;
+ * about G times the MFMA work of SUM per pass over the keys). */
 typedef enum { DSV_GROUP_SUM = 0, DSV_GROUP_MAX = 1 } dsv_reduce;
 
 typedef enum {
@@ -98,15 +99,16 @@ int64_t dsv_idx_row_offset(const dsv_problem* p, const int32_t* k_per_head, int3
  * (DSV summaries: zh §2.1 and §2.2, pt §2A-§2B, fr §2A-§2B, ko §2가-§2나.)
  *   q_lr, k_lr : [B][H][S][r] device, dtype p->dtype.
  *   k_per_head : host [H].
- *   reduce     : DSV_GROUP_SUM.
+ *   reduce     : DSV_GROUP_SUM or DSV_GROUP_MAX.
  *   idx        : device int32, dsv_idx_elems() elements, written.
- * For every (b,h,g): sigma[m] = (sum_{n in g} q_lr[n]) . k_lr[m] evaluated in fp32 (equal to
- * summing the per-query scores, by linearity); the row holds the k_h keys with the largest
- * sigma, equal scores ranked by lower key index, written in ascending key order.
+ * For every (b,h,g): with SUM, sigma[m] = (sum_{n in g} q_lr[n]) . k_lr[m] evaluated in fp32
+ * (equal to summing the per-query scores, by linearity); with MAX, sigma[m] = the largest
+ * per-query score q_lr[n] . k_lr[m] over the members (fp32). The row holds the k_h keys with
+ * the largest sigma, equal scores ranked by lower key index, written in ascending key order.
  * Exactness: the scores, hence idx, are exact when Q_lr and K_lr hold integers with
- * G*max|q| < 2^16 and G*r*max|q|*max|k| < 2^24 (the bf16 path splits the group sum into two
- * bf16 terms; outside this domain the group sum is rounded to 16 significant bits). The S x S
- * and NG x S score matrices are never stored. */
+ * G*max|q| < 2^16 and G*r*max|q|*max|k| < 2^24 (SUM: the bf16 path splits the group sum into
+ * two bf16 terms; outside this domain the group sum is rounded to 16 significant bits; MAX:
+ * r*max|q|*max|k| < 2^24). The S x S and NG x S score matrices are never stored. */
 int dsv_lowrank_topk(const dsv_problem* p, const void* q_lr, const void* k_lr,
                      const int32_t* k_per_head, int reduce, int32_t* idx, void* ws,
                      size_t ws_bytes, void* stream);

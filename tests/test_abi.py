@@ -77,8 +77,9 @@ def test_validation_rejects_bad_k_pointers_and_reduce():
     ptrs[2] = FAKE + 8
     assert dsv.STATUS[dsv.validate(dsv.DSV_OP_FWD, p, ks, ptrs)] == "DSV_ERR_ALIGN"
     ptrs = [FAKE] * 3
-    assert dsv.STATUS[dsv.validate(dsv.DSV_OP_TOPK, p, ks, ptrs,
-                                   reduce=dsv.DSV_GROUP_MAX)] == "DSV_ERR_UNSUPPORTED"
+    assert dsv.validate(dsv.DSV_OP_TOPK, p, ks, ptrs, reduce=dsv.DSV_GROUP_MAX) == 0
+    assert dsv.STATUS[dsv.validate(dsv.DSV_OP_TOPK, p, ks, ptrs, reduce=5)] == \
+        "DSV_ERR_UNSUPPORTED"
     assert dsv.STATUS[dsv.validate(dsv.DSV_OP_TOPK, p, ks, [FAKE] * 2)] == "DSV_ERR_NULL"
 
 
