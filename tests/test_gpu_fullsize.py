@@ -157,3 +157,21 @@ def test_mid_adaptive_k_sampled_groups():
                                                mem[g:g + 1])[0]
             ref = oad.k_from_counts(oad.group_bin_counts(sig, ls32), 0.9, w)
             assert kg[0, h, g] == ref, (h, g, kg[0, h, g], ref)
+
+
+def test_mid_topk_max_sampled_groups():
+    """MAX top-k at S=65536: sampled groups of two heads against the brute-force oracle."""
+    cfg = workload("mid")
+    say("[full] mid: top-k with the MAX group reduction")
+    x = gpu_inputs(cfg, backward=False)
+    p = dsv.problem_for(cfg)
+    idx = dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], x["k_per_head"], reduce=dsv.DSV_GROUP_MAX)
+    torch.cuda.synchronize()
+    mem = members(cfg)
+    for h in (0, 17):
+        rows = gpu_rows(cfg, x, idx, 0, h)
+        for g in _sampled_groups(cfg.n_groups, 3, 300 + h):
+            sig = otopk.group_scores_max_bruteforce(f64(x["q_lr"][0, h]), f64(x["k_lr"][0, h]),
+                                                    mem[g:g + 1])
+            ref = otopk.topk_rows_by_sort(sig, int(x["k_per_head"][h]))[0]
+            assert np.array_equal(rows[g], ref), (h, g)
