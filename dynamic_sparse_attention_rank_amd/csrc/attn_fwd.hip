@@ -6,8 +6,9 @@
 //     O[n] = sum_{m in idx(g)} softmax_m(scale * q_n . k_m) v_m,   LSE[n] = log sum_m exp(...)
 //
 // bf16 path (gfx950 MFMA): one wave per group (G = 16..64 queries, d = 64 or 128).
-//   * The group's Q rows sit in LDS (one swizzled copy); S^T = K Q^T reads them as 16-byte B
-//     operands, so a 16x16 score tile gives a lane one query and 4 keys.
+//   * The group's Q rows are staged once in LDS (one swizzled copy) and read from there into
+//     registers as the B operands of S^T = K Q^T for the whole index row; a 16x16 score tile
+//     gives a lane one query and 4 keys.
 //   * Keys are consumed in chunks of 32 from the ascending index row. The chunk's K and V rows
 //     are gathered into an LDS tile by direct-to-LDS loads that cover whole rows (full cache
 //     lines, about twice the gather rate of operand-shaped 64-byte pieces); K operands are
@@ -16,9 +17,11 @@
 //   * Online softmax in the log2 domain with an fp32 running max and sum; the max is only
 //     raised (and O rescaled) when a new score exceeds it by more than 2^8, which keeps exp2
 //     arguments <= 8 and makes rescaling rare. Results are exact regardless of when it is raised.
-//   * The next chunk's rows are requested as soon as the current ones are in registers, and
-//     the key indices one chunk further ahead; every load in the loop is unconditional
-//     (positions clamped), so the waits for them are exact.
+//   * The next chunk's rows are requested as soon as the current ones are in registers; every
+//     lane loads the indices of its own row loads one chunk further ahead. Every load in the
+//     loop is unconditional (positions clamped), so the waits for them are exact.
+//   * Built with MFMA results in VGPRs: the rare rescale multiplies the O accumulators with
+//     VALU ops, and AGPR accumulators would be copied to VGPRs on every chunk.
 // fp32 path: plain fp32 FMA per lane (one lane per query); it exists for fp32 inputs and is
 // not tuned.
 #include <math.h>
