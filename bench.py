@@ -209,8 +209,10 @@ def main():
     o = torch.empty(shp, dtype=dt, device=dev)
     lse = torch.empty(shp[:3], dtype=torch.float32, device=dev)
     dq, dk, dv = (torch.empty(shp, dtype=torch.float32, device=dev) for _ in range(3))
-    # the backward's minimum workspace covers one (b, h) slot; four slots per launch
-    ws_n = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks) * min(4, cfg.batch * cfg.heads)
+    # the backward's minimum workspace covers one (b, h) slot; three times it lets each launch
+    # take two heads (at S=64K, 12 launches), whose gathered K/V rows stay in the MALL (more
+    # heads per launch measured slower)
+    ws_n = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks) * min(3, cfg.batch * cfg.heads)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     staged = cfg.dtype == "bf16"   # per-stage backward events exist on the bf16 path
