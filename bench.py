@@ -100,9 +100,10 @@ def kernel_sources_sha256(names):
     return h.hexdigest()
 
 
-def counter_traffic(kernel, workload):
+def counter_traffic(kernel, workload, launches):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary, or None
-    if there is none for this kernel and workload or its sources have changed since."""
+    if there is none for this kernel and workload, its sources have changed since, or the
+    summary was taken with another number of launches per step (another split of the work)."""
     path = os.path.join(ROOT, "profiles", f"hbm_counters_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -117,6 +118,8 @@ def counter_traffic(kernel, workload):
             vals[cur][key.strip()] = val.strip()
     v = vals.get(kernel)
     if not v or v.get("sources_sha256") != kernel_sources_sha256(v.get("sources", "").split()):
+        return None
+    if int(v.get("launches_per_step", -1)) != launches:
         return None
     return float(v["fetch_bytes_per_launch"]) + float(v["write_bytes_per_launch"])
 
@@ -309,7 +312,7 @@ def main():
         ach = kd["units_per_launch"] / sec / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak,
                 "unit": "TFLOP/s", "frac": ach / peak}
-    roof["traffic"] = counter_traffic(dom, cfg.name)
+    roof["traffic"] = counter_traffic(dom, cfg.name, kd["launches_per_step"])
 
     out = {
         "metric": "sparse attn fwd+bwd TFLOP/s (selected-KV & dense-equiv) + top-k ms, S=64K",
