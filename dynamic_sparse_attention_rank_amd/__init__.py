@@ -27,7 +27,7 @@ EXPORTED = ("dsv_workspace_bytes", "dsv_idx_elems", "dsv_idx_row_offset", "dsv_l
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd", "dsv_bwd_chunks",
             "dsv_sparse_attn_bwd_profiled", "dsv_validate", "dsv_status_string",
             "dsv_last_error", "dsv_version", "dsv_plan_heads", "dsv_default_cost_model",
-            "dsv_dispatch_k", "dsv_adaptive_k")
+            "dsv_dispatch_k", "dsv_adaptive_k", "dsv_topk_max_cache_bytes")
 
 
 class DsvError(RuntimeError):
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
         vp, sz, f = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
         L.dsv_workspace_bytes.argtypes = [ctypes.c_int, P, i32p]
         L.dsv_workspace_bytes.restype = sz
+        L.dsv_topk_max_cache_bytes.argtypes = [P]
+        L.dsv_topk_max_cache_bytes.restype = sz
         L.dsv_idx_elems.argtypes = [P, i32p]
         L.dsv_idx_elems.restype = ctypes.c_int64
         L.dsv_idx_row_offset.argtypes = [P, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
@@ -218,8 +220,10 @@ def _storage_dtype(p: Problem):
 
 
 def lowrank_topk(p: Problem, q_lr, k_lr, k_per_head: Sequence[int], idx=None,
-                 reduce: int = DSV_GROUP_SUM, stream=None):
-    """Critical-KV index lists (packed int32, see include/dsv.h) for Q_lr, K_lr [B,H,S,r]."""
+                 reduce: int = DSV_GROUP_SUM, stream=None, ws=None):
+    """Critical-KV index lists (packed int32, see include/dsv.h) for Q_lr, K_lr [B,H,S,r].
+    `ws` (optional uint8 device tensor): with reduce=MAX, room for c * topk_max_cache_bytes(p)
+    bytes keeps the group scores of c (b, h) slots between selection passes."""
     torch = _torch()
     dt = _storage_dtype(p)
     shp = (p.batch, p.heads, p.seq, p.rank)
@@ -231,9 +235,21 @@ def lowrank_topk(p: Problem, q_lr, k_lr, k_per_head: Sequence[int], idx=None,
     ip = _dev(idx, "idx", torch.int32)
     if idx.numel() < n:
         raise ValueError("idx is too small")
+    wp, wb = None, 0
+    if ws is not None:
+        wp = _dev(ws, "ws", torch.uint8)
+        wb = ws.numel()
     _check(lib().dsv_lowrank_topk(ctypes.byref(p), qp, kp, _kph(k_per_head), reduce, ip,
-                                  None, 0, _stream_ptr(stream)))
+                                  wp, wb, _stream_ptr(stream)))
     return idx
+
+
+def topk_max_cache_bytes(p: Problem) -> int:
+    """Workspace bytes per (b, h) slot for the MAX score cache of lowrank_topk."""
+    n = int(lib().dsv_topk_max_cache_bytes(ctypes.byref(p)))
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError(last_error())
+    return n
 
 
 def adaptive_k(p: Problem, q_lr, k_lr, mass: float = 0.9, logit_scale: Optional[float] = None,

@@ -180,15 +180,21 @@ int dsv_validate(int op, const dsv_problem* p, const int32_t* k_per_head, int re
 int dsv_lowrank_topk(const dsv_problem* p, const void* q_lr, const void* k_lr,
                      const int32_t* k_per_head, int reduce, int32_t* idx, void* ws,
                      size_t ws_bytes, void* stream) {
-  (void)ws;
   const void* ptrs[] = {q_lr, k_lr, idx};
   int st = dsv_validate(DSV_OP_TOPK, p, k_per_head, reduce, ptrs, 3, ws_bytes);
   if (st != DSV_OK) return st;
   Geom geo;
   validate_problem(p, k_per_head, &geo);
-  int e = launch_topk(geo, q_lr, k_lr, reduce, idx, stream);
+  int e = launch_topk(geo, q_lr, k_lr, reduce, idx, ws, ws ? ws_bytes : 0, stream);
   if (e) return fail(DSV_ERR_HIP, "top-k launch failed (hipError %d)", e);
   return DSV_OK;
+}
+
+size_t dsv_topk_max_cache_bytes(const dsv_problem* p) {
+  std::vector<int32_t> ones(p && p->heads > 0 ? p->heads : 1, 1);
+  Geom geo;
+  if (validate_problem(p, ones.data(), &geo) != DSV_OK) return (size_t)-1;
+  return topk_max_cache_slot_bytes(geo);
 }
 
 int dsv_adaptive_k(const dsv_problem* p, const void* q_lr, const void* k_lr, float logit_scale,

@@ -45,8 +45,12 @@ struct AdaptiveParams {
 };
 
 // Kernel launchers (one per translation unit). Return 0 or a hipError_t value.
+// reduce = MAX uses ws (when 256-byte aligned and at least one slot's worth) to keep the group
+// scores between passes, processing as many (b, h) slots per launch as fit.
 int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int reduce, int32_t* idx,
-                void* stream);
+                void* ws, size_t ws_bytes, void* stream);
+size_t topk_max_cache_slot_bytes(const Geom& geo);   // NG rows of S keys (4 bytes each) in
+                                                     // 128-key segments, 256-aligned
 int launch_adaptive_k(const Geom& geo, const void* q_lr, const void* k_lr,
                       const AdaptiveParams& ap, int32_t* k_group, int32_t* k_head, void* stream);
 int launch_attn_fwd(const Geom& geo, const void* q, const void* k, const void* v,

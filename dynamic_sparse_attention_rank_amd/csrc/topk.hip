@@ -28,6 +28,8 @@
 //     32-key slice, and per-tile slice counts in LDS give each slice its offset.
 //   * Consecutive workgroups go to different XCDs; the block index is remapped so that the
 //     workgroups of one (b, h) share an XCD (and its L2) while they stream the same K_lr.
+#include <algorithm>
+
 #include "device_common.h"
 #include "dsv_internal.h"
 
@@ -532,15 +534,23 @@ __global__ __launch_bounds__(TK_THREADS) void adaptive_k_kernel(const void* __re
 // (lanes 0..31: the first group, 32..63: the second; lane c holds key 32t + c of block t),
 // with no workgroup barriers: its histograms and state are its own. Equal bins of one
 // instruction are folded by ballots in the first pass, where nearly all keys share a few bins.
+// With CACHE, the first pass also stores every group score as its order-preserving key in a
+// caller workspace (one row per group; slots s0 .. s0 + gridDim / blocks-per-slot of this
+// launch), and the later passes and the compaction read the keys back instead of recomputing
+// the 32-member products: one S x S x r product per launch instead of one per pass. A row
+// holds segments of 4 key blocks (128 keys): the key of lane c in block t sits at
+// 128 (t / 4) + 4c + t % 4, so one 16-byte load gives a lane its keys of 4 blocks. Both
+// variants select the same keys.
 constexpr int TM_WAVES = 4;
 constexpr int TM_THREADS = 64 * TM_WAVES;
 constexpr int TM_GROUPS = 2 * TM_WAVES;   // groups per workgroup
 
-template <bool F32, int R>
+template <bool F32, int R, bool CACHE>
 __global__ __launch_bounds__(TM_THREADS) void topk_max_kernel(const void* __restrict__ qlr_,
                                                               const void* __restrict__ klr_,
                                                               int32_t* __restrict__ idx,
-                                                              Geom geo) {
+                                                              Geom geo, int s0,
+                                                              uint32_t* __restrict__ cache) {
   using C = TopkCfg<F32, R>;
   __shared__ uint32_t hist[TM_GROUPS * TK_HSTRIDE];
   __shared__ uint32_t st_prefix[TM_GROUPS];
@@ -558,8 +568,9 @@ __global__ __launch_bounds__(TM_THREADS) void topk_max_kernel(const void* __rest
   const int xcd = blockIdx.x & 7;
   const int logical = xcd * (nblk >> 3) + min(xcd, nblk & 7) + (blockIdx.x >> 3);
   const int gblocks = (geo.NG + TM_GROUPS - 1) / TM_GROUPS;
-  const int slot = logical / gblocks;
-  const int gblock = logical - slot * gblocks;
+  const int lslot = logical / gblocks;   // slot inside this launch
+  const int gblock = logical - lslot * gblocks;
+  const int slot = s0 + lslot;
   const int b = slot / geo.H;
   const int h = geo.order[slot - b * geo.H];
   const int S = geo.S;
@@ -642,6 +653,12 @@ __global__ __launch_bounds__(TM_THREADS) void topk_max_kernel(const void* __rest
     return hh ? m1 : m0;
   };
   const int nblocks = (S + 31) >> 5;
+  // the lane's row of cached keys (its group's; a lane of an absent second group reads the
+  // first group's row and its results are discarded); rows of nseg segments of 128 keys
+  const int nseg = (nblocks + 3) >> 2;
+  uint32_t* const crow =
+      CACHE ? cache + ((long long)lslot * geo.NG + (gvalid ? my_g : g0)) * (128LL * nseg)
+            : nullptr;
   // body(score, t): loads two blocks ahead, scores one block ahead
   auto walk = [&](auto&& body) {
     u32x4 k0[C::NB], k1[C::NB];
@@ -659,6 +676,31 @@ __global__ __launch_bounds__(TM_THREADS) void topk_max_kernel(const void* __rest
       body(sc, t + 1);
       sc = nx;
     }
+  };
+
+  // the later walks: cached keys, U segments (4U blocks) of loads in flight; a lane reads back
+  // only the positions it stored itself (blocks past the last one: never used)
+  auto walk_cached = [&](auto&& body) {
+    constexpr int U = 4;
+    for (int T0 = 0; T0 < nseg; T0 += U) {
+      u32x4 u[U];
+#pragma unroll
+      for (int i = 0; i < U; ++i)
+        u[i] = ld16(crow + 128LL * min(T0 + i, nseg - 1) + 4 * c32);
+#pragma unroll
+      for (int i = 0; i < U; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 4 * (T0 + i) + e;
+          if (t < nblocks) body(key_float(u[i][e]), t);   // uniform
+        }
+    }
+  };
+  auto walk_later = [&](auto&& body) {
+    if constexpr (CACHE)
+      walk_cached(body);
+    else
+      walk(body);
   };
 
   if (c32 == 0) {
@@ -683,6 +725,8 @@ __global__ __launch_bounds__(TM_THREADS) void topk_max_kernel(const void* __rest
     if (pass == 0) {
       // nearly every key falls into a few bins: one atomic per distinct (group, bin)
       walk([&](const float sc, const int t) {
+        if constexpr (CACHE)
+          if (gvalid) crow[128 * (t >> 2) + 4 * c32 + (t & 3)] = score_key(sc);
         const bool take = act && 32 * t + c32 < S;
         const uint32_t bin = score_key(sc) >> 24;
         unsigned long long todo = __ballot(take);
@@ -698,8 +742,9 @@ __global__ __launch_bounds__(TM_THREADS) void topk_max_kernel(const void* __rest
         }
       });
       lowor = 1u;   // not tracked in the first pass
+      if constexpr (CACHE) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
     } else {
-      walk([&](const float sc, const int t) {
+      walk_later([&](const float sc, const int t) {
         if (act && 32 * t + c32 < S && sc >= lo && sc < hi) {
           const uint32_t key = score_key(sc);
           __hip_atomic_fetch_add(&hrow[(key >> dshift) & 255u], 1u, __ATOMIC_RELAXED,
@@ -769,7 +814,7 @@ __global__ __launch_bounds__(TM_THREADS) void topk_max_kernel(const void* __rest
   int cnt = 0;
   int32_t* const orow = idx + geo.row_offset(b, h, gvalid ? my_g : g0);
   const uint32_t below = (1u << c32) - 1u;
-  walk([&](const float sc, const int t) {
+  walk_later([&](const float sc, const int t) {
     const int m = 32 * t + c32;
     const bool valid = m < S;
     const bool gt = valid && sc >= f_hi;
@@ -793,22 +838,40 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int32_t v) {
 
 }  // namespace
 
+size_t topk_max_cache_slot_bytes(const Geom& geo) {
+  const size_t row = ((size_t)geo.S + 127) / 128 * 128;   // whole 128-key segments
+  return ((size_t)geo.NG * row * sizeof(uint32_t) + 255) & ~(size_t)255;
+}
+
 int launch_topk(const Geom& geo, const void* q_lr, const void* k_lr, int reduce, int32_t* idx,
-                void* stream) {
+                void* ws, size_t ws_bytes, void* stream) {
   const bool mx = reduce == DSV_GROUP_MAX;
   const int gpb = mx ? TM_GROUPS : TK_GROUPS;
   const int gblocks = (geo.NG + gpb - 1) / gpb;
-  const dim3 grid(geo.B * geo.H * gblocks);
+  const int nslots = geo.B * geo.H;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool f32 = geo.dtype == DSV_FP32;
+  // MAX with a workspace for at least one slot's scores: chunks of slots that fit it
+  const size_t per_slot = topk_max_cache_slot_bytes(geo);
+  const int cslots = (mx && ws && reinterpret_cast<uintptr_t>(ws) % 256 == 0)
+                         ? (int)std::min<size_t>((size_t)nslots, ws_bytes / per_slot)
+                         : 0;
+  uint32_t* cache = static_cast<uint32_t*>(ws);
 #define DSV_TOPK_CASE(F, RR)                                                                    \
   if (f32 == F && geo.r == RR) {                                                                \
-    if (mx)                                                                                     \
-      hipLaunchKernelGGL((topk_max_kernel<F, RR>), grid, dim3(TM_THREADS), 0, st, q_lr, k_lr,   \
-                         idx, geo);                                                             \
-    else                                                                                        \
-      hipLaunchKernelGGL((topk_kernel<F, RR>), grid, dim3(TK_THREADS), 0, st, q_lr, k_lr, idx,  \
-                         geo);                                                                  \
+    if (mx && cslots > 0) {                                                                     \
+      for (int s0 = 0; s0 < nslots; s0 += cslots) {                                             \
+        const int n = std::min(cslots, nslots - s0);                                            \
+        hipLaunchKernelGGL((topk_max_kernel<F, RR, true>), dim3(n * gblocks),                   \
+                           dim3(TM_THREADS), 0, st, q_lr, k_lr, idx, geo, s0, cache);           \
+      }                                                                                         \
+    } else if (mx) {                                                                            \
+      hipLaunchKernelGGL((topk_max_kernel<F, RR, false>), dim3(nslots * gblocks),               \
+                         dim3(TM_THREADS), 0, st, q_lr, k_lr, idx, geo, 0, nullptr);            \
+    } else {                                                                                    \
+      hipLaunchKernelGGL((topk_kernel<F, RR>), dim3(nslots * gblocks), dim3(TK_THREADS), 0, st, \
+                         q_lr, k_lr, idx, geo);                                                 \
+    }                                                                                           \
     return (int)hipGetLastError();                                                              \
   }
   DSV_TOPK_CASE(false, 16)

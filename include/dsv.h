@@ -108,10 +108,21 @@ int64_t dsv_idx_row_offset(const dsv_problem* p, const int32_t* k_per_head, int3
  * Exactness: the scores, hence idx, are exact when Q_lr and K_lr hold integers with
  * G*max|q| < 2^16 and G*r*max|q|*max|k| < 2^24 (SUM: the bf16 path splits the group sum into
  * two bf16 terms; outside this domain the group sum is rounded to 16 significant bits; MAX:
- * r*max|q|*max|k| < 2^24). The S x S and NG x S score matrices are never stored. */
+ * r*max|q|*max|k| < 2^24). The S x S score matrix is never stored.
+ *   ws, ws_bytes : optional device workspace (may be NULL / 0; SUM ignores it). With MAX and
+ *                  ws 256-byte aligned, ws_bytes >= c * dsv_topk_max_cache_bytes(p) (c >= 1)
+ *                  lets c (b,h) slots per launch keep their NG x S group scores in ws between
+ *                  the passes of the selection instead of recomputing the member products in
+ *                  every pass; the result is the same. Contents on entry ignored, clobbered.
+ * The stream gets one launch, or with the MAX cache one launch per c slots. */
 int dsv_lowrank_topk(const dsv_problem* p, const void* q_lr, const void* k_lr,
                      const int32_t* k_per_head, int reduce, int32_t* idx, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* Workspace bytes per (b,h) slot for the MAX score cache of dsv_lowrank_topk: NG rows of
+ * S keys rounded up to a multiple of 128, 4 bytes each, the total rounded up to 256
+ * ((size_t)-1 if the problem is invalid). */
+size_t dsv_topk_max_cache_bytes(const dsv_problem* p);
 
 /* Adaptive k: the number of keys per group that carry a given share of the group's estimated
  * attention mass. (DSV summaries: zh §2.1 stage two, "critical KV estimation": the low-rank

@@ -166,7 +166,14 @@ def test_mid_topk_max_sampled_groups():
     x = gpu_inputs(cfg, backward=False)
     p = dsv.problem_for(cfg)
     idx = dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], x["k_per_head"], reduce=dsv.DSV_GROUP_MAX)
+    # the configuration bench.py times: every slot's group scores cached in the workspace
+    ws = torch.empty(dsv.topk_max_cache_bytes(p) * cfg.batch * cfg.heads, dtype=torch.uint8,
+                     device="cuda")
+    idx_c = dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], x["k_per_head"],
+                             reduce=dsv.DSV_GROUP_MAX, ws=ws)
     torch.cuda.synchronize()
+    del ws
+    assert torch.equal(idx_c, idx)
     mem = members(cfg)
     for h in (0, 17):
         rows = gpu_rows(cfg, x, idx, 0, h)

@@ -60,3 +60,46 @@ def test_topk_max_differs_from_sum_and_repeats():
     torch.cuda.synchronize()
     assert torch.equal(a, b2)
     assert not torch.equal(a, s)   # the two readings select different keys on these inputs
+
+
+def _cache_ws(p, slots):
+    return torch.empty(dsv.topk_max_cache_bytes(p) * slots, dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("label,name,over,ks", CASES, ids=[c[0] for c in CASES])
+def test_topk_max_cached_bit_exact(label, name, over, ks):
+    """Group scores kept in the workspace between passes: same rows as the oracle."""
+    cfg = workload(name, **over)
+    say(f"[topk-max cached] {label}")
+    x = gpu_inputs(cfg, backward=False, k_per_head=ks)
+    p = dsv.problem_for(cfg)
+    ws = _cache_ws(p, cfg.batch * cfg.heads)
+    idx = dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], x["k_per_head"], reduce=dsv.DSV_GROUP_MAX,
+                           ws=ws)
+    torch.cuda.synchronize()
+    mem = members(cfg)
+    for b in range(cfg.batch):
+        for h in range(cfg.heads):
+            got = gpu_rows(cfg, x, idx, b, h)
+            ref = _max_rows(cfg, x, b, h, mem)
+            assert np.array_equal(got, ref), (b, h, np.argwhere(got != ref)[:5])
+
+
+@pytest.mark.parametrize("slots", [1, 2, 5, 6])
+def test_topk_max_cache_chunks(slots):
+    """Workspaces for fewer slots than B*H (launches of `slots` slots, the last one short), and
+    one just short of a slot (no cache): bit-identical to the recomputing kernel."""
+    cfg = workload("small", batch=2, heads=3, frames=4, height=8, width=12, group=(2, 2, 4),
+                   rank=32)
+    say(f"[topk-max cache chunks] slots={slots}")
+    x = gpu_inputs(cfg, backward=False, k_per_head=[7, 45, 100])
+    p = dsv.problem_for(cfg)
+    ref = dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], x["k_per_head"], reduce=dsv.DSV_GROUP_MAX)
+    ws = _cache_ws(p, slots)
+    got = dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], x["k_per_head"], reduce=dsv.DSV_GROUP_MAX,
+                           ws=ws)
+    short = dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], x["k_per_head"],
+                             reduce=dsv.DSV_GROUP_MAX, ws=ws[:dsv.topk_max_cache_bytes(p) - 256])
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref)
+    assert torch.equal(short, ref)
