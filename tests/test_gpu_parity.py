@@ -136,6 +136,12 @@ FWD_CASES = [
                            dtype="fp32"), [17, 256]),
     ("fp32-d64-G16-k1", dict(heads=1, frames=4, height=8, width=8, group=(2, 2, 4),
                              dtype="fp32"), [1]),
+    # the remaining (head dim, query blocks) instances of the bf16 kernel
+    ("bf16-d128-G16", dict(heads=2, frames=4, height=8, width=16, group=(2, 2, 4),
+                           head_dim=128, rank=32), [70, 129]),
+    ("bf16-d128-G48", dict(heads=1, frames=3, height=8, width=16, group=(3, 4, 4),
+                           head_dim=128, rank=32), [95]),
+    ("bf16-d64-G32", dict(heads=2, frames=2, height=8, width=16, group=(2, 4, 4)), [31, 200]),
 ]
 
 
@@ -219,6 +225,12 @@ BWD_CASES = [
                            dtype="fp32"), [17, 256]),
     ("fp32-d64-G32-k1", dict(heads=1, frames=4, height=8, width=8, group=(2, 4, 4),
                              dtype="fp32"), [1]),
+    # the remaining (head dim, query blocks) instances of the bf16 kernel
+    ("bf16-d128-G16", dict(heads=2, frames=4, height=8, width=16, group=(2, 2, 4),
+                           head_dim=128, rank=32), [70, 129]),
+    ("bf16-d128-G32", dict(heads=2, frames=4, height=8, width=16, group=(2, 4, 4),
+                           head_dim=128, rank=32), [33, 257]),
+    ("bf16-d64-G48", dict(heads=1, frames=3, height=8, width=16, group=(3, 4, 4)), [130]),
 ]
 
 
