@@ -203,14 +203,19 @@ __global__ __launch_bounds__(256) void bucket_offsets(const uint32_t* __restrict
 // Bucket-ordered edge list: perm[off[j] + i], i < tot[j], holds the edges (g, p) whose key
 // lies in bucket j, ordered by group, then by position, each as (slot-relative staging row
 // g*padded_k + p) << 5 | (key - 32 j). One wave per (slot, bucket); 64 groups per step,
-// positions from a wave scan; the keys of a step's runs are read 8 per lane at a time.
+// positions from a wave scan; the keys of a step's runs are read 8 per lane at a time. A
+// 128-byte line of an index row holds the keys of about ten consecutive buckets, so the block
+// index is remapped to give each XCD a contiguous range of buckets (one L2 then serves a line
+// to all of them).
 __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ rsT,
                                                   const uint32_t* __restrict__ off,
                                                   const int32_t* __restrict__ idx, Chunk ch,
                                                   uint32_t* __restrict__ perm, Geom geo) {
   const int nB = n_buckets(geo.S);
-  const int sl = blockIdx.x / nB;
-  const int j = blockIdx.x - sl * nB;
+  const int nblk = gridDim.x, xcd = blockIdx.x & 7;
+  const int logical = xcd * (nblk >> 3) + min(xcd, nblk & 7) + (blockIdx.x >> 3);
+  const int sl = logical / nB;
+  const int j = logical - sl * nB;
   const int lane = threadIdx.x;
   int b, h;
   chunk_slot(geo, ch.s0 + sl, b, h);
