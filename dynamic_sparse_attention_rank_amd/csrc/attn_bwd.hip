@@ -274,8 +274,9 @@ __global__ void fill_zero(float4* __restrict__ p, long long n4) {
 // Lane l owns features (D/64)*l .. of the half; the bucket's key rows accumulate in LDS.
 // Each step takes 64 entries of the bucket's edge list (edge row, key, step: one per lane),
 // then walks them one row per instruction, so no two lanes ever touch the same LDS word and
-// rows with equal keys are added in list order. 32 row loads are in flight per wave. Every
-// key row of the bucket is then written once (zero where no group selected the key).
+// rows with equal keys are added in list order. The step's 64 row loads are issued at once,
+// and the next step's entries and steps are requested during this one. Every key row of the
+// bucket is then written once (zero where no group selected the key).
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 template <int D>
 __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__ off,
@@ -286,7 +287,6 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
                                                    float* __restrict__ dk, float* __restrict__ dv,
                                                    Geom geo) {
   constexpr int FPL = D / 64;   // features per lane
-  constexpr int U = 32;         // rows in flight
   __shared__ __attribute__((aligned(16))) float acc[kBucket * D];
   const int nB = n_buckets(geo.S);
   const int half = blockIdx.x & 1;
@@ -308,24 +308,25 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
   const uint32_t* pm = perm + eb;
   const uint16_t* src = (half ? ck : cv) + eb * D + FPL * lane;
   const int key0 = j * kBucket;
-  for (long long r0 = s0; r0 < s1; r0 += 64) {
-    const int n = (int)std::min<long long>(64, s1 - r0);
-    // lanes past the end read row 0 of the slot and add it with step 0
-    uint32_t e = 0;
-    int kk = 0;
-    float sc = 0.f;
-    if (lane < n) {
-      const uint32_t ent = pm[r0 + lane];
-      e = std::min<uint32_t>(ent >> 5, (uint32_t)(nrows - 1));
-      kk = (int)(ent & 31u);
-      const float2 st = bstep[(eb + e) >> 4];   // the step of the row's 16-key block
-      sc = half ? st.y : st.x;
-    }
-    for (int u0 = 0; u0 < n; u0 += U) {
-      uint32_t x[U];
+  // entry -> slot-relative staging row (clamped into the slot)
+  auto row_of = [&](uint32_t ent) { return std::min<uint32_t>(ent >> 5, (uint32_t)(nrows - 1)); };
+  if (s1 > s0) {
+    // the first block's entries and steps; afterwards each block requests the next block's
+    // entries at its start and their steps after its row loads, so that both have arrived
+    // when the next block starts (all loads unconditional, positions clamped)
+    uint32_t ent = pm[std::min<long long>(s0 + lane, s1 - 1)];
+    float2 st = bstep[(eb + row_of(ent)) >> 4];
+    for (long long r0 = s0; r0 < s1; r0 += 64) {
+      const int n = (int)std::min<long long>(64, s1 - r0);
+      // lanes past the end repeat the last entry and add it with step 0
+      const uint32_t e = row_of(ent);
+      const int kk = (int)(ent & 31u);
+      const float sc = lane < n ? (half ? st.y : st.x) : 0.f;
+      const uint32_t ent_n = pm[std::min<long long>(r0 + 64 + lane, s1 - 1)];
+      uint32_t x[64];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const uint32_t eu = __builtin_amdgcn_readlane(e, u0 + u);
+      for (int u = 0; u < 64; ++u) {
+        const uint32_t eu = __builtin_amdgcn_readlane(e, u);
         // staging rows are read once: non-temporal, so they do not displace other lines
         if constexpr (FPL == 2)
           x[u] = __builtin_nontemporal_load(
@@ -333,10 +334,11 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
         else
           x[u] = (uint16_t)__builtin_nontemporal_load(src + (long long)eu * D);
       }
+      const float2 st_n = bstep[(eb + row_of(ent_n)) >> 4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int ku = __builtin_amdgcn_readlane(kk, u0 + u);
-        const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), u0 + u));
+      for (int u = 0; u < 64; ++u) {
+        const int ku = __builtin_amdgcn_readlane(kk, u);
+        const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), u));
         float* a = acc + ku * D + FPL * lane;
         if constexpr (FPL == 2) {
           float2 w = *reinterpret_cast<float2*>(a);
@@ -347,6 +349,8 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
           a[0] += su * f16_lo(x[u]);
         }
       }
+      ent = ent_n;
+      st = st_n;
     }
   }
   __syncthreads();
