@@ -161,3 +161,16 @@ def test_bwd_chunks_and_profiled_entry_point_validation():
     st = L.dsv_sparse_attn_bwd_profiled(ctypes.byref(pf), *([FAKE] * 7), kf, 0.1, FAKE, FAKE,
                                         FAKE, None, 0, None, ev, 4)
     assert dsv.STATUS[st] == "DSV_ERR_UNSUPPORTED"
+
+
+def test_topk_max_cache_bytes():
+    """Per-slot bytes of the MAX score cache: NG rows of S keys rounded up to 128, 4 bytes
+    each, the total rounded up to 256; a bad problem raises (the C call returns SIZE_MAX)."""
+    al = lambda x: -(-x // 256) * 256
+    for p in (mid(), dsv.problem(2, 3, 4, 8, 8, 64, 16, (2, 2, 4), "bf16"),
+              dsv.problem(1, 2, 3, 8, 12, 64, 16, (1, 4, 4), "fp32")):
+        row = -(-p.seq // 128) * 128
+        assert dsv.topk_max_cache_bytes(p) == al(p.n_groups * row * 4)
+    assert dsv.topk_max_cache_bytes(mid()) == 1024 * 65536 * 4
+    with pytest.raises(ValueError):
+        dsv.topk_max_cache_bytes(dsv.problem(2, 3, 4, 8, 8, 64, 16, (3, 2, 4), "bf16"))
