@@ -62,8 +62,18 @@ def test_mid_topk_fwd_bwd():
     torch.cuda.synchronize()
     _topk_checks(cfg, x, idx)
     o, lse = run_fwd(cfg, x, idx)
-    dq, dk, dv = run_bwd(cfg, x, idx, o, lse)
+    # the launch configuration bench.py times: a workspace of 3x the minimum (two heads per
+    # launch); the default (one head per launch) must give the same bits
+    p = dsv.problem_for(cfg)
+    ws = torch.empty(dsv.workspace_bytes(dsv.DSV_OP_BWD, p, x["k_per_head"]) * 3,
+                     dtype=torch.uint8, device="cuda")
+    dq, dk, dv = dsv.sparse_attn_bwd(p, x["q"], x["k"], x["v"], o, x["do"], lse, idx,
+                                     x["k_per_head"], x["scale"], ws=ws)
+    del ws
+    d1 = run_bwd(cfg, x, idx, o, lse)
     torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip((dq, dk, dv), d1))
+    del d1
     _fwd_sampled(cfg, x, idx, o, lse, n_groups=4)
     mem = members(cfg)
     # dQ on sampled groups of three heads; dK/dV of head 5 over all its groups
