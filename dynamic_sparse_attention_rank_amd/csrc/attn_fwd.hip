@@ -19,7 +19,8 @@
 //     arguments <= 8 and makes rescaling rare. Results are exact regardless of when it is raised.
 //   * The next chunk's rows are requested as soon as the current ones are in registers; every
 //     lane loads the indices of its own row loads one chunk further ahead. Every load in the
-//     loop is unconditional (positions clamped), so the waits for them are exact.
+//     loop is unconditional (positions clamped), so no conditional memory operation makes the
+//     compiler wait early. The tile is read after all of the wave's loads have retired.
 //   * Built with MFMA results in VGPRs: the rare rescale multiplies the O accumulators with
 //     VALU ops, and AGPR accumulators would be copied to VGPRs on every chunk.
 // fp32 path: plain fp32 FMA per lane (one lane per query); it exists for fp32 inputs and is
@@ -144,8 +145,9 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
   const float raise_s = kRaise / c2;
   auto chunk = [&](const int cb, auto tail_tag) {
     constexpr bool kTail = decltype(tail_tag)::value;
-    // this chunk's rows have landed once only the key loads issued after them remain
-    wait_vmcnt<NI>();
+    // this chunk's rows are in LDS once all of the wave's loads have retired (the key loads
+    // issued after them are then in too)
+    wait_vmcnt<0>();
     // ---- operands: K rows 16kb + li (A of S^T = K Q^T, features 32ks + 8lg ..) and V^T
     // (row li <-> feature 16fb + li, slot (lg, e) <-> LDS row 4lg + e (e < 4) or
     // 16 + 4lg + e - 4 (e >= 4)) by transposed reads

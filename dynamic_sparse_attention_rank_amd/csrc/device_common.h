@@ -187,8 +187,9 @@ __device__ __forceinline__ void global_load_lds16(const void* g, void* lds_base)
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
                                    0);
 }
-// Wait until at most N vector memory operations of this wave are outstanding (loads, stores
-// and direct-to-LDS loads retire in issue order), and keep memory accesses on their side.
+// Wait until at most N vector memory operations of this wave are outstanding, and keep memory
+// accesses on their side. Rows brought in by direct-to-LDS loads are read only after N = 0:
+// their retirement order relative to ordinary loads is not relied on.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
