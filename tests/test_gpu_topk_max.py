@@ -87,8 +87,9 @@ def test_topk_max_cached_bit_exact(label, name, over, ks):
 
 @pytest.mark.parametrize("slots", [1, 2, 5, 6])
 def test_topk_max_cache_chunks(slots):
-    """Workspaces for fewer slots than B*H (launches of `slots` slots, the last one short), and
-    one just short of a slot (no cache): bit-identical to the recomputing kernel."""
+    """Workspaces for fewer slots than B*H (launches of `slots` slots, the last one short), one
+    just short of a slot and one not 256-byte aligned (no cache): bit-identical to the
+    recomputing kernel."""
     cfg = workload("small", batch=2, heads=3, frames=4, height=8, width=12, group=(2, 2, 4),
                    rank=32)
     say(f"[topk-max cache chunks] slots={slots}")
@@ -100,6 +101,11 @@ def test_topk_max_cache_chunks(slots):
                            ws=ws)
     short = dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], x["k_per_head"],
                              reduce=dsv.DSV_GROUP_MAX, ws=ws[:dsv.topk_max_cache_bytes(p) - 256])
+    # not 256-byte aligned: the scores are recomputed instead of cached
+    skew = torch.empty(dsv.topk_max_cache_bytes(p) * slots + 64, dtype=torch.uint8, device="cuda")
+    odd = dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], x["k_per_head"], reduce=dsv.DSV_GROUP_MAX,
+                           ws=skew[64:])
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
     assert torch.equal(short, ref)
+    assert torch.equal(odd, ref)
