@@ -190,8 +190,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the DSV hot path is measured on one GPU's share "
-              "of the work (no sharding or collectives in this build); use --gpus 1.",
-              file=sys.stderr)
+              "of the work (the library has no sharded path and makes no collective calls); "
+              "use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
