@@ -123,7 +123,8 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int p = RPI * i + la;
-      const uint32_t off = min(kr.k[i], (uint32_t)geo.S - 1u) * (uint32_t)(2 * D) +
+      // clamped here, a chunk after the key loads were issued, so that they are not waited for
+      const uint32_t off = (uint32_t)clamp_key((int)kr.k[i], geo.S) * (uint32_t)(2 * D) +
                            (uint32_t)((lp ^ (p % GPR)) << 4);
       global_load_lds16(Kb + off, &kvs[0][RPI * i * D]);
       global_load_lds16(Vb + off, &kvs[1][RPI * i * D]);

@@ -285,3 +285,43 @@ def test_bwd_profiled_matches_plain_bitwise():
         assert ms.value >= 0.0
     for e in evs:
         L.hipEventDestroy(e)
+
+
+def test_malformed_index_rows_are_memory_safe():
+    """Index rows with keys outside [0, S), a repeated key and a descending row: the forward
+    follows the clamped lists as listed (against the oracle on the clamped rows, repeats
+    counted twice), dQ of the well-formed and the reordered rows matches the oracle, and every
+    output (dK/dV are unspecified for such lists) is finite."""
+    cfg = workload("small", heads=2, frames=4, height=16, width=16, head_dim=128, rank=32)
+    say("[malformed idx] keys out of range, repeated, descending")
+    x = gpu_inputs(cfg, backward=True, k_per_head=[100, 77])
+    idx = run_topk(cfg, x)
+    torch.cuda.synchronize()
+    p = dsv.problem_for(cfg)
+    S, k0 = cfg.seq, x["k_per_head"][0]
+    h_idx = idx.cpu().numpy().copy()
+    off0 = dsv.idx_row_offset(p, x["k_per_head"], 0, 0, 0)
+    row = lambda g: slice(off0 + g * k0, off0 + (g + 1) * k0)
+    h_idx[row(0)][[3, 10, k0 - 1]] = [-5, S + 7, 2**31 - 1]   # out of range
+    h_idx[row(1)][20:30] = h_idx[row(1)][20]                    # one key ten times
+    h_idx[row(2)] = h_idx[row(2)][::-1].copy()                  # descending
+    bad = torch.from_numpy(h_idx).to(idx.device)
+    o, lse = run_fwd(cfg, x, bad)
+    dq, dk, dv = run_bwd(cfg, x, bad, o, lse)
+    torch.cuda.synchronize()
+    for t in (o, lse, dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    mem = members(cfg)
+    for h in range(cfg.heads):
+        rows = np.clip(gpu_rows(cfg, x, bad, 0, h).astype(np.int64), 0, S - 1)
+        ro, rl = oracle_fwd(cfg, x, rows, 0, h, mem=mem)   # any list: repeats count twice
+        e = (maxerr(f64(o[0, h]), ro), maxerr(f64(lse[0, h]), rl))
+        assert max(e) <= TOL[cfg.dtype], (h, e)
+        # dQ does not depend on the order of a list: the descending row is checked in
+        # ascending order; the rows with out-of-range or repeated keys only for finiteness
+        groups = list(range(2 if h == 0 else 0, cfg.n_groups))
+        rows[2] = np.sort(rows[2])
+        rq, _, _ = oracle_bwd(cfg, x, rows, 0, h, groups=groups, mem=mem)
+        tok = mem[groups].ravel()
+        eq = maxerr(f64(dq[0, h])[tok], rq[tok])
+        assert eq <= TOL[cfg.dtype], (h, eq)
