@@ -379,8 +379,13 @@ def main():
     part, load, rho = dsv.plan_heads(ks, 8, cfg.seq * p.n_groups * cm.topk_ns_per_score * 1e-6,
                                      p.n_groups * cm.attn_ns_per_edge * 1e-6)
     kd_out, n_dense = dsv.dispatch_k(p, ks, cm)
+    mx_tf = member_flop / (mx_ms * 1e-3) / 1e12
     extras = {"topk_max": {"ms": mx_ms, "scores_per_s": scores / (mx_ms * 1e-3),
-                           "member_score_tflops": member_flop / (mx_ms * 1e-3) / 1e12,
+                           "member_score_tflops": mx_tf,
+                           # one S x S x r member-score product per call is the algorithmic
+                           # minimum (the later selection passes reread cached scores)
+                           "roofline": {"bound": "mfma", "achieved": mx_tf, "peak": peak,
+                                        "unit": "TFLOP/s", "frac": mx_tf / peak},
                            "cache_bytes": dsv.topk_max_cache_bytes(p) * cfg.batch * cfg.heads,
                            "ms_recomputing_scores": mx_re_ms},
               "adaptive_k": {"ms": ak_ms, "mass": 0.9,
