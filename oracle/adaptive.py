@@ -8,66 +8,61 @@ those that contribute more than 90 % of the attention score.
 Readings (the pages give no formula):
   * a group's estimated logits are logit_scale * sigma[g][m], sigma the group score of the
     top-k estimator (SUM over members); logit_scale = scale / G is the mean member logit;
-  * the mass of a key is its softmax weight; k is found from a histogram of the logits below
-    the group maximum (bins of 1/4 logit unit, 128 bins, the last one open-ended), each key of
-    bin b weighted exp(-(b + 1/2)/4) (the last bin exp(-127/4)), accumulated in bin order;
+  * the attention mass of key m is its softmax weight over all S keys of the row;
+  * a group's k is the smallest number of keys whose weights, largest first, reach `mass`
+    of the row's total weight (the "critical" keys carry that share of the score);
   * the head's k is the largest k of its groups over the batch.
-The histogram is the exact object; only the weights are binned. `exact_k` (a full sort of the
-true softmax weights) pins it within the bin width.
+
+Everything is float64. The weights are exp(logit_scale * (sigma - max sigma)) (the common
+factor exp(-max) cancels), the total and the prefix sums are exactly rounded (math.fsum).
+`k_bracket` widens the decision by an absolute band on the prefix sums: it returns every k
+that a computation of the same rule whose sums are within `band` of these would return.
 """
 from __future__ import annotations
 
 import math
-from typing import List, Sequence
+from typing import Tuple
 
 import numpy as np
 
-BINS = 128
-PER_NAT = 4
+
+def softmax_weights(sigma_row: np.ndarray, logit_scale: float) -> np.ndarray:
+    """exp(logit_scale * (sigma_m - max sigma)) for every key of the row (fp64, max weight 1)."""
+    s = np.asarray(sigma_row, dtype=np.float64)
+    return np.exp(float(logit_scale) * (s - s.max()))
 
 
-def bin_weights() -> List[float]:
-    w = [math.exp(-(b + 0.5) / PER_NAT) for b in range(BINS - 1)]
-    w.append(math.exp(-(BINS - 1) / PER_NAT))
-    return w
+def _sorted_desc(w: np.ndarray) -> np.ndarray:
+    return np.sort(w)[::-1]
 
 
-def group_bin_counts(sigma_row: np.ndarray, logit_scale: float) -> np.ndarray:
-    """Histogram of a group's keys over the logit gap below the maximum. The gap and its
-    product with 4 * logit_scale are taken in fp32, as the kernel does."""
-    s = np.asarray(sigma_row, dtype=np.float32)
-    M = s.max()
-    tau_r = np.float32(logit_scale) * np.float32(PER_NAT)
-    x = (M - s) * tau_r                      # fp32 subtract, then fp32 multiply
-    b = np.where(x < np.float32(BINS - 1), np.floor(x), BINS - 1).astype(np.int64)
-    return np.bincount(b, minlength=BINS)
-
-
-def k_from_counts(counts: Sequence[int], mass: float, w: Sequence[float]) -> int:
-    """Running softmax mass in bin order (fp64, one operation at a time)."""
-    z = 0.0
-    for c, wb in zip(counts, w):
-        z = z + float(c) * wb
-    target = mass * z
-    cum, n = 0.0, 0
-    for c, wb in zip(counts, w):
-        nxt = cum + float(c) * wb
-        if c != 0 and nxt >= target:
-            need = math.ceil((target - cum) / wb)
-            return max(n + min(need, int(c)), 1)
-        cum, n = nxt, n + int(c)
-    return max(n, 1)
-
-
-def group_k(sigma_row: np.ndarray, logit_scale: float, mass: float) -> int:
-    return k_from_counts(group_bin_counts(sigma_row, logit_scale), mass, bin_weights())
+def _first_reaching(wd: np.ndarray, target: float) -> int:
+    """Smallest n >= 1 with fsum(wd[:n]) >= target (wd descending; len(wd) if none)."""
+    S = wd.shape[0]
+    c = np.cumsum(wd)                        # an estimate; corrected with exact sums below
+    n = min(int(np.searchsorted(c, target)) + 1, S)
+    pre = lambda j: math.fsum(wd[:j])       # noqa: E731 — exactly rounded prefix sum
+    while n > 1 and pre(n - 1) >= target:
+        n -= 1
+    while n < S and pre(n) < target:
+        n += 1
+    return n
 
 
 def exact_k(sigma_row: np.ndarray, logit_scale: float, mass: float) -> int:
-    """Smallest number of keys whose true softmax weights (largest first) reach `mass` of the
-    total, by a full sort in fp64."""
-    s = np.asarray(sigma_row, dtype=np.float64) * logit_scale
-    p = np.exp(s - s.max())
-    p = np.sort(p)[::-1]
-    c = np.cumsum(p)
-    return int(np.searchsorted(c, mass * c[-1] * (1 - 1e-15)) + 1)
+    """Smallest number of keys whose softmax weights (largest first) reach `mass` of the
+    row's total weight."""
+    w = softmax_weights(sigma_row, logit_scale)
+    wd = _sorted_desc(w)
+    return _first_reaching(wd, mass * math.fsum(w))
+
+
+def k_bracket(sigma_row: np.ndarray, logit_scale: float, mass: float,
+              band: float) -> Tuple[int, int]:
+    """(k_lo, k_hi): the smallest counts whose prefix sums reach mass * total - band and
+    mass * total + band. exact_k lies in between, and so does the k of any evaluation of the
+    rule whose prefix sums and target are each within band / 2 of the exact ones."""
+    w = softmax_weights(sigma_row, logit_scale)
+    wd = _sorted_desc(w)
+    target = mass * math.fsum(w)
+    return _first_reaching(wd, target - band), _first_reaching(wd, target + band)

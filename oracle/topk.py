@@ -18,11 +18,6 @@ from __future__ import annotations
 import numpy as np
 
 
-def per_query_scores(q_lr: np.ndarray, k_lr: np.ndarray) -> np.ndarray:
-    """u[n, m] = sum_c Q_lr[n, c] K_lr[m, c] for every query n and key m ([S, S], fp64)."""
-    return np.asarray(q_lr, dtype=np.float64) @ np.asarray(k_lr, dtype=np.float64).T
-
-
 def group_scores_bruteforce(q_lr: np.ndarray, k_lr: np.ndarray, members: np.ndarray) -> np.ndarray:
     """sigma[g, m] = sum_{n in g} u[n, m], with u the per-query scores ([NG, S], fp64).
 
