@@ -27,7 +27,7 @@ EXPORTED = ("dsv_workspace_bytes", "dsv_idx_elems", "dsv_idx_row_offset", "dsv_l
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd", "dsv_bwd_chunks",
             "dsv_sparse_attn_bwd_profiled", "dsv_validate", "dsv_status_string",
             "dsv_last_error", "dsv_version", "dsv_plan_heads", "dsv_default_cost_model",
-            "dsv_dispatch_k", "dsv_adaptive_k", "dsv_topk_max_cache_bytes")
+            "dsv_dispatch_k", "dsv_adaptive_k", "dsv_topk_max_cache_bytes", "dsv_plan_order")
 
 
 class DsvError(RuntimeError):
@@ -105,6 +105,8 @@ def lib() -> ctypes.CDLL:
         dp = ctypes.POINTER(ctypes.c_double)
         L.dsv_plan_heads.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
                                      ctypes.c_double, i32p, dp, dp]
+        L.dsv_plan_order.argtypes = [i32p, ctypes.c_int32, ctypes.c_double, ctypes.c_double,
+                                     i32p]
         L.dsv_default_cost_model.argtypes = [P, ctypes.c_int, ctypes.POINTER(CostModel)]
         L.dsv_dispatch_k.argtypes = [P, i32p, ctypes.POINTER(CostModel), i32p, i32p]
         L.dsv_adaptive_k.argtypes = [P, vp, vp, f, ctypes.c_double, vp, vp, vp]
@@ -114,7 +116,8 @@ def lib() -> ctypes.CDLL:
         L.dsv_version.restype = ctypes.c_char_p
         for fn in ("dsv_lowrank_topk", "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd",
                    "dsv_sparse_attn_bwd_profiled", "dsv_validate", "dsv_plan_heads",
-                   "dsv_default_cost_model", "dsv_dispatch_k", "dsv_adaptive_k"):
+                   "dsv_default_cost_model", "dsv_dispatch_k", "dsv_adaptive_k",
+                   "dsv_plan_order"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -171,6 +174,17 @@ def plan_heads(k_per_head: Sequence[int], n_parts: int, fixed_cost: float = 0.0,
     return list(part)[:H], list(load)[:n_parts], rho.value
 
 
+def plan_order(k_per_head: Sequence[int], fixed_cost: float = 0.0,
+               cost_per_k: float = 1.0) -> List[int]:
+    """Heads in the planner's processing order (decreasing cost, ties to the lower head); with
+    the defaults, the order in which the kernels launch the heads of a problem."""
+    H = len(k_per_head)
+    out = (ctypes.c_int32 * max(H, 1))()
+    _check(lib().dsv_plan_order(_kph(k_per_head), H, float(fixed_cost), float(cost_per_k),
+                                out))
+    return list(out)[:H]
+
+
 def default_cost_model(p: Problem, with_backward: bool = True) -> CostModel:
     """Measured MI355X per-unit costs of this library's kernels, scaled to the problem."""
     cm = CostModel()
@@ -195,10 +209,13 @@ def _torch():
     return torch
 
 
-def _stream_ptr(stream) -> int:
+def _stream(stream):
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return int(s.cuda_stream)
+    return stream if stream is not None else torch.cuda.current_stream()
+
+
+def _stream_ptr(stream) -> int:
+    return int(_stream(stream).cuda_stream)
 
 
 def _dev(t, name, dtype=None, shape=None):
@@ -230,8 +247,9 @@ def lowrank_topk(p: Problem, q_lr, k_lr, k_per_head: Sequence[int], idx=None,
     qp = _dev(q_lr, "q_lr", dt, shp)
     kp = _dev(k_lr, "k_lr", dt, shp)
     n = idx_elems(p, k_per_head)
-    if idx is None:
-        idx = torch.zeros(max(n, 1), dtype=torch.int32, device=q_lr.device)
+    if idx is None:   # allocated on the launch stream: the caching allocator orders its reuse
+        with torch.cuda.stream(_stream(stream)):
+            idx = torch.empty(max(n, 1), dtype=torch.int32, device=q_lr.device)
     ip = _dev(idx, "idx", torch.int32)
     if idx.numel() < n:
         raise ValueError("idx is too small")
@@ -264,11 +282,12 @@ def adaptive_k(p: Problem, q_lr, k_lr, mass: float = 0.9, logit_scale: Optional[
     kp = _dev(k_lr, "k_lr", dt, shp)
     if logit_scale is None:
         logit_scale = 1.0 / (math.sqrt(p.head_dim) * p.group_size)
-    if k_group is None:
-        k_group = torch.empty((p.batch, p.heads, p.n_groups), dtype=torch.int32,
-                              device=q_lr.device)
+    with torch.cuda.stream(_stream(stream)):   # outputs belong to the launch stream
+        if k_group is None:
+            k_group = torch.empty((p.batch, p.heads, p.n_groups), dtype=torch.int32,
+                                  device=q_lr.device)
+        k_head = torch.empty(p.heads, dtype=torch.int32, device=q_lr.device)
     gp = _dev(k_group, "k_group", torch.int32, (p.batch, p.heads, p.n_groups))
-    k_head = torch.empty(p.heads, dtype=torch.int32, device=q_lr.device)
     _check(lib().dsv_adaptive_k(ctypes.byref(p), qp, kp, float(logit_scale), float(mass), gp,
                                 k_head.data_ptr(), _stream_ptr(stream)))
     return k_head, k_group
@@ -286,10 +305,11 @@ def sparse_attn_fwd(p: Problem, q, k, v, idx, k_per_head: Sequence[int],
            _dev(idx, "idx", torch.int32)]
     if idx.numel() < idx_elems(p, k_per_head):
         raise ValueError("idx is too small")
-    if o is None:
-        o = torch.empty(shp, dtype=dt, device=q.device)
-    if lse is None:
-        lse = torch.empty(shp[:3], dtype=torch.float32, device=q.device)
+    with torch.cuda.stream(_stream(stream)):   # outputs belong to the launch stream
+        if o is None:
+            o = torch.empty(shp, dtype=dt, device=q.device)
+        if lse is None:
+            lse = torch.empty(shp[:3], dtype=torch.float32, device=q.device)
     op = _dev(o, "o", dt, shp)
     lp = _dev(lse, "lse", torch.float32, shp[:3])
     _check(lib().dsv_sparse_attn_fwd(ctypes.byref(p), ptr[0], ptr[1], ptr[2], ptr[3],
@@ -322,14 +342,18 @@ def sparse_attn_bwd(p: Problem, q, k, v, o, d_o, lse, idx, k_per_head: Sequence[
     if idx.numel() < idx_elems(p, k_per_head):
         raise ValueError("idx is too small")
     outs = []
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if t is None:
-            t = torch.empty(shp, dtype=torch.float32, device=q.device)
-        _dev(t, name, torch.float32, shp)
-        outs.append(t)
     need = workspace_bytes(DSV_OP_BWD, p, k_per_head)
-    if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+    # Outputs and the call's own workspace are allocated on the launch stream: the caching
+    # allocator then hands the workspace to nothing else until that stream has passed the
+    # call, although it is dropped when this function returns.
+    with torch.cuda.stream(_stream(stream)):
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            if t is None:
+                t = torch.empty(shp, dtype=torch.float32, device=q.device)
+            _dev(t, name, torch.float32, shp)
+            outs.append(t)
+        if ws is None and need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=q.device)
     wp = _dev(ws, "ws", torch.uint8) if ws is not None else None
     wn = ws.numel() if ws is not None else 0
     args = (ctypes.byref(p), *ptr[:6], ptr[6], _kph(k_per_head), float(scale),

@@ -76,10 +76,11 @@ int validate_problem(const dsv_problem* p, const int32_t* kph, Geom* geo) {
       g.pre[h] = acc;
       acc += kph[h];
     }
-    int ord[kMaxHeads];
-    std::iota(ord, ord + p->heads, 0);
-    std::stable_sort(ord, ord + p->heads, [&](int a, int b) { return kph[a] > kph[b]; });
-    for (int h = 0; h < p->heads; ++h) g.order[h] = ord[h];
+    // heads launch in the planner's order for a single device: the attention's cost per
+    // head grows with k_h, so heavy heads go first (longest processing time first)
+    double cost[kMaxHeads];
+    for (int h = 0; h < p->heads; ++h) cost[h] = (double)kph[h];
+    lpt_order(cost, p->heads, g.order);
   }
   return DSV_OK;
 }
@@ -88,6 +89,14 @@ static int check_ptr(const void* ptr, const char* name, size_t align) {
   if (!ptr) return fail(DSV_ERR_NULL, "%s is NULL", name);
   if (reinterpret_cast<uintptr_t>(ptr) % align)
     return fail(DSV_ERR_ALIGN, "%s is not %zu-byte aligned", name, align);
+  return DSV_OK;
+}
+
+// The kernels keep the running maximum on raw scores q.k, which orders logits only for a
+// positive scale.
+static int check_scale(float scale) {
+  if (!(scale > 0.0f) || !isfinite(scale))
+    return fail(DSV_ERR_SHAPE, "scale = %g: it must be positive and finite", (double)scale);
   return DSV_OK;
 }
 
@@ -212,10 +221,9 @@ int dsv_adaptive_k(const dsv_problem* p, const void* q_lr, const void* k_lr, flo
     return fail(DSV_ERR_SHAPE, "logit_scale must be positive and finite");
   if (!(mass > 0.0 && mass <= 1.0)) return fail(DSV_ERR_SHAPE, "mass must be in (0, 1]");
   AdaptiveParams ap;
-  for (int b = 0; b < AK_BINS - 1; ++b) ap.w[b] = exp(-((double)b + 0.5) / AK_BINS_PER_NAT);
-  ap.w[AK_BINS - 1] = exp(-(double)(AK_BINS - 1) / AK_BINS_PER_NAT);
+  ap.ls = (double)logit_scale;
+  ap.fx = ldexp(1.0, adaptive_fx_bits(geo.S));
   ap.mass = mass;
-  ap.tau_r = logit_scale * (float)AK_BINS_PER_NAT;
   const int e = launch_adaptive_k(geo, q_lr, k_lr, ap, k_group, k_head, stream);
   if (e) return fail(DSV_ERR_HIP, "adaptive-k launch failed (hipError %d)", e);
   return DSV_OK;
@@ -228,6 +236,7 @@ int dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, cons
   const void* ptrs[] = {q, k, v, idx, o, lse};
   int st = dsv_validate(DSV_OP_FWD, p, k_per_head, DSV_GROUP_SUM, ptrs, 6, ws_bytes);
   if (st != DSV_OK) return st;
+  if ((st = check_scale(scale)) != DSV_OK) return st;
   Geom geo;
   validate_problem(p, k_per_head, &geo);
   int e = launch_attn_fwd(geo, q, k, v, idx, scale, o, lse, stream);
@@ -243,6 +252,7 @@ static int bwd_common(const dsv_problem* p, const void* q, const void* k, const 
   const void* ptrs[] = {q, k, v, o, d_o, lse, idx, dq, dk, dv};
   int st = dsv_validate(DSV_OP_BWD, p, k_per_head, DSV_GROUP_SUM, ptrs, 10, ws_bytes);
   if (st != DSV_OK) return st;
+  if ((st = check_scale(scale)) != DSV_OK) return st;
   Geom geo;
   validate_problem(p, k_per_head, &geo);
   if (bwd_workspace_bytes(geo) > 0 && (st = check_ptr(ws, "ws", 256)) != DSV_OK) return st;

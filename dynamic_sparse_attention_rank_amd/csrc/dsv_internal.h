@@ -23,7 +23,7 @@ struct Geom {
   long long ksum;            // sum_h k_h
   int k[kMaxHeads];          // k_h
   long long pre[kMaxHeads];  // sum_{h'<h} k_h'
-  int order[kMaxHeads];      // heads by decreasing k (stable): heavy heads are launched first
+  int order[kMaxHeads];      // launch order: the planner's order for one device (cost ~ k_h)
 
   // Start of row (b, h, g) in the packed idx array.
   DSV_HD inline long long row_offset(int b, int h, int g) const {
@@ -31,18 +31,27 @@ struct Geom {
   }
 };
 
+// The planner's processing order (dsv_plan.cpp): heads by decreasing cost, equal costs by
+// lower head index. With one device it is also the order in which the kernels launch heads.
+void lpt_order(const double* cost, int n, int* order);
+
 // Validation (HIP-free). Fills `geo` when the problem is valid.
 int validate_problem(const dsv_problem* p, const int32_t* k_per_head, Geom* geo);
 void set_error(const char* fmt, ...);
 
-// Adaptive k: bins of the estimated logit below a group's maximum, and their softmax weights.
-constexpr int AK_BINS = 128;
-constexpr int AK_BINS_PER_NAT = 4;
+// Adaptive k: per-key softmax weights exp(ls * (sigma - max)) in fp64, rounded to integer
+// multiples of 1 / fx (fx = 2^P, P = 62 - bit length of S, so a whole row sums below 2^63).
 struct AdaptiveParams {
-  double w[AK_BINS];   // weight of bin b: exp(-(b + 1/2) / 4), the last bin exp(-(AK_BINS-1)/4)
-  double mass;         // share of the mass the group's k keys must carry, in (0, 1]
-  float tau_r;         // logit_scale * AK_BINS_PER_NAT, rounded to fp32
+  double ls;     // logit scale (the caller's fp32 value)
+  double fx;     // 2^P
+  double mass;   // share of the row's weight the group's k keys must carry, in (0, 1]
 };
+// Fixed-point exponent P of the adaptive-k weights for a row of S keys.
+inline int adaptive_fx_bits(int S) {
+  int bl = 0;
+  while (bl < 31 && (1u << bl) <= (unsigned)S) ++bl;   // bit length of S
+  return 62 - bl;
+}
 
 // Kernel launchers (one per translation unit). Return 0 or a hipError_t value.
 // reduce = MAX uses ws (when 256-byte aligned and at least one slot's worth) to keep the group

@@ -9,9 +9,42 @@
 
 #include "dsv_internal.h"
 
+namespace dsv {
+
+// Longest-processing-time order: heads by decreasing cost, equal costs by lower head index.
+void lpt_order(const double* cost, int n, int* order) {
+  std::iota(order, order + n, 0);
+  std::stable_sort(order, order + n, [&](int a, int b) { return cost[a] > cost[b]; });
+}
+
+}  // namespace dsv
+
 using namespace dsv;
 
 extern "C" {
+
+int dsv_plan_order(const int32_t* k_per_head, int32_t heads, double fixed_cost,
+                   double cost_per_k, int32_t* order) {
+  if (!k_per_head || !order) {
+    set_error("k_per_head and order must not be NULL");
+    return DSV_ERR_NULL;
+  }
+  if (heads <= 0) {
+    set_error("heads = %d must be positive", heads);
+    return DSV_ERR_SHAPE;
+  }
+  if (!(fixed_cost >= 0.0) || !(cost_per_k >= 0.0) || !isfinite(fixed_cost) ||
+      !isfinite(cost_per_k)) {
+    set_error("costs must be finite and non-negative");
+    return DSV_ERR_SHAPE;
+  }
+  std::vector<double> cost(heads);
+  for (int h = 0; h < heads; ++h) cost[h] = fixed_cost + cost_per_k * (double)k_per_head[h];
+  std::vector<int> o(heads);
+  lpt_order(cost.data(), heads, o.data());
+  for (int i = 0; i < heads; ++i) order[i] = o[i];
+  return DSV_OK;
+}
 
 int dsv_plan_heads(const int32_t* k_per_head, int32_t heads, int32_t n_parts, double fixed_cost,
                    double cost_per_k, int32_t* part_of_head, double* part_load, double* rho) {
@@ -36,8 +69,7 @@ int dsv_plan_heads(const int32_t* k_per_head, int32_t heads, int32_t n_parts, do
   std::vector<double> cost(heads);
   for (int h = 0; h < heads; ++h) cost[h] = fixed_cost + cost_per_k * (double)k_per_head[h];
   std::vector<int> order(heads);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return cost[a] > cost[b]; });
+  lpt_order(cost.data(), heads, order.data());
   std::vector<double> load(n_parts, 0.0);
   for (int h : order) {
     int best = 0;

@@ -427,12 +427,20 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
 
 // ---- adaptive k (the "critical KV pairs carry a given share of the attention mass" rule)
 //
-// Per group: the group scores' maximum M, then a histogram of its keys over AK_BINS bins of the
-// estimated logit below the maximum, bin = floor((M - sigma) * tau_r) (fp32, clamped to the last
-// bin), where tau_r = logit_scale * bins per nat. One lane per group then accumulates, in bin
-// order and in fp64, the softmax weights count[b] * w[b] (w from the host) and finds the first
-// bin at which the running mass reaches `mass` times the total; k is the keys of the earlier
-// bins plus the number of that bin's keys (at weight w[b]) still needed, at least 1.
+// A group's k is the smallest number of keys whose softmax weights w_m = exp(ls (sigma_m - M))
+// (M = the group's largest score), largest first, reach `mass` of the row's total weight. The
+// largest weights belong to the largest scores, so the keys are taken in score order and the
+// answer is found by the same radix walk over the order-preserving score image as the top-k:
+// every digit bin carries its keys' count and the sum of their weights, each weight evaluated
+// in fp64 and rounded to a fixed-point integer u = rint(w 2^P) (P from the host so that a whole
+// row sums below 2^63). Integer sums do not depend on the order of the atomics, so the result
+// is reproducible bit for bit. Pass 0 (every key) gives the row total Z and the target
+// ceil(mass Z); each pass keeps the bin in which the running sum from the top reaches it. When
+// that bin holds a single score value T (its keys have no bits below the digit, or all 32 bits
+// are fixed), j = ceil((target - sum above T) / u_T) of its keys are needed and k = (keys above
+// T) + j.
+constexpr int AK_STRIDE = 257;   // 256 bins + 1 pad word per group
+
 template <bool F32, int R>
 __global__ __launch_bounds__(TK_THREADS) void adaptive_k_kernel(const void* __restrict__ qlr_,
                                                                 const void* __restrict__ klr_,
@@ -442,11 +450,19 @@ __global__ __launch_bounds__(TK_THREADS) void adaptive_k_kernel(const void* __re
                                                                 Geom geo) {
   using C = TopkCfg<F32, R>;
   static_assert(TK_SUMW * 64 * C::NF <= TK_GROUPS * TK_HSTRIDE, "partial sums overflow");
-  static_assert(AK_BINS + 1 <= TK_HSTRIDE, "bins overflow");
-  __shared__ uint32_t hist[TK_GROUPS * TK_HSTRIDE];   // also the group sums' partials, first
-  __shared__ uint32_t st_max[TK_GROUPS];               // order-preserving image of the maximum
+  __shared__ unsigned long long hmass[TK_GROUPS * AK_STRIDE];   // summed fixed-point weights
+  __shared__ uint32_t hcnt[TK_GROUPS * TK_HSTRIDE];   // counts; the group sums' partials first
+  __shared__ uint32_t st_max[TK_GROUPS];              // order-preserving image of the maximum
+  __shared__ uint32_t st_prefix[TK_GROUPS];
+  __shared__ int st_npass[TK_GROUPS];                 // as in topk_kernel
+  __shared__ uint32_t st_lowbits[TK_GROUPS];
+  __shared__ unsigned long long st_above[TK_GROUPS];  // weight of the keys above the prefix
+  __shared__ uint32_t st_nabove[TK_GROUPS];           // and their number
+  __shared__ unsigned long long st_target[TK_GROUPS];
+  __shared__ int st_active[4];
 
   const int tid = threadIdx.x;
+  const int kw = tid >> 6;
   const int lane = tid & 63;
   const int g = lane & 31;
   int b, h, gblock;
@@ -455,9 +471,18 @@ __global__ __launch_bounds__(TK_THREADS) void adaptive_k_kernel(const void* __re
   const int S = geo.S;
 
   ScoreStream<F32, R> ss;
-  ss.init(geo, qlr_, klr_, b * geo.H + h, my_group, reinterpret_cast<float*>(hist));
-  for (int i = tid; i < TK_GROUPS * TK_HSTRIDE; i += TK_THREADS) hist[i] = 0;
-  for (int i = tid; i < TK_GROUPS; i += TK_THREADS) st_max[i] = 0;
+  ss.init(geo, qlr_, klr_, b * geo.H + h, my_group, reinterpret_cast<float*>(hcnt));
+  for (int i = tid; i < TK_GROUPS * AK_STRIDE; i += TK_THREADS) hmass[i] = 0ull;
+  for (int i = tid; i < TK_GROUPS * TK_HSTRIDE; i += TK_THREADS) hcnt[i] = 0u;
+  for (int i = tid; i < TK_GROUPS; i += TK_THREADS) {
+    st_max[i] = 0u;
+    st_prefix[i] = 0u;
+    st_lowbits[i] = 0u;
+    st_above[i] = 0ull;
+    st_nabove[i] = 0u;
+    st_target[i] = 0ull;
+    st_npass[i] = (gblock * TK_GROUPS + i < geo.NG) ? 0 : -1;
+  }
   __syncthreads();
 
   // ---- the maximum of every group's scores
@@ -478,49 +503,133 @@ __global__ __launch_bounds__(TK_THREADS) void adaptive_k_kernel(const void* __re
   __hip_atomic_fetch_max(&st_max[g], score_key(mx), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_WORKGROUP);
   __syncthreads();
-  const uint32_t mk = st_max[g];
-  const float M = __uint_as_float(mk ^ ((mk & 0x80000000u) ? 0x80000000u : 0xffffffffu));
 
-  // ---- histogram of the logit gap below the maximum
-  uint32_t* const hrow = &hist[g * TK_HSTRIDE];
-  const float tau_r = ap.tau_r;
-  ss.walk([&](const floatx16& acc, int t, auto tail_tag) {
-    constexpr bool kTail = decltype(tail_tag)::value;
-    const int mb = t * TK_TILE + 32 * ss.kw + 4 * ss.hh;
+  // fixed-point weight of score s in a group with maximum m (fp64, explicit roundings: the
+  // bins and the final step must see the very same integer for equal scores)
+  auto weight_fx = [&](float s, double m) -> unsigned long long {
+    const double w = exp(__dmul_rn(ap.ls, __dsub_rn((double)s, m)));
+    return (unsigned long long)rint(__dmul_rn(w, ap.fx));
+  };
+  const double M64 = (double)key_float(st_max[g]);
+
+  // ---- radix passes with weighted bins
+  for (int pass = 0; pass < 4; ++pass) {
+    if (tid == 0) {
+      int act = 0;
+      for (int i = 0; i < TK_GROUPS; ++i) act |= (st_npass[i] == pass);
+      st_active[pass] = act;
+    }
+    __syncthreads();
+    if (!st_active[pass]) continue;   // uniform
+    const int dshift = 24 - 8 * pass;
+    const int pshift = 32 - 8 * pass;
+    const unsigned long long pfx = st_prefix[g];
+    const bool act = st_npass[g] == pass;
+    // after pass 0: the scores whose keys carry the prefix are those in [lo, hi)
+    const float lo = key_lower_bound(pfx << (pshift & 31));
+    const float hi = key_upper_bound((pfx + 1) << (pshift & 31));
+    uint32_t* const crow = &hcnt[g * TK_HSTRIDE];
+    unsigned long long* const mrow = &hmass[g * AK_STRIDE];
+    uint32_t lowor = 0;
+    ss.walk([&](const floatx16& acc, int t, auto tail_tag) {
+      constexpr bool kTail = decltype(tail_tag)::value;
+      const int mb = t * TK_TILE + 32 * ss.kw + 4 * ss.hh;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float x = __fmul_rn(__fsub_rn(M, acc[e]), tau_r);
-      const uint32_t bin = x < (float)(AK_BINS - 1) ? (uint32_t)x : (uint32_t)(AK_BINS - 1);
-      bool take = true;
-      if constexpr (kTail) take = mb + 8 * (e >> 2) + (e & 3) < S;
-      if (take)
-        __hip_atomic_fetch_add(&hrow[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-  });
-  __syncthreads();
-
-  // ---- one lane per group: softmax-weighted cumulative mass in bin order (fp64, no fusion)
-  if (tid < TK_GROUPS && my_group < geo.NG) {
-    double z = 0.0;
-    for (int bb = 0; bb < AK_BINS; ++bb) z = __dadd_rn(z, __dmul_rn((double)hrow[bb], ap.w[bb]));
-    const double target = __dmul_rn(ap.mass, z);
-    double cum = 0.0;
-    long long n = 0;
-    long long k = S;
-    for (int bb = 0; bb < AK_BINS; ++bb) {
-      const double c = __dmul_rn((double)hrow[bb], ap.w[bb]);
-      const double nxt = __dadd_rn(cum, c);
-      if (hrow[bb] != 0u && nxt >= target) {
-        const double need = ceil(__ddiv_rn(__dsub_rn(target, cum), ap.w[bb]));
-        k = n + (long long)fmin(need, (double)hrow[bb]);
-        break;
+      for (int e = 0; e < 16; ++e) {
+        bool take = act;
+        if constexpr (kTail) take = take && mb + 8 * (e >> 2) + (e & 3) < S;
+        if (pass > 0) take = take && acc[e] >= lo && acc[e] < hi;
+        if (take) {
+          const uint32_t key = score_key(acc[e]);
+          const uint32_t d = (key >> dshift) & 255u;
+          __hip_atomic_fetch_add(&crow[d], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_add(&mrow[d], weight_fx(acc[e], M64), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+          lowor |= key;
+        }
       }
-      cum = nxt;
-      n += hrow[bb];
+    });
+    // pass 0 does not track the low bits (its bins are never final)
+    if (pass == 0 || (lowor & ((1u << dshift) - 1u)) != 0) st_lowbits[g] = 1u;
+    __syncthreads();
+
+    // Each wave resolves some of the groups: bins from the top, running sums by a wave scan.
+    for (int gl = kw; gl < TK_GROUPS; gl += TK_KW) {
+      if (st_npass[gl] != pass) continue;   // uniform across the wave
+      unsigned long long m[4], msum = 0ull;
+      uint32_t c[4], csum = 0u;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int bin = 255 - (4 * lane + tt);
+        m[tt] = hmass[gl * AK_STRIDE + bin];
+        c[tt] = hcnt[gl * TK_HSTRIDE + bin];
+        msum += m[tt];
+        csum += c[tt];
+      }
+      unsigned long long mincl = msum;
+      uint32_t cincl = csum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned long long x = __shfl_up(mincl, off, 64);
+        const uint32_t y = __shfl_up(cincl, off, 64);
+        if (lane >= off) {
+          mincl += x;
+          cincl += y;
+        }
+      }
+      unsigned long long target = st_target[gl];
+      if (pass == 0) {   // the row total; the target never exceeds it
+        const unsigned long long Z = __shfl(mincl, 63, 64);
+        const double tz = ceil(__dmul_rn(ap.mass, (double)Z));
+        target = tz >= (double)Z ? Z : (unsigned long long)tz;
+      }
+      const unsigned long long above = st_above[gl];
+      const uint32_t nabove = st_nabove[gl];
+      const uint32_t pfx_gl = st_prefix[gl];
+      const bool lowbits = st_lowbits[gl] != 0u;
+      const uint32_t mkey = st_max[gl];
+      wave_lds_fence();   // every lane has read the state before one lane rewrites it
+      unsigned long long mex = mincl - msum;
+      uint32_t cex = cincl - csum;
+      if (above + mex < target && target <= above + mincl) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (above + mex + m[tt] >= target) {
+            const uint32_t bin = 255u - (4u * lane + tt);
+            const uint32_t npfx = pass == 0 ? bin : ((pfx_gl << 8) | bin);
+            const unsigned long long nabove_m = above + mex;
+            const uint32_t nabove_c = nabove + cex;
+            if (pass == 3 || !lowbits) {
+              // one score value T remains: the keys of the bin are all equal to it
+              const uint32_t tkey = npfx << (24 - 8 * pass);
+              const unsigned long long uT = weight_fx(key_float(tkey), (double)key_float(mkey));
+              const unsigned long long j = (target - nabove_m + uT - 1ull) / uT;
+              const int kg = (int)max(1ull, (unsigned long long)nabove_c + j);
+              const int grp = gblock * TK_GROUPS + gl;
+              if (k_group) k_group[((long long)b * geo.H + h) * geo.NG + grp] = kg;
+              atomicMax(&k_head[h], kg);
+              st_npass[gl] = 16 + pass + 1;
+            } else {
+              st_prefix[gl] = npfx;
+              st_above[gl] = nabove_m;
+              st_nabove[gl] = nabove_c;
+              st_npass[gl] = pass + 1;
+            }
+            break;
+          }
+          mex += m[tt];
+          cex += c[tt];
+        }
+      }
+      if (pass == 0 && lane == 0) st_target[gl] = target;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        hmass[gl * AK_STRIDE + 4 * lane + tt] = 0ull;
+        hcnt[gl * TK_HSTRIDE + 4 * lane + tt] = 0u;
+      }
+      if (lane == 0) st_lowbits[gl] = 0u;
     }
-    const int kg = (int)max(k, 1LL);
-    if (k_group) k_group[((long long)b * geo.H + h) * geo.NG + my_group] = kg;
-    atomicMax(&k_head[h], kg);
+    __syncthreads();
   }
 }
 

@@ -132,20 +132,23 @@ size_t dsv_topk_max_cache_bytes(const dsv_problem* p);
  * estimate of QK^T identifies the KV pairs that contribute more than 90% of the attention
  * score; pt §2A, fr §2A, ko §2가.)
  *   q_lr, k_lr  : as for dsv_lowrank_topk (group scores sigma[g][m], SUM reduction).
- *   logit_scale : > 0; the estimated logit of key m for group g is logit_scale * sigma[g][m]
- *                 (scale / G makes it the mean of the members' scaled low-rank logits).
+ *   logit_scale : > 0 and finite; the estimated logit of key m for group g is
+ *                 logit_scale * sigma[g][m] (scale / G makes it the mean of the members'
+ *                 scaled low-rank logits).
  *   mass        : in (0, 1], e.g. 0.9.
  *   k_group     : device int32 [B][H][NG] or NULL, written: k of every group.
- *   k_head      : device int32 [H], written: the largest k of the head's groups over the batch,
- *                 i.e. a k_per_head for which every group's keys carry at least `mass`.
- * Per group, from a histogram rather than a sort: with M the largest group score, key m falls
- * in bin b = min(floor(fp32((M - sigma[m]) * fp32(4 * logit_scale))), 127), i.e. bins of a
- * quarter of a logit unit below the maximum (the last bin holds the rest). Bin b carries the
- * softmax weight w_b = exp(-(b + 1/2)/4) per key (the last bin exp(-127/4)). In fp64 and in
- * bin order: Z = sum_b count_b w_b; the first non-empty bin b* at which the running sum reaches
- * mass * Z gives k = (keys in bins < b*) + min(count_b*, ceil((mass * Z - running sum before
- * b*) / w_b*)), at least 1. Counts are exact and the fp64 sums run in a fixed order, so the
- * result is reproducible bit for bit. Launches on `stream`; no workspace. */
+ *   k_head      : device int32 [H], written: the largest k of the head's groups over the batch.
+ * A group's k is the smallest number of its keys whose softmax weights
+ * w_m = exp(logit_scale * (sigma[g][m] - max_m' sigma[g][m'])), largest first, reach `mass` of
+ * the row's total weight. The largest weights belong to the largest scores, so the first k
+ * keys of dsv_lowrank_topk (same scores, same order) carry that share; with k_per_head =
+ * k_head every group of the head gets at least its own k keys.
+ * Arithmetic: each w_m is evaluated in fp64 and rounded to an integer multiple of 2^-P,
+ * P = 62 - (bit length of S); all sums are exact integer sums, so the result does not depend
+ * on the order of the work and repeats bit for bit. Compared with exact arithmetic, each
+ * prefix sum of the weights and the target mass * total are off by at most S * 2^-(P+1) +
+ * 2^-P plus a few fp64 roundings of the total: k can differ from the exact rule only in a row
+ * where some prefix sum lies that close to mass * total. Launches on `stream`; no workspace. */
 int dsv_adaptive_k(const dsv_problem* p, const void* q_lr, const void* k_lr, float logit_scale,
                    double mass, int32_t* k_group, int32_t* k_head, void* stream);
 
@@ -154,6 +157,7 @@ int dsv_adaptive_k(const dsv_problem* p, const void* q_lr, const void* k_lr, flo
  *   q,k,v : [B][H][S][d] device, dtype p->dtype.   idx, k_per_head: as above.
  *   o     : [B][H][S][d] device, dtype p->dtype (written).
  *   lse   : [B][H][S] fp32 device (written): log sum_m exp(scale*q.k_m) over the row's keys.
+ *   scale : > 0 and finite (DSV_ERR_SHAPE otherwise), e.g. 1/sqrt(d).
  * For query n in group g: O[n] = sum_{m in idx(g)} softmax_m(scale*q_n.k_m) v_m, computed with
  * fp32 accumulation (bf16 MFMA operands on the bf16 path). */
 int dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, const void* v,
@@ -163,7 +167,7 @@ int dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, cons
 /* Query-grouped sparse attention, backward (idx is a constant: no gradient flows to the
  * low-rank factors).
  *   o, d_o : [B][H][S][d] device, dtype p->dtype (o is the forward output).
- *   lse    : forward LSE.
+ *   lse    : forward LSE.   scale: as for the forward (> 0 and finite).
  *   dq,dk,dv : [B][H][S][d] fp32 device (written in full: every key receives the sum over
  *              all groups that selected it, 0 if none did).
  *   ws       : device, 256-byte aligned, at least dsv_workspace_bytes(DSV_OP_BWD, ...) bytes
@@ -217,6 +221,15 @@ int dsv_sparse_attn_bwd_profiled(const dsv_problem* p, const void* q, const void
  * of one device in this same decreasing-cost order. */
 int dsv_plan_heads(const int32_t* k_per_head, int32_t heads, int32_t n_parts, double fixed_cost,
                    double cost_per_k, int32_t* part_of_head, double* part_load, double* rho);
+
+/* The planner's processing order: heads by decreasing cost fixed_cost + cost_per_k * k_h
+ * (equal costs: lower head index first), i.e. the order in which dsv_plan_heads places them.
+ * On one device (n_parts = 1) every head lands on it in this order, and the kernels launch the
+ * heads of a problem in the order dsv_plan_order(k_per_head, H, 0, 1, order) gives.
+ * (DSV summaries zh §2.3 head re-balancing; db-SP summary, head-level greedy.)
+ *   order : host [heads], written: head indices, first processed first. */
+int dsv_plan_order(const int32_t* k_per_head, int32_t heads, double fixed_cost,
+                   double cost_per_k, int32_t* order);
 
 /* Per-unit costs of this library's kernels on one MI355X, for planning and dispatch. */
 typedef struct {

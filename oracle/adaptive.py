@@ -62,7 +62,14 @@ def k_bracket(sigma_row: np.ndarray, logit_scale: float, mass: float,
     """(k_lo, k_hi): the smallest counts whose prefix sums reach mass * total - band and
     mass * total + band. exact_k lies in between, and so does the k of any evaluation of the
     rule whose prefix sums and target are each within band / 2 of the exact ones."""
+    return k_with_bracket(sigma_row, logit_scale, mass, band)[1:]
+
+
+def k_with_bracket(sigma_row: np.ndarray, logit_scale: float, mass: float,
+                   band: float) -> Tuple[int, int, int]:
+    """(exact_k, k_lo, k_hi) from one sort of the row's weights."""
     w = softmax_weights(sigma_row, logit_scale)
     wd = _sorted_desc(w)
     target = mass * math.fsum(w)
-    return _first_reaching(wd, target - band), _first_reaching(wd, target + band)
+    return (_first_reaching(wd, target), _first_reaching(wd, target - band),
+            _first_reaching(wd, target + band))

@@ -28,9 +28,14 @@ def head_costs(k_per_head: Sequence[int], fixed: float, per_k: float) -> List[fl
     return [fixed + per_k * float(k) for k in k_per_head]
 
 
+def lpt_order(costs: Sequence[float]) -> List[int]:
+    """The greedy's processing order: heads by decreasing cost, equal costs by lower index."""
+    return sorted(range(len(costs)), key=lambda h: (-costs[h], h))
+
+
 def lpt(costs: Sequence[float], n_parts: int) -> Tuple[List[int], List[float]]:
     """Longest-processing-time greedy: (device of each head, load of each device)."""
-    order = sorted(range(len(costs)), key=lambda h: (-costs[h], h))
+    order = lpt_order(costs)
     load = [0.0] * n_parts
     part = [0] * len(costs)
     for h in order:

@@ -108,6 +108,14 @@ def oracle_bwd(cfg, x, rows, b, h, groups=None, mem=None):
                                   f64(x["do"][b, h]), mem, rows, x["scale"], groups=groups)
 
 
+def adaptive_band(S: int) -> float:
+    """Absolute band on the prefix sums within which dsv_adaptive_k may decide differently from
+    the exact rule (include/dsv.h): twice the per-sum bound of its fixed-point weights, plus
+    fp64 roundings of sums of at most S weights <= 1, with a wide margin."""
+    P = 62 - int(S).bit_length()
+    return 2.0 * (S * 2.0 ** -(P + 1) + 2.0 ** -P) + S * 2.0 ** -46
+
+
 def maxerr(a, b) -> float:
     a = np.asarray(a)
     b = np.asarray(b)

@@ -100,6 +100,22 @@ def test_entry_points_reject_before_any_hip_call():
     assert dsv.STATUS[st] == "DSV_ERR_NULL"
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
+def test_attention_rejects_a_scale_that_is_not_positive_and_finite(scale):
+    """The kernels order logits by raw q.k: a scale <= 0 or not finite is refused before any
+    HIP call (forward and backward)."""
+    L = dsv.lib()
+    p = mid()
+    ks = (ctypes.c_int32 * 24)(*([6554] * 24))
+    st = L.dsv_sparse_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, ks, scale, FAKE, FAKE,
+                               None, 0, None)
+    assert dsv.STATUS[st] == "DSV_ERR_SHAPE" and "scale" in dsv.last_error()
+    need = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, list(ks))
+    st = L.dsv_sparse_attn_bwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ks,
+                               scale, FAKE, FAKE, FAKE, FAKE, need, None)
+    assert dsv.STATUS[st] == "DSV_ERR_SHAPE" and "scale" in dsv.last_error()
+
+
 def test_workspace_and_idx_layout_agree_with_oracle():
     p = dsv.problem(2, 3, 4, 8, 8, 64, 16, (2, 2, 4), "bf16")
     ks = [5, 17, 3]

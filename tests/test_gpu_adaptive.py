@@ -1,5 +1,7 @@
-"""GPU parity of the adaptive k (dsv_adaptive_k) against the oracle: every group's k
-bit-exact, the head's k their maximum, repeatable bit for bit."""
+"""GPU parity of the adaptive k (dsv_adaptive_k) against the oracle's plain rule (fp64 softmax
+weights, full sort, exactly rounded prefix sums): every group's k equal to it wherever no
+prefix sum lies within the kernel's stated rounding band of the target, and inside the band's
+bracket everywhere; the head's k their maximum; repeatable bit for bit."""
 import math
 
 import numpy as np
@@ -9,7 +11,7 @@ import torch
 import dynamic_sparse_attention_rank_amd as dsv
 from oracle import adaptive as oad
 from oracle import topk as otopk
-from parity_util import f64, gpu_inputs, members, say, workload
+from parity_util import adaptive_band, f64, gpu_inputs, members, say, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -40,13 +42,20 @@ def test_adaptive_k_bit_exact(label, name, over, mass, fac):
     kg = kg.cpu().numpy()
     kh = kh.cpu().numpy()
     mem = members(cfg)
-    w = oad.bin_weights()
+    band = adaptive_band(p.seq)
+    n_amb = 0
     for b in range(cfg.batch):
         for h in range(cfg.heads):
             sig = otopk.group_scores_sum_first(f64(x["q_lr"][b, h]), f64(x["k_lr"][b, h]), mem)
-            ref = np.array([oad.k_from_counts(oad.group_bin_counts(sig[g], ls32), mass, w)
-                            for g in range(sig.shape[0])])
-            assert np.array_equal(kg[b, h], ref), (b, h, np.argwhere(kg[b, h] != ref)[:5])
+            for g in range(sig.shape[0]):
+                ke, lo, hi = oad.k_with_bracket(sig[g], ls32, mass, band)
+                got = int(kg[b, h, g])
+                assert lo <= got <= hi, (b, h, g, got, ke, lo, hi)
+                if lo == hi:
+                    assert got == ke, (b, h, g, got, ke)
+                else:
+                    n_amb += 1
+    say(f"   {kg.size} groups, {n_amb} within the rounding band of the target")
     assert np.array_equal(kh, kg.max(axis=(0, 2)))
     if mass == 1.0:
         assert np.all(kg == p.seq)

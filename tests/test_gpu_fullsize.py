@@ -146,10 +146,11 @@ def test_training_steps():
 
 
 def test_mid_adaptive_k_sampled_groups():
-    """Adaptive k at S=65536: sampled groups of three heads bit-exact against the oracle; the
-    head k is the largest group k."""
+    """Adaptive k at S=65536: sampled groups of three heads against the oracle's sort rule
+    (equal outside the rounding band); the head k is the largest group k."""
     import math
     from oracle import adaptive as oad
+    from parity_util import adaptive_band
     cfg = workload("mid")
     say("[full] mid: adaptive k, mass 0.9")
     x = gpu_inputs(cfg, backward=False)
@@ -160,13 +161,14 @@ def test_mid_adaptive_k_sampled_groups():
     assert np.array_equal(kh.cpu().numpy(), kg.max(axis=(0, 2)))
     ls32 = float(np.float32(1.0 / (math.sqrt(cfg.head_dim) * p.group_size)))
     mem = members(cfg)
-    w = oad.bin_weights()
+    band = adaptive_band(p.seq)
     for h in (0, 7, 23):
         for g in _sampled_groups(cfg.n_groups, 4, 200 + h):
             sig = otopk.group_scores_sum_first(f64(x["q_lr"][0, h]), f64(x["k_lr"][0, h]),
                                                mem[g:g + 1])[0]
-            ref = oad.k_from_counts(oad.group_bin_counts(sig, ls32), 0.9, w)
-            assert kg[0, h, g] == ref, (h, g, kg[0, h, g], ref)
+            ke, lo, hi = oad.k_with_bracket(sig, ls32, 0.9, band)
+            got = int(kg[0, h, g])
+            assert lo <= got <= hi and (lo != hi or got == ke), (h, g, got, ke, lo, hi)
 
 
 def test_mid_topk_max_sampled_groups():

@@ -325,3 +325,35 @@ def test_malformed_index_rows_are_memory_safe():
         tok = mem[groups].ravel()
         eq = maxerr(f64(dq[0, h])[tok], rq[tok])
         assert eq <= TOL[cfg.dtype], (h, eq)
+
+
+def test_pipeline_on_a_side_stream_matches_the_current_stream():
+    """The binding allocates its outputs and the backward's workspace on the launch stream:
+    top-k, forward and backward launched on a side stream (default priority) give the same
+    bits as on the current stream, while the current stream allocates and fills other memory
+    meanwhile."""
+    cfg = workload("small", heads=4)
+    say("[stream] full pipeline on a side stream")
+    x = gpu_inputs(cfg, backward=True)
+    p = dsv.problem_for(cfg)
+    ks = x["k_per_head"]
+
+    def run(stream):
+        idx = dsv.lowrank_topk(p, x["q_lr"], x["k_lr"], ks, stream=stream)
+        o, lse = dsv.sparse_attn_fwd(p, x["q"], x["k"], x["v"], idx, ks, x["scale"],
+                                     stream=stream)
+        d = dsv.sparse_attn_bwd(p, x["q"], x["k"], x["v"], o, x["do"], lse, idx, ks,
+                                x["scale"], stream=stream)
+        return (idx, o, lse) + tuple(d)
+
+    ref = run(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = run(side)
+    # the current stream keeps allocating and writing while the side stream works
+    junk = [torch.full((1 << 22,), 7.0, device="cuda") for _ in range(8)]
+    del junk
+    torch.cuda.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)

@@ -23,6 +23,25 @@ def test_plan_heads_matches_oracle(seed):
     assert rho == pytest.approx(planning.rho_s(oload), rel=1e-15)
 
 
+@pytest.mark.parametrize("seed", range(10))
+def test_plan_order_matches_oracle(seed):
+    rng = random.Random(100 + seed)
+    H = rng.randint(1, 64)
+    ks = [rng.choice([2621, 6554, 13107, 26214]) for _ in range(H)]
+    fixed, per_k = rng.choice([(0.0, 1.0), (0.3, 2e-4), (1.0, 0.0)])
+    assert dsv.plan_order(ks, fixed, per_k) == \
+        planning.lpt_order(planning.head_costs(ks, fixed, per_k))
+
+
+def test_plan_order_is_the_one_device_placement_order():
+    # on one device the greedy places every head, in its processing order
+    ks = [2621, 26214, 6554, 26214, 13107, 2621]
+    order = dsv.plan_order(ks)
+    assert order == [1, 3, 4, 2, 0, 5]
+    part, load, rho = dsv.plan_heads(ks, 1, 0.0, 1.0)
+    assert part == [0] * 6 and rho == 1.0
+
+
 def test_plan_heads_long_workload():
     # the heterogeneous-k workload (S = 128K, k in {2%, 5%, 10%, 20%} of S, 16 heads) on 8
     # devices; a round-robin placement (heads 0..15 -> devices h % 8) for comparison
