@@ -27,7 +27,8 @@ EXPORTED = ("dsv_workspace_bytes", "dsv_idx_elems", "dsv_idx_row_offset", "dsv_l
             "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd", "dsv_bwd_chunks",
             "dsv_sparse_attn_bwd_profiled", "dsv_validate", "dsv_status_string",
             "dsv_last_error", "dsv_version", "dsv_plan_heads", "dsv_default_cost_model",
-            "dsv_dispatch_k", "dsv_adaptive_k", "dsv_topk_max_cache_bytes", "dsv_plan_order")
+            "dsv_dispatch_k", "dsv_adaptive_k", "dsv_topk_max_cache_bytes", "dsv_plan_order",
+            "dsv_sparse_attn_bwd_noalloc")
 
 
 class DsvError(RuntimeError):
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.dsv_sparse_attn_bwd_profiled.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32p, f, vp,
                                                    vp, vp, vp, sz, vp, ctypes.POINTER(vp),
                                                    ctypes.c_int]
+        L.dsv_sparse_attn_bwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32p, f, vp,
+                                                  vp, vp, vp]
         L.dsv_bwd_chunks.argtypes = [P, i32p, sz]
         L.dsv_bwd_chunks.restype = ctypes.c_int
         L.dsv_validate.argtypes = [ctypes.c_int, P, i32p, ctypes.c_int,
@@ -117,7 +120,7 @@ def lib() -> ctypes.CDLL:
         for fn in ("dsv_lowrank_topk", "dsv_sparse_attn_fwd", "dsv_sparse_attn_bwd",
                    "dsv_sparse_attn_bwd_profiled", "dsv_validate", "dsv_plan_heads",
                    "dsv_default_cost_model", "dsv_dispatch_k", "dsv_adaptive_k",
-                   "dsv_plan_order"):
+                   "dsv_plan_order", "dsv_sparse_attn_bwd_noalloc"):
             getattr(L, fn).restype = ctypes.c_int
         _lib = L
     return _lib

@@ -33,6 +33,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.h"
 #include "dsv_internal.h"
@@ -876,6 +877,33 @@ int bwd_chunk_count(const Geom& geo, size_t ws_bytes) {
   int n = 0;
   for (int s0 = 0; s0 < geo.B * geo.H; ++n) s0 += next_chunk(geo, s0, cs, ecap).n;
   return n;
+}
+
+// ---- the no-allocation backward's scratch: one fixed device array per GPU, in place of a
+// caller workspace. In host code `scratch` is only a stand-in for the symbol: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device current) and
+// only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[DSV_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+int bwd_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return 0;
 }
 
 int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v, const void* o,

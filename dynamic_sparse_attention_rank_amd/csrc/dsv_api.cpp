@@ -280,6 +280,35 @@ int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, cons
                     stream, nullptr, 0);
 }
 
+int dsv_sparse_attn_bwd_noalloc(const dsv_problem* p, const void* q, const void* k,
+                                const void* v, const void* o, const void* d_o, const float* lse,
+                                const int32_t* idx, const int32_t* k_per_head, float scale,
+                                float* dq, float* dk, float* dv, void* stream) {
+  Geom geo;
+  int st = validate_problem(p, k_per_head, &geo);
+  if (st != DSV_OK) return st;
+  const size_t need = bwd_workspace_bytes(geo);
+  // every argument check of the workspace entry point first (no HIP call before them)
+  const void* ptrs[] = {q, k, v, o, d_o, lse, idx, dq, dk, dv};
+  if ((st = dsv_validate(DSV_OP_BWD, p, k_per_head, DSV_GROUP_SUM, ptrs, 10, need)) != DSV_OK)
+    return st;
+  if ((st = check_scale(scale)) != DSV_OK) return st;
+  if (need > (size_t)DSV_NOALLOC_SCRATCH_BYTES)
+    return fail(DSV_ERR_WORKSPACE,
+                "backward needs %zu bytes of workspace for its largest head; the no-allocation "
+                "entry point has a fixed scratch of %zu bytes",
+                need, (size_t)DSV_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (need > 0) {
+    const int e = bwd_scratch(&ws);
+    if (e) return fail(DSV_ERR_HIP, "scratch lookup failed (hipError %d)", e);
+    ws_bytes = (size_t)DSV_NOALLOC_SCRATCH_BYTES;
+  }
+  return bwd_common(p, q, k, v, o, d_o, lse, idx, k_per_head, scale, dq, dk, dv, ws, ws_bytes,
+                    stream, nullptr, 0);
+}
+
 int dsv_bwd_chunks(const dsv_problem* p, const int32_t* k_per_head, size_t ws_bytes) {
   Geom geo;
   if (validate_problem(p, k_per_head, &geo) != DSV_OK) return -1;

@@ -75,5 +75,9 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
 size_t bwd_workspace_bytes(const Geom& geo);
 // Number of head chunks (launch groups) the backward uses with this workspace (1 on fp32).
 int bwd_chunk_count(const Geom& geo, size_t ws_bytes);
+// Device address of the no-allocation backward's scratch array (DSV_NOALLOC_SCRATCH_BYTES) on
+// the calling thread's current device, looked up on the first call per device. 0 or a
+// hipError_t value.
+int bwd_scratch(void** ptr);
 
 }  // namespace dsv

@@ -185,6 +185,28 @@ int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, cons
                         const int32_t* k_per_head, float scale, float* dq, float* dk, float* dv,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Size of the fixed device scratch array of dsv_sparse_attn_bwd_noalloc: 256 MiB per GPU,
+ * held from the library's load until the process ends. */
+#define DSV_NOALLOC_SCRATCH_BYTES (256u * 1024u * 1024u)
+
+/* dsv_sparse_attn_bwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). It runs the same kernels with a fixed scratch array of
+ * DSV_NOALLOC_SCRATCH_BYTES that the library keeps on each GPU, and calls no allocator.
+ *   Arguments, layouts, results and errors: as dsv_sparse_attn_bwd (the results are the same
+ *   bits). stream must belong to the calling thread's current device.
+ *   DSV_ERR_WORKSPACE (nothing enqueued) when dsv_workspace_bytes(DSV_OP_BWD, p, k_per_head)
+ *   exceeds DSV_NOALLOC_SCRATCH_BYTES: the heaviest head's staging rows must fit (S = 16K,
+ *   d = 64, G = 64, k = 10% needs about 112 MB; S = 64K, d = 128, k = 10% does not fit).
+ *   DSV_ERR_HIP if the scratch array's address cannot be looked up.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's contents: calls
+ * that overlap on one GPU (several streams or threads) race, and must be serialised by the
+ * caller. The first call on each device looks the array's address up (no allocation). */
+int dsv_sparse_attn_bwd_noalloc(const dsv_problem* p, const void* q, const void* k,
+                                const void* v, const void* o, const void* d_o, const float* lse,
+                                const int32_t* idx, const int32_t* k_per_head, float scale,
+                                float* dq, float* dk, float* dv, void* stream);
+
 /* Number of head chunks dsv_sparse_attn_bwd uses with a workspace of ws_bytes: the heads
  * are processed in that many groups of launches, each staging its rows in the workspace.
  * 1 on the fp32 path; -1 if the problem is invalid or ws_bytes is below the minimum. */

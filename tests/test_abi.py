@@ -190,3 +190,24 @@ def test_topk_max_cache_bytes():
     assert dsv.topk_max_cache_bytes(mid()) == 1024 * 65536 * 4
     with pytest.raises(ValueError):
         dsv.topk_max_cache_bytes(dsv.problem(2, 3, 4, 8, 8, 64, 16, (3, 2, 4), "bf16"))
+
+
+def test_noalloc_bwd_validates_before_any_hip_call():
+    """The no-allocation backward refuses, before touching HIP, a problem whose heaviest head
+    does not fit its fixed scratch (S = 64K, d = 128, k = 10%), and bad arguments as the
+    workspace entry point does."""
+    L = dsv.lib()
+    p = dsv.problem(1, 1, 16, 64, 64, 128, 32, (4, 4, 4), "bf16")
+    ks = (ctypes.c_int32 * 1)(6554)
+    assert dsv.workspace_bytes(dsv.DSV_OP_BWD, p, [6554]) > 256 * 1024 * 1024
+    args = [FAKE] * 7
+    st = L.dsv_sparse_attn_bwd_noalloc(ctypes.byref(p), *args, ks, 0.088, FAKE, FAKE, FAKE, None)
+    assert dsv.STATUS[st] == "DSV_ERR_WORKSPACE" and "scratch" in dsv.last_error()
+    small = dsv.problem(1, 1, 16, 32, 32, 64, 16, (4, 4, 4), "bf16")
+    ks1 = (ctypes.c_int32 * 1)(1638)
+    st = L.dsv_sparse_attn_bwd_noalloc(ctypes.byref(small), FAKE, 0, *[FAKE] * 5, ks1, 0.125,
+                                       FAKE, FAKE, FAKE, None)
+    assert dsv.STATUS[st] == "DSV_ERR_NULL"
+    st = L.dsv_sparse_attn_bwd_noalloc(ctypes.byref(small), *[FAKE] * 7, ks1, 0.0, FAKE, FAKE,
+                                       FAKE, None)
+    assert dsv.STATUS[st] == "DSV_ERR_SHAPE"
