@@ -66,6 +66,13 @@ __device__ __forceinline__ float key_upper_bound(unsigned long long k) {
   return key_float((uint32_t)k);
 }
 
+// The smallest float above a finite x.
+__device__ __forceinline__ float next_up(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) == 0u) return __uint_as_float(1u);   // +-0 -> smallest subnormal
+  return __uint_as_float((u & 0x80000000u) ? u - 1u : u + 1u);
+}
+
 // Contraction layout. bf16: k-step i covers features 16i .. 16i + 15, lane slot h = l / 32 holds
 // 16i + 8h .. 16i + 8h + 7 (one 16-byte load). fp32: slot h holds features h R/2 .. h R/2 + R/2 - 1,
 // one per v_mfma_f32_32x32x2f32 step (R/8 16-byte loads). A lane's own feature f (< R/2) is
@@ -177,11 +184,13 @@ struct ScoreStream {
 #pragma unroll
     for (int i = 0; i < C::NB; ++i) a[i] = ld16(krow + C::off(i, hh));
   }
-  // scores of the tile's 32 keys (rows) for the 32 groups (columns)
+  // scores of the tile's 32 keys (rows) for the 32 groups (columns), plus c0 (the lane's
+  // group's offset: 0, or minus its window base, which keeps integer scores exact)
+  float c0 = 0.0f;
   __device__ __forceinline__ floatx16 scores(const u32x4* a) const {
     floatx16 acc;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+    for (int e = 0; e < 16; ++e) acc[e] = c0;
 #pragma unroll
     for (int i = 0; i < C::NB; ++i) {
       if constexpr (F32) {
@@ -216,7 +225,39 @@ struct ScoreStream {
     }
     if (nfull * TK_TILE < S) body(acc, nfull, Flag<true>{});   // acc holds tile nfull
   }
+  // The full tiles j * stride, j < ns (a sample of the key stream), as walk() does.
+  template <class Body>
+  __device__ __forceinline__ void walk_sample(int ns, int stride, Body&& body) const {
+    u32x4 a0[C::NB], a1[C::NB];
+    load_a(0, a0);
+    load_a(min(1, ns - 1) * stride, a1);
+    floatx16 acc = scores(a0);
+    for (int j = 0; j < ns; j += 2) {
+      load_a(min(j + 2, ns - 1) * stride, a0);
+      floatx16 nxt = scores(a1);
+      body(acc, j * stride);
+      acc = nxt;
+      if (j + 1 >= ns) break;
+      load_a(min(j + 3, ns - 1) * stride, a1);
+      nxt = scores(a0);
+      body(acc, (j + 1) * stride);
+      acc = nxt;
+    }
+  }
 };
+
+// Threshold window. A sample of the key stream (TK_SAMPLE_TILES tiles spread over it) gives each
+// group an estimate of its k-th largest score; one sweep then counts every key into TK_W bins
+// of one score unit each around that estimate (plus a bin below and one above the window), so
+// for integer-valued scores the bin where the count from the top reaches k holds a single
+// score value T, with `need` of its keys still to take. The compaction tests scores against T
+// exactly and verifies that it took k keys; a group whose threshold falls outside its window,
+// or whose count does not verify (scores that are not integers), is resolved by the radix
+// passes instead, which are exact for any scores.
+constexpr int TK_W = 512;                  // window bins of one score unit each
+constexpr int TK_WSTRIDE = TK_W + 3;       // bins: below, window, above, tail dummy (3 mod 64)
+constexpr int TK_SAMPLE_TILES = 8;         // sampled tiles (8 x 512 keys)
+constexpr int TK_SBINS = 256;              // linear bins of the sample histogram
 
 template <bool F32, int R>
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict__ qlr_,
@@ -224,18 +265,29 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
                                                           int32_t* __restrict__ idx, Geom geo) {
   using C = TopkCfg<F32, R>;
   static_assert(TK_SUMW * 64 * C::NF <= TK_GROUPS * TK_HSTRIDE, "partial sums overflow");
-  __shared__ uint32_t hist[TK_GROUPS * TK_HSTRIDE];   // also the group sums' partials, first
+  static_assert(TK_SBINS <= TK_HSTRIDE && TK_W == 8 * 64, "bin layout");
+  // group-sum partials first, then the sample histogram, then the radix histograms
+  __shared__ uint32_t hist[TK_GROUPS * TK_HSTRIDE];
+  __shared__ uint32_t whist[TK_GROUPS * TK_WSTRIDE];   // window counts
   // compaction: per tile parity, group and key slice, the slice's count of keys above the
   // threshold (bits 0..15) and equal to it (bits 16..31)
   __shared__ __attribute__((aligned(16))) uint32_t tcnt[2][TK_GROUPS][TK_KW];
   __shared__ uint32_t st_prefix[TK_GROUPS];
-  __shared__ int st_krem[TK_GROUPS];
-  // Group state: -1 = no such group; 0..3 = still refining, that many digits known (and the
-  // next histogram pass is that index); 16 + D = finished with D digits known.
+  __shared__ int st_krem[TK_GROUPS];   // keys still to take at the threshold
+  // Group state: -1 = no such group; 0..3 = radix refining, that many digits known (and the
+  // next histogram pass is that index); 16 + D = radix finished with D digits known;
+  // kWindow = threshold value st_t found in the window.
+  constexpr int kWindow = 32;
   __shared__ int st_npass[TK_GROUPS];
   __shared__ int st_active[4];
-  // per group: set when a key counted in the current pass has a nonzero bit below the digit
+  // per group: set when a key counted in the current radix pass has a nonzero bit below the
+  // digit
   __shared__ uint32_t st_lowbits[TK_GROUPS];
+  __shared__ uint32_t st_mn[TK_GROUPS], st_mx[TK_GROUPS];   // sample extremes (key images)
+  __shared__ float st_tlo[TK_GROUPS];   // window base: bin i + 1 counts score st_tlo + i
+  __shared__ float st_t[TK_GROUPS];
+  __shared__ int st_done[TK_GROUPS];    // row written with exactly k keys
+  __shared__ int st_retry;
 
   const int tid = threadIdx.x;
   const int kw = tid >> 6;       // wave = key slice
@@ -262,27 +314,158 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
   ss.init(geo, qlr_, klr_, bh, my_group, reinterpret_cast<float*>(hist));
 
   for (int i = tid; i < TK_GROUPS; i += TK_THREADS) {
+    const bool valid = gblock * TK_GROUPS + i < geo.NG;
     st_prefix[i] = 0;
     st_lowbits[i] = 0;
     st_krem[i] = kh;
-    st_npass[i] = (gblock * TK_GROUPS + i < geo.NG) ? 0 : -1;   // -1: no such group
+    st_npass[i] = valid ? 0 : -1;
+    st_done[i] = valid ? 0 : 1;
+    st_mn[i] = 0xffffffffu;
+    st_mx[i] = 0u;
   }
   for (int i = tid; i < TK_GROUPS * TK_HSTRIDE; i += TK_THREADS) hist[i] = 0;
-
+  for (int i = tid; i < TK_GROUPS * TK_WSTRIDE; i += TK_THREADS) whist[i] = 0;
   __syncthreads();
 
-  // ---- radix passes (pass 4 = compaction)
-  for (int pass = 0; pass <= 4; ++pass) {
-    if (pass < 4) {
+  // ---- threshold window (a uniform decision: every wave takes the same branches)
+  const int nfull = S / TK_TILE;
+  const int ns = min(TK_SAMPLE_TILES, nfull);
+  if (ns > 0) {
+    const int stride = nfull / ns;
+    // sample extremes
+    float smn = INFINITY, smx = -INFINITY;
+    ss.walk_sample(ns, stride, [&](const floatx16& acc, int) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        smn = fminf(smn, acc[e]);
+        smx = fmaxf(smx, acc[e]);
+      }
+    });
+    smn = fminf(smn, __shfl_xor(smn, 32, 64));
+    smx = fmaxf(smx, __shfl_xor(smx, 32, 64));
+    __hip_atomic_fetch_min(&st_mn[g], score_key(smn), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_max(&st_mx[g], score_key(smx), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+    __syncthreads();
+    // sample histogram: TK_SBINS equal bins over [min, max]
+    {
+      const float mn = key_float(st_mn[g]), mx = key_float(st_mx[g]);
+      const float inv = mx > mn ? (float)TK_SBINS / (mx - mn) : 0.0f;
+      uint32_t* const hrow = &hist[g * TK_HSTRIDE];
+      ss.walk_sample(ns, stride, [&](const floatx16& acc, int) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int bin = min((int)((acc[e] - mn) * inv), TK_SBINS - 1);
+          __hip_atomic_fetch_add(&hrow[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      });
+    }
+    __syncthreads();
+    // the estimate: the sample's score at the rank that k takes in the whole row; the window
+    // is centred on it
+    const int nsamp = ns * TK_TILE;
+    const uint32_t rt = (uint32_t)max(1LL, ((long long)nsamp * kh + S - 1) / S);
+    for (int gl = kw; gl < TK_GROUPS; gl += TK_KW) {
+      if (st_npass[gl] < 0) continue;   // uniform across the wave
+      uint32_t* hr = &hist[gl * TK_HSTRIDE];
+      uint32_t c[4], lsum = 0;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        c[tt] = hr[TK_SBINS - 1 - (4 * lane + tt)];
+        lsum += c[tt];
+      }
+      uint32_t incl = lsum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t x = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += x;
+      }
+      uint32_t excl = incl - lsum;
+      const float mn = key_float(st_mn[gl]), mx = key_float(st_mx[gl]);
+      wave_lds_fence();
+      if (excl < rt && rt <= incl) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (excl + c[tt] >= rt) {
+            const int bin = TK_SBINS - 1 - (4 * lane + tt);
+            const float est = mx > mn ? mn + ((float)bin + 0.5f) * ((mx - mn) / (float)TK_SBINS)
+                                      : mn;
+            st_tlo[gl] = floorf(est) - (float)(TK_W / 2);
+            break;
+          }
+          excl += c[tt];
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) hr[4 * lane + tt] = 0;
+    }
+    __syncthreads();
+    // window sweep: scores offset by -tlo in the MFMA accumulator, bins by floor
+    ss.c0 = st_npass[g] >= 0 ? -st_tlo[g] : 0.0f;
+    uint32_t* const wrow = &whist[g * TK_WSTRIDE];
+    ss.walk([&](const floatx16& acc, int t, auto tail_tag) {
+      constexpr bool kTail = decltype(tail_tag)::value;
+      const int mb = t * TK_TILE + 32 * kw + 4 * hh;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        int bin = min(max(__float2int_rd(acc[e]), -1), TK_W) + 1;
+        if constexpr (kTail) bin = mb + 8 * (e >> 2) + (e & 3) < S ? bin : TK_W + 2;
+        __hip_atomic_fetch_add(&wrow[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    });
+    ss.c0 = 0.0f;
+    __syncthreads();
+    // the bin where the count from the top reaches k: 8 bins per lane, from the top
+    for (int gl = kw; gl < TK_GROUPS; gl += TK_KW) {
+      if (st_npass[gl] < 0) continue;   // uniform
+      const uint32_t* wr = &whist[gl * TK_WSTRIDE];
+      const uint32_t above = wr[TK_W + 1];
+      uint32_t c[8], lsum = 0;
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        c[tt] = wr[TK_W - (8 * lane + tt)];
+        lsum += c[tt];
+      }
+      uint32_t incl = lsum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t x = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += x;
+      }
+      uint32_t excl = above + incl - lsum;
+      incl += above;
+      const float tlo = st_tlo[gl];
+      const uint32_t k = (uint32_t)kh;
+      wave_lds_fence();
+      if (above < k && excl < k && k <= incl) {   // otherwise: outside the window (radix)
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt) {
+          if (excl + c[tt] >= k) {
+            const int bin = TK_W - (8 * lane + tt);   // counts score tlo + bin - 1
+            st_t[gl] = tlo + (float)(bin - 1);
+            st_krem[gl] = (int)(k - excl);
+            st_npass[gl] = kWindow;
+            break;
+          }
+          excl += c[tt];
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- rounds: radix passes for the groups still refining, then compaction of the rows not
+  // yet written; a window row whose count does not verify goes to the radix passes
+  for (int round = 0; round < 2; ++round) {
+    for (int pass = 0; pass < 4; ++pass) {
       if (tid == 0) {
         int act = 0;
         for (int i = 0; i < TK_GROUPS; ++i) act |= (st_npass[i] == pass);
         st_active[pass] = act;
       }
       __syncthreads();
-      if (!st_active[pass]) continue;   // uniform: every group stopped refining earlier
-    }
-    if (pass < 4) {
+      if (!st_active[pass]) continue;   // uniform: no group refines in this pass
       // Histogram pass. The lane also ORs the bits below the digit over the keys it counts.
       const int dshift = 24 - 8 * pass;
       const int pshift = 32 - 8 * pass;
@@ -318,69 +501,6 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
         ss.walk([&](const floatx16& acc, int t, auto tail) { count(acc, t, tail, Flag<false>{}); });
       }
       if ((lowor & ((1u << dshift) - 1u)) != 0) st_lowbits[g] = 1u;   // any lane: not zero
-    } else {
-      // Compaction. Both lanes of a group keep the same running state.
-      const int gs = st_npass[g];
-      const unsigned long long pfx = gs >= 16 ? st_prefix[g] : 0xffffffffull;
-      const int shift = gs >= 16 ? 32 - 8 * (gs - 16) : 0;   // no key exceeds all-ones
-      // keys above the threshold prefix: key >= khi; equal to it: klo <= key < khi
-      const float f_hi = key_lower_bound((pfx + 1) << shift);
-      const float f_hi_u = key_upper_bound((pfx + 1) << shift);
-      const float f_lo = key_lower_bound(pfx << shift);
-      int left = gs >= 16 ? st_krem[g] : 0;                    // equal keys still to take
-      int cnt = 0;
-      int32_t* const orow = idx + geo.row_offset(b, h, gs >= 0 ? my_group : 0);
-      ss.walk([&](const floatx16& acc, int t, auto tail_tag) {
-        constexpr bool kTail = decltype(tail_tag)::value;
-        const int mb = t * TK_TILE + 32 * kw + 4 * hh;
-        uint32_t gtm = 0, eqm = 0;   // bit e: element e above / equal
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          bool valid = true;
-          if constexpr (kTail) valid = mb + 8 * (e >> 2) + (e & 3) < S;
-          gtm |= (uint32_t)(valid & (acc[e] >= f_hi)) << e;
-          eqm |= (uint32_t)(valid & (acc[e] >= f_lo) & (acc[e] < f_hi_u)) << e;
-        }
-        const uint32_t both = gtm | (eqm << 16);
-        const uint32_t pboth = (uint32_t)__shfl_xor((int)both, 32, 64);
-        const uint32_t pgtm = pboth & 0xffffu, peqm = pboth >> 16;
-        tcnt[t & 1][g][kw] = (uint32_t)(__popc(gtm) + __popc(pgtm)) |
-                             ((uint32_t)(__popc(eqm) + __popc(peqm)) << 16);
-        __syncthreads();
-        uint32_t pre = 0, tot = 0;   // (above, equal) counts of the earlier slices / all slices
-#pragma unroll
-        for (int w4 = 0; w4 < TK_KW; w4 += 4) {
-          const u32x4 c = *reinterpret_cast<const u32x4*>(&tcnt[t & 1][g][w4]);
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            if (w4 + w < kw) pre += c[w];
-            tot += c[w];
-          }
-        }
-        const int pre_gt = (int)(pre & 0xffffu), pre_eq = (int)(pre >> 16);
-        const int lft = max(left, 0);
-        const int base = cnt + pre_gt + min(lft, pre_eq);
-        // the lane's selected keys, one at a time (about 10 % of them); eqm is zero in most tiles
-        const int lr = max(lft - pre_eq, 0);   // equal keys this slice may still take
-        uint32_t todo = gtm | eqm;
-        while (todo != 0u) {
-          const int e = __builtin_ctz(todo);
-          todo &= todo - 1u;
-          const int i = e >> 2;
-          const uint32_t own = (1u << e) - 1u;
-          const uint32_t par = (1u << (4 * i + 4 * hh)) - 1u;   // partner blocks before e
-          const int gtb = __popc(gtm & own) + __popc(pgtm & par);
-          const int eqb = __popc(eqm & own) + __popc(peqm & par);
-          const bool sel = ((gtm >> e) & 1u) || eqb < lr;
-          const int pos = base + gtb + min(lr, eqb);
-          if (sel && pos < kh) orow[pos] = mb + 8 * i + (e & 3);
-        }
-        cnt += (int)(tot & 0xffffu) + min(lft, (int)(tot >> 16));
-        left -= (int)(tot >> 16);
-      });
-    }
-
-    if (pass < 4) {
       __syncthreads();
       // Each wave resolves digit `pass` for some of the groups and clears their histograms.
       for (int gl = kw; gl < TK_GROUPS; gl += TK_KW) {
@@ -401,16 +521,18 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
         }
         const uint32_t krem = (uint32_t)st_krem[gl];
         uint32_t excl = incl - lsum;
+        const uint32_t pfx_gl = st_prefix[gl];
+        const bool low_gl = st_lowbits[gl] != 0u;
+        wave_lds_fence();   // every lane has read the state before one lane rewrites it
         if (excl < krem && krem <= incl) {
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
             if (excl + c[tt] >= krem) {
               const uint32_t bin = 255u - (4u * lane + tt);
               const uint32_t left = krem - excl;   // keys still needed inside `bin`
-              st_prefix[gl] = (pass == 0) ? bin : ((st_prefix[gl] << 8) | bin);
+              st_prefix[gl] = (pass == 0) ? bin : ((pfx_gl << 8) | bin);
               st_krem[gl] = (int)left;
-              st_npass[gl] = (left == c[tt] || pass == 3 || st_lowbits[gl] == 0)
-                                 ? 16 + pass + 1 : pass + 1;
+              st_npass[gl] = (left == c[tt] || pass == 3 || !low_gl) ? 16 + pass + 1 : pass + 1;
               break;
             }
             excl += c[tt];
@@ -418,10 +540,98 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
         }
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) hr[4 * lane + tt] = 0;
-        st_lowbits[gl] = 0;
+        if (lane == 0) st_lowbits[gl] = 0;
       }
       __syncthreads();
     }
+
+    // ---- compaction of the rows not yet written. Both lanes of a group keep the same
+    // running state. Keys above the threshold: score >= f_hi; equal to it: f_lo <= score <
+    // f_hi_u; the first `left` equal keys are taken.
+    const int gs = st_npass[g];
+    const bool writes = st_done[g] == 0;
+    float f_hi, f_hi_u, f_lo;
+    int left;
+    if (gs == kWindow) {
+      const float T = st_t[g];
+      f_lo = T;
+      f_hi = f_hi_u = next_up(T);
+      left = st_krem[g];
+    } else {
+      const unsigned long long pfx = gs >= 16 ? st_prefix[g] : 0xffffffffull;
+      const int shift = gs >= 16 ? 32 - 8 * (gs - 16) : 0;   // no key exceeds all-ones
+      f_hi = key_lower_bound((pfx + 1) << shift);
+      f_hi_u = key_upper_bound((pfx + 1) << shift);
+      f_lo = key_lower_bound(pfx << shift);
+      left = gs >= 16 ? st_krem[g] : 0;
+    }
+    int cnt = 0;
+    int32_t* const orow = idx + geo.row_offset(b, h, gs >= 0 ? my_group : 0);
+    ss.walk([&](const floatx16& acc, int t, auto tail_tag) {
+      constexpr bool kTail = decltype(tail_tag)::value;
+      const int mb = t * TK_TILE + 32 * kw + 4 * hh;
+      uint32_t gtm = 0, eqm = 0;   // bit e: element e above / equal
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        bool valid = true;
+        if constexpr (kTail) valid = mb + 8 * (e >> 2) + (e & 3) < S;
+        gtm |= (uint32_t)(valid & (acc[e] >= f_hi)) << e;
+        eqm |= (uint32_t)(valid & (acc[e] >= f_lo) & (acc[e] < f_hi_u)) << e;
+      }
+      const uint32_t both = gtm | (eqm << 16);
+      const uint32_t pboth = (uint32_t)__shfl_xor((int)both, 32, 64);
+      const uint32_t pgtm = pboth & 0xffffu, peqm = pboth >> 16;
+      tcnt[t & 1][g][kw] = (uint32_t)(__popc(gtm) + __popc(pgtm)) |
+                           ((uint32_t)(__popc(eqm) + __popc(peqm)) << 16);
+      __syncthreads();
+      uint32_t pre = 0, tot = 0;   // (above, equal) counts of the earlier slices / all slices
+#pragma unroll
+      for (int w4 = 0; w4 < TK_KW; w4 += 4) {
+        const u32x4 c = *reinterpret_cast<const u32x4*>(&tcnt[t & 1][g][w4]);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          if (w4 + w < kw) pre += c[w];
+          tot += c[w];
+        }
+      }
+      const int pre_gt = (int)(pre & 0xffffu), pre_eq = (int)(pre >> 16);
+      const int lft = max(left, 0);
+      const int base = cnt + pre_gt + min(lft, pre_eq);
+      // the lane's selected keys, one at a time (about 10 % of them); eqm is zero in most tiles
+      const int lr = max(lft - pre_eq, 0);   // equal keys this slice may still take
+      uint32_t todo = writes ? (gtm | eqm) : 0u;
+      while (todo != 0u) {
+        const int e = __builtin_ctz(todo);
+        todo &= todo - 1u;
+        const int i = e >> 2;
+        const uint32_t own = (1u << e) - 1u;
+        const uint32_t par = (1u << (4 * i + 4 * hh)) - 1u;   // partner blocks before e
+        const int gtb = __popc(gtm & own) + __popc(pgtm & par);
+        const int eqb = __popc(eqm & own) + __popc(peqm & par);
+        const bool sel = ((gtm >> e) & 1u) || eqb < lr;
+        const int pos = base + gtb + min(lr, eqb);
+        if (sel && pos < kh) orow[pos] = mb + 8 * i + (e & 3);
+      }
+      cnt += (int)(tot & 0xffffu) + min(lft, (int)(tot >> 16));
+      left -= (int)(tot >> 16);
+    });
+    // verify: a row is done when exactly k keys were taken; otherwise (a window threshold on
+    // scores that are not integers) the group is resolved by the radix passes
+    if (tid == 0) st_retry = 0;
+    __syncthreads();
+    if (writes && gs >= 0 && hh == 0 && kw == 0) {
+      if (cnt == kh) {
+        st_done[g] = 1;
+      } else {
+        st_npass[g] = 0;
+        st_prefix[g] = 0;
+        st_krem[g] = kh;
+        st_lowbits[g] = 0;
+        st_retry = 1;
+      }
+    }
+    __syncthreads();
+    if (!st_retry) break;
   }
 }
 
