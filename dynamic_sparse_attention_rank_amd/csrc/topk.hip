@@ -255,7 +255,7 @@ struct ScoreStream {
 // or whose count does not verify (scores that are not integers), is resolved by the radix
 // passes instead, which are exact for any scores.
 constexpr int TK_W = 512;                  // window bins of one score unit each
-constexpr int TK_WSTRIDE = TK_W + 3;       // bins: below, window, above, tail dummy (3 mod 64)
+constexpr int TK_WSTRIDE = TK_W + 3;       // bins: (below), window, above, pad (3 mod 64)
 constexpr int TK_SAMPLE_TILES = 8;         // sampled tiles (8 x 512 keys)
 constexpr int TK_SBINS = 256;              // linear bins of the sample histogram
 
@@ -283,6 +283,8 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
   // per group: set when a key counted in the current radix pass has a nonzero bit below the
   // digit
   __shared__ uint32_t st_lowbits[TK_GROUPS];
+  // per group, once the radix passes finish: 1 if the key range left holds a single score
+  __shared__ uint32_t st_single[TK_GROUPS];
   __shared__ uint32_t st_mn[TK_GROUPS], st_mx[TK_GROUPS];   // sample extremes (key images)
   __shared__ float st_tlo[TK_GROUPS];   // window base: bin i + 1 counts score st_tlo + i
   __shared__ float st_t[TK_GROUPS];
@@ -409,9 +411,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
       const int mb = t * TK_TILE + 32 * kw + 4 * hh;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        int bin = min(max(__float2int_rd(acc[e]), -1), TK_W) + 1;
-        if constexpr (kTail) bin = mb + 8 * (e >> 2) + (e & 3) < S ? bin : TK_W + 2;
-        __hip_atomic_fetch_add(&wrow[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        // keys below the window are not counted (only the count from the top matters)
+        int bin = min(__float2int_rd(acc[e]), TK_W) + 1;
+        if constexpr (kTail) bin = mb + 8 * (e >> 2) + (e & 3) < S ? bin : 0;
+        if (bin > 0)
+          __hip_atomic_fetch_add(&wrow[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     });
     ss.c0 = 0.0f;
@@ -532,7 +536,9 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
               const uint32_t left = krem - excl;   // keys still needed inside `bin`
               st_prefix[gl] = (pass == 0) ? bin : ((pfx_gl << 8) | bin);
               st_krem[gl] = (int)left;
-              st_npass[gl] = (left == c[tt] || pass == 3 || !low_gl) ? 16 + pass + 1 : pass + 1;
+              const bool single = pass == 3 || !low_gl;
+              st_npass[gl] = (left == c[tt] || single) ? 16 + pass + 1 : pass + 1;
+              st_single[gl] = single ? 1u : 0u;
               break;
             }
             excl += c[tt];
@@ -546,24 +552,34 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
     }
 
     // ---- compaction of the rows not yet written. Both lanes of a group keep the same
-    // running state. Keys above the threshold: score >= f_hi; equal to it: f_lo <= score <
-    // f_hi_u; the first `left` equal keys are taken.
+    // running state. Keys above the threshold: score >= f_hi; equal to it: score == f_eq (NaN:
+    // none); the first `left` equal keys are taken.
     const int gs = st_npass[g];
     const bool writes = st_done[g] == 0;
-    float f_hi, f_hi_u, f_lo;
+    float f_hi, f_eq;
     int left;
     if (gs == kWindow) {
-      const float T = st_t[g];
-      f_lo = T;
-      f_hi = f_hi_u = next_up(T);
+      f_eq = st_t[g];
+      f_hi = next_up(f_eq);
       left = st_krem[g];
-    } else {
-      const unsigned long long pfx = gs >= 16 ? st_prefix[g] : 0xffffffffull;
-      const int shift = gs >= 16 ? 32 - 8 * (gs - 16) : 0;   // no key exceeds all-ones
+    } else if (gs >= 16) {
+      // radix: the digits fix a key prefix; every key above the prefix's range is taken, and
+      // either the whole range is needed (left equals its count) or it holds one score
+      const int shift = 32 - 8 * (gs - 16);
+      const unsigned long long pfx = st_prefix[g];
+      const float lo = key_lower_bound(pfx << shift);
       f_hi = key_lower_bound((pfx + 1) << shift);
-      f_hi_u = key_upper_bound((pfx + 1) << shift);
-      f_lo = key_lower_bound(pfx << shift);
-      left = gs >= 16 ? st_krem[g] : 0;
+      left = st_krem[g];
+      const bool single = st_single[g] != 0u;
+      f_eq = single ? lo : __builtin_nanf("");
+      if (!single) {   // the whole range: above from its lower bound on, nothing equal
+        f_hi = lo;
+        left = 0;
+      }
+    } else {   // no such group
+      f_hi = INFINITY;
+      f_eq = __builtin_nanf("");
+      left = 0;
     }
     int cnt = 0;
     int32_t* const orow = idx + geo.row_offset(b, h, gs >= 0 ? my_group : 0);
@@ -572,11 +588,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
       const int mb = t * TK_TILE + 32 * kw + 4 * hh;
       uint32_t gtm = 0, eqm = 0;   // bit e: element e above / equal
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 15; e >= 0; --e) {
         bool valid = true;
         if constexpr (kTail) valid = mb + 8 * (e >> 2) + (e & 3) < S;
-        gtm |= (uint32_t)(valid & (acc[e] >= f_hi)) << e;
-        eqm |= (uint32_t)(valid & (acc[e] >= f_lo) & (acc[e] < f_hi_u)) << e;
+        gtm = (gtm << 1) | (uint32_t)(valid & (acc[e] >= f_hi));
+        eqm = (eqm << 1) | (uint32_t)(valid & (acc[e] == f_eq));
       }
       const uint32_t both = gtm | (eqm << 16);
       const uint32_t pboth = (uint32_t)__shfl_xor((int)both, 32, 64);

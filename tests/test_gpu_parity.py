@@ -73,6 +73,53 @@ def test_topk_all_ties_takes_lowest_indices():
     assert np.array_equal(rows, np.tile(np.arange(37), (rows.shape[0], 1)))
 
 
+def _sampled_key_mask(S):
+    """Keys of the tiles the top-k samples for its threshold window: 8 tiles of 512 keys, tile
+    j * (S // 512 // 8) (include/dsv.h: selection by a sampled window, radix otherwise)."""
+    nfull = S // 512
+    ns = min(8, nfull)
+    mask = np.zeros(S, dtype=bool)
+    for j in range(ns):
+        t = j * (nfull // ns)
+        mask[512 * t:512 * (t + 1)] = True
+    return mask
+
+
+def test_topk_window_misses_fall_back_to_radix():
+    """Sampled key tiles unrepresentative (their K_lr rows zero, scores 0) so the threshold
+    window misses for groups with nonzero sums; groups whose Q_lr is zero (all scores tie at
+    0) resolve in the window. Both kinds of row bit-exact against the oracle."""
+    cfg = workload("small", heads=2)
+    say("[topk] window misses -> radix passes")
+    x = gpu_inputs(cfg, backward=False, k_per_head=[1638, 200])
+    mask = torch.from_numpy(_sampled_key_mask(cfg.seq)).to(x["k_lr"].device)
+    x["k_lr"][:, :, mask, :] = 0
+    mem = torch.from_numpy(members(cfg)).to(x["q_lr"].device)
+    for g in range(0, cfg.n_groups, 5):   # every fifth group: all its scores tie at 0
+        x["q_lr"][:, :, mem[g], :] = 0
+    idx = run_topk(cfg, x)
+    torch.cuda.synchronize()
+    for h in range(cfg.heads):
+        assert np.array_equal(gpu_rows(cfg, x, idx, 0, h), oracle_rows(cfg, x, 0, h)), h
+
+
+def test_topk_half_integer_scores_verify_and_retry():
+    """Half-integer K_lr entries make scores that share a one-unit window bin without being
+    equal: the window's count check fails and the rows are redone by the radix passes. The
+    scores are still exact (multiples of 1/2), so the rows are compared bit for bit."""
+    cfg = workload("small", heads=2, frames=8, height=16, width=16)
+    say("[topk] half-integer scores -> verified retry")
+    x = gpu_inputs(cfg, backward=False, k_per_head=[256, 61])
+    g = torch.Generator(device=x["k_lr"].device)
+    g.manual_seed(5)
+    half = torch.rand(x["k_lr"].shape, generator=g, device=x["k_lr"].device) < 0.3
+    x["k_lr"] = torch.where(half, x["k_lr"] + 0.5, x["k_lr"]).contiguous()
+    idx = run_topk(cfg, x)
+    torch.cuda.synchronize()
+    for h in range(cfg.heads):
+        assert np.array_equal(gpu_rows(cfg, x, idx, 0, h), oracle_rows(cfg, x, 0, h)), h
+
+
 def test_topk_repeatable_bitwise():
     cfg = workload("small", heads=4)
     x = gpu_inputs(cfg, backward=False)
