@@ -93,6 +93,31 @@ def topk_row_is_exact(sigma_row: np.ndarray, row: np.ndarray, k: int) -> bool:
     return bool(np.array_equal(ties_sel, ties_all[: ties_sel.size]))
 
 
+def topk_rows_are_exact(sigma: np.ndarray, rows: np.ndarray, k: int) -> np.ndarray:
+    """topk_row_is_exact for every row at once ([NG] bool), in a few passes over sigma.
+
+    With T the smallest selected score of a row: the row is the sort's answer iff it is strictly
+    ascending with k entries in [0, S), every key scoring above T is selected (as many keys
+    above T in the whole row as among the selected), and the selected keys scoring T are all
+    the keys scoring T up to the largest selected one (then they are the lowest-index ties)."""
+    sigma = np.asarray(sigma)
+    NG, S = sigma.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    if rows.shape != (NG, k):
+        return np.zeros(NG, dtype=bool)
+    ok = np.all(np.diff(rows, axis=1) > 0, axis=1) & (rows[:, 0] >= 0) & (rows[:, -1] < S)
+    rc = np.clip(rows, 0, S - 1)
+    sel = np.take_along_axis(sigma, rc, axis=1)
+    T = sel.min(axis=1)[:, None]
+    above_all = np.count_nonzero(sigma > T, axis=1)
+    above_sel = np.count_nonzero(sel > T, axis=1)
+    tie_sel = sel == T
+    n_tie_sel = np.count_nonzero(tie_sel, axis=1)
+    last_tie = np.where(tie_sel, rc, -1).max(axis=1)[:, None]
+    n_tie_upto = np.count_nonzero((sigma == T) & (np.arange(S)[None, :] <= last_tie), axis=1)
+    return ok & (above_all == above_sel) & (n_tie_upto == n_tie_sel)
+
+
 def idx_row_offsets(B: int, H: int, NG: int, k_per_head) -> np.ndarray:
     """int64 [B, H]: start of the (b, h) block in the packed idx array (rows of k_h, no padding)."""
     k = np.asarray(k_per_head, dtype=np.int64)

@@ -58,31 +58,16 @@ def gpu_rows(cfg, x, idx, b, h):
 
 
 def characterise_all_rows(cfg, x, idx, b, h, mem=None) -> int:
-    """Number of rows of (b, h) that fail the exact top-k characterisation (sum-first scores,
-    which the CPU tests pin to the brute-force definition)."""
+    """Number of rows of (b, h) that fail the exact top-k characterisation
+    (oracle.topk.topk_rows_are_exact on sum-first scores, which the CPU tests pin to the
+    brute-force definition; the integer scores are held as int32, exactly)."""
     mem = members(cfg) if mem is None else mem
     sig = otopk.group_scores_sum_first(f64(x["q_lr"][b, h]), f64(x["k_lr"][b, h]), mem)
+    if np.all(sig == np.round(sig)) and np.abs(sig).max() < 2 ** 31:
+        sig = sig.astype(np.int32)
     rows = gpu_rows(cfg, x, idx, b, h)
     kh = int(x["k_per_head"][h])
-    bad = 0
-    NG, S = sig.shape
-    # vectorised characterisation over all rows at once
-    if rows.shape != (NG, kh) or np.any(np.diff(rows, axis=1) <= 0) or rows.min() < 0 \
-            or rows.max() >= S:
-        return NG
-    mask = np.zeros((NG, S), dtype=bool)
-    np.put_along_axis(mask, rows, True, axis=1)
-    sel_min = np.where(mask, sig, np.inf).min(axis=1)
-    uns_max = np.where(mask, -np.inf, sig).max(axis=1)
-    bad_rows = uns_max > sel_min
-    # ties at the threshold: selected ties must be a prefix of all ties in index order
-    eqT = sig == sel_min[:, None]
-    sel_eq = eqT & mask
-    n_sel_eq = sel_eq.sum(axis=1)
-    rank_eq = np.cumsum(eqT, axis=1)   # 1-based rank of each tie among the row's ties
-    bad_ties = np.any(sel_eq & (rank_eq > n_sel_eq[:, None]), axis=1)
-    bad = int(np.sum(bad_rows | bad_ties))
-    return bad
+    return int(np.count_nonzero(~otopk.topk_rows_are_exact(sig, rows, kh)))
 
 
 def run_fwd(cfg, x, idx):

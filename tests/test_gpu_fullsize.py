@@ -7,6 +7,8 @@ The oracle cannot run every output at these sizes in seconds, so:
   * backward: dQ on sampled groups, dK/dV of one full head (all groups' contributions), and
     the sum rules on every head.
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -25,12 +27,19 @@ def _sampled_groups(NG, n, seed):
     return sorted(set([0, NG - 1] + rng.choice(NG, size=n, replace=False).tolist()))
 
 
+def _characterise_heads(cfg, x, idx, heads, mem):
+    """The exact characterisation on every row of the given (b, h) slots, 8 host threads."""
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        bad = list(ex.map(lambda bh: characterise_all_rows(cfg, x, idx, bh[0], bh[1], mem),
+                          heads))
+    for (b, h), nb in zip(heads, bad):
+        assert nb == 0, (b, h, nb)
+
+
 def _topk_checks(cfg, x, idx, heads=None, brute_groups=3, seed=0):
     mem = members(cfg)
     heads = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)] if heads is None else heads
-    for b, h in heads:
-        bad = characterise_all_rows(cfg, x, idx, b, h, mem)
-        assert bad == 0, (b, h, bad)
+    _characterise_heads(cfg, x, idx, heads, mem)
     b, h = heads[0]
     rows = gpu_rows(cfg, x, idx, b, h)
     for g in _sampled_groups(cfg.n_groups, brute_groups, seed):
@@ -104,45 +113,59 @@ def test_long_heterogeneous_topk_fwd():
     assert len(set(ks)) > 1
     idx = run_topk(cfg, x)
     torch.cuda.synchronize()
+    # every row of every head (the heaviest first for the brute-force samples)
     heavy = int(np.argmax(ks))
-    light = int(np.argmin(ks))
-    _topk_checks(cfg, x, idx, heads=[(0, heavy), (0, light)] +
-                 [(0, h) for h in range(0, cfg.heads, 3)])
+    _topk_checks(cfg, x, idx, heads=[(0, heavy)] + [(0, h) for h in range(cfg.heads)
+                                                     if h != heavy])
     o, lse = run_fwd(cfg, x, idx)
     torch.cuda.synchronize()
     _fwd_sampled(cfg, x, idx, o, lse, n_groups=3)
 
 
+@pytest.mark.timeout(1200)
 def test_training_steps():
+    """20 seeded steps with fresh inputs: every row of every (b, h) slot characterised on every
+    step; the forward on sampled groups of two slots per step; the backward of one slot per
+    step against the gathered oracle (the slot rotating over the steps): dQ, dK and dV of the
+    whole slot on steps 0, 5, 10, 15 and 19, dQ of sampled groups on the others."""
     cfg = workload("training")
     say("[full] training: 2 x S=61440, 24 heads, k=5%, 20 seeded steps")
+    mem = members(cfg)
+    slots = [(b, h) for b in range(cfg.batch) for h in range(cfg.heads)]
+    worst = {"fwd": 0.0, "dq": 0.0, "dk": 0.0, "dv": 0.0}
     for step in range(cfg.steps):
         x = gpu_inputs(cfg, step=step, backward=True)
         idx = run_topk(cfg, x)
         o, lse = run_fwd(cfg, x, idx)
         dq, dk, dv = run_bwd(cfg, x, idx, o, lse)
         torch.cuda.synchronize()
-        if step == 0:
-            _topk_checks(cfg, x, idx, brute_groups=2)
-            _fwd_sampled(cfg, x, idx, o, lse, n_groups=2)
-            b, h = 1, 7
+        _characterise_heads(cfg, x, idx, slots, mem)
+        if step == 0:   # brute-force group scores on sampled groups of one slot
+            _topk_checks(cfg, x, idx, heads=[slots[0]], brute_groups=2)
+        for b, h in (slots[(5 * step) % len(slots)], slots[(5 * step + 29) % len(slots)]):
             rows = gpu_rows(cfg, x, idx, b, h)
-            rq, rk, rv = oracle_bwd(cfg, x, rows, b, h, mem=members(cfg))
+            groups = _sampled_groups(cfg.n_groups, 2, 400 + step)
+            ro, rl = oracle_fwd(cfg, x, rows, b, h, groups=groups, mem=mem)
+            e = max(maxerr(f64(o[b, h]), ro), maxerr(f64(lse[b, h]), rl))
+            worst["fwd"] = max(worst["fwd"], e)
+            assert e <= TOL["bf16"], (step, b, h, e)
+        b, h = slots[(7 * step + 3) % len(slots)]
+        rows = gpu_rows(cfg, x, idx, b, h)
+        if step % 5 == 0 or step == cfg.steps - 1:   # the whole slot: dQ, dK and dV
+            rq, rk, rv = oracle_bwd(cfg, x, rows, b, h, mem=mem)
             e = (maxerr(f64(dq[b, h]), rq), maxerr(f64(dk[b, h]), rk),
                  maxerr(f64(dv[b, h]), rv))
-            say(f"   step 0 bwd (b={b}, h={h}) max-abs-err {e}")
-            assert max(e) <= TOL["bf16"], e
-        else:
-            # every step: exact top-k characterisation on two heads, one sampled fwd group
-            hs = [(step % 2, (3 * step) % cfg.heads), ((step + 1) % 2, (7 * step + 1) % cfg.heads)]
-            _topk_checks(cfg, x, idx, heads=hs, brute_groups=0, seed=step)
-            b, h = hs[0]
-            rows = gpu_rows(cfg, x, idx, b, h)
-            ro, _ = oracle_fwd(cfg, x, rows, b, h, groups=[step % cfg.n_groups])
-            assert maxerr(f64(o[b, h]), ro) <= TOL["bf16"]
-        say(f"   step {step} ok")
+        else:                                      # dQ of sampled groups
+            groups = _sampled_groups(cfg.n_groups, 3, 500 + step)
+            rq, _, _ = oracle_bwd(cfg, x, rows, b, h, groups=groups, mem=mem)
+            e = (maxerr(f64(dq[b, h]), rq),)
+        for name, v in zip(("dq", "dk", "dv"), e):
+            worst[name] = max(worst[name], v)
+        assert max(e) <= TOL["bf16"], (step, b, h, e)
+        say(f"   step {step}: 48 slots characterised; bwd (b={b}, h={h}) max-abs-err {e}")
         del x, idx, o, lse, dq, dk, dv
         torch.cuda.empty_cache()
+    say(f"   worst over 20 steps: {worst}")
 
 
 def test_mid_adaptive_k_sampled_groups():

@@ -159,6 +159,53 @@ def test_characterisation_agrees_with_sort_and_rejects_mistakes(seed):
         assert not topk.topk_row_is_exact(sig[g], row[:-1], k)        # too short
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_batched_characterisation_equals_the_row_check(seed):
+    """topk_rows_are_exact (all rows at once) gives the per-row check's verdict on the sort's
+    answer and on planted mistakes: a tie swapped for a later tie, a lower-scoring key, a
+    duplicate, a key out of range, a descending row, a row of the wrong length."""
+    rng = np.random.default_rng(200 + seed)
+    S, NG = 257, 12
+    sig = rng.integers(-9, 10, size=(NG, S)).astype(np.int64)
+    for k in (1, 13, 128, 256, 257):
+        rows = topk.topk_rows_by_sort(sig.astype(float), k)
+        assert topk.topk_rows_are_exact(sig, rows, k).all()
+        assert topk.topk_rows_are_exact(sig.astype(float), rows, k).all()
+    k = 50
+    rows = topk.topk_rows_by_sort(sig.astype(float), k)
+    planted = []
+    for g in range(NG):
+        row = rows[g].copy()
+        T = sig[g, row].min()
+        kind = g % 6
+        if kind == 0:
+            ties_out = [m for m in np.flatnonzero(sig[g] == T) if m not in set(row)]
+            sel_ties = [m for m in row if sig[g, m] == T]
+            if not ties_out:
+                planted.append(row)
+                continue
+            row = np.sort(np.array([m for m in row if m != sel_ties[-1]] + [ties_out[-1]]))
+        elif kind == 1:
+            lower = np.flatnonzero(sig[g] < T)
+            row = np.sort(np.concatenate([row[1:], lower[:1]]))
+        elif kind == 2:
+            row[5] = row[4]                       # duplicate
+        elif kind == 3:
+            row[-1] = S                           # out of range
+        elif kind == 4:
+            row = row[::-1].copy()                # descending
+        else:
+            pass                                  # the correct row
+        planted.append(row)
+    planted = np.stack(planted)
+    want = np.array([topk.topk_row_is_exact(sig[g].astype(float), planted[g], k)
+                     for g in range(NG)])
+    got = topk.topk_rows_are_exact(sig, planted, k)
+    assert np.array_equal(got, want)
+    assert not want[1] and not want[2] and not want[3] and not want[4] and want[5]
+    assert not topk.topk_rows_are_exact(sig, rows[:, :-1], k).any()   # wrong length
+
+
 def test_packed_layout_offsets_heterogeneous_k():
     B, H, NG = 2, 3, 5
     kph = [4, 1, 7]
