@@ -16,7 +16,13 @@ ARCH = os.environ.get("DSV_OFFLOAD_ARCH", "gfx950")
 # The forward keeps its output accumulators in VGPRs (MFMA results written to VGPRs, not
 # AGPRs): its lazy rescale multiplies them with VALU ops, and with AGPR accumulators the
 # compiler copies all of them to VGPRs on every chunk, rescaled or not.
-EXTRA_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# The backward's staging format is chosen per chunk by a branch that is the same in every
+# lane; left unstructurized (a plain if/else), the compiler's waits for the prefetched K/V
+# rows at the top of its loop leave the previous chunk's stores in flight. With MFMA results
+# in VGPRs it also fits in 512 registers without spilling.
+EXTRA_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
+                                "-mllvm", "-structurizecfg-skip-uniform-regions=true"]}
 
 
 def hipcc() -> str:

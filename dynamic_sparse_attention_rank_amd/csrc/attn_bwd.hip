@@ -20,10 +20,14 @@
 //     dS^T from a [key][member] LDS tile read back transposed. dQ is written once.
 //   * dK/dV: each (group, selected key) edge yields one row of dV and one of dK, summed over
 //     all groups that selected the key. fp32 atomics on this chip sustain only ~0.33 T adds/s,
-//     so the rows are not added in place. The edge (g, p) owns staging row g*padded_k + p:
-//     fp16 entries with one power-of-two scale per 16-key block from a-priori bounds
-//     (|dV| <= sum P * max|dO|, |dK| <= scale * sum|dS| * max|Q|), so each entry keeps a
-//     relative error <= 2^-11. The rows are written with whole-line non-temporal stores.
+//     so the rows are not added in place. The edge (g, p) owns staging row g*padded_k + p.
+//     A-priori bounds per 16-key block (|dV| <= sum P * max|dO|, |dK| <= scale * sum|dS| *
+//     max|Q|) choose its format per 32-key chunk: at d = 128, where both bounds of both blocks
+//     are at most kStage8Bound, the rows are 8-bit codes with one scale per block from the
+//     block's largest entry m (absolute error <= m/254 <= kStage8Bound/254 per entry);
+//     elsewhere fp16 entries with one power-of-two scale per block (relative error <= 2^-11).
+//     The rows are written with whole-line non-temporal stores, the block scales to a small
+//     table that the reduce reads through L2.
 //     Small pre-passes list, for every 32-key bucket, its edges in (group, position) order;
 //     a reduce kernel then sums each bucket's rows in LDS (one wave per bucket and half, one
 //     row per instruction, no atomics) and writes every dK/dV row exactly once, so dK/dV are
@@ -34,6 +38,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "dsv_internal.h"
@@ -63,6 +68,12 @@ constexpr int kMaxChunk = 64;    // (b, h) slots per chunk
 // kStageMax (fp16 reaches 65504), and fp16's 11-bit significand gives each entry a relative
 // error <= 2^-11 whatever its size, down to 2^-28 of the bound where fp16 turns subnormal.
 constexpr float kStageMax = 16384.f;
+// Chunks whose dV and dK bounds are all within kStage8Bound are staged as 8-bit rows (d = 128):
+// code = 128 + round(x * 127 / m) with m the largest |x| of the 16-key block, so every entry is
+// off by at most m/254 <= kStage8Bound/254 ~ 2e-3, and a row takes half the bytes of fp16.
+constexpr float kStage8Bound = 0.5f;
+template <int D>
+constexpr bool kStage8 = D == 128;
 
 // kStageMax / bound rounded down to a power of two (clamped to [2^-126, 2^100]); 0 if bound
 // is not positive.
@@ -273,16 +284,20 @@ __global__ void fill_zero(float4* __restrict__ p, long long n4) {
 
 // Sum each bucket's staging rows: one wave per (slot, bucket, half), half 0 = dV, 1 = dK.
 // Lane l owns features (D/64)*l .. of the half; the bucket's key rows accumulate in LDS.
-// Each step takes 64 entries of the bucket's edge list (edge row, key, step: one per lane),
-// then walks them one row per instruction, so no two lanes ever touch the same LDS word and
-// rows with equal keys are added in list order. The step's 64 row loads are issued at once,
-// and the next step's entries and steps are requested during this one. Every key row of the
-// bucket is then written once (zero where no group selected the key).
+// Each step takes 64 entries of the bucket's edge list (edge row, key, row factor: one per
+// lane), then walks them one row per instruction, so no two lanes ever touch the same LDS word
+// and rows with equal keys are added in list order. The step's 64 row loads are issued at
+// once, and the next step's entries and factors are requested during this one. Every key row
+// of the bucket is then written once (zero where no group selected the key).
+// A row's factor f (one per 16-row block) says its format: sign bit clear, fp16 entries times
+// f; set (d = 128 only), 8-bit codes c with entry (c - 128) * |f|. Both kinds sit at the start of the row's 2d-byte
+// slot; each lane loads one 32-bit word of it, at byte 4l (fp16) or 4(l/2) (8-bit: the lane
+// takes half of the word), and adds its two entries into the LDS slots of their features.
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 template <int D>
 __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__ off,
                                                    const uint32_t* __restrict__ perm,
-                                                   const float2* __restrict__ bstep,
+                                                   const float2* __restrict__ bfac,
                                                    const uint16_t* __restrict__ cv,
                                                    const uint16_t* __restrict__ ck, Chunk ch,
                                                    float* __restrict__ dk, float* __restrict__ dv,
@@ -307,60 +322,116 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
   const long long s0 = std::min<long long>(o[j], nrows);
   const long long s1 = std::min<long long>(std::max<long long>(o[j + 1], o[j]), nrows);
   const uint32_t* pm = perm + eb;
-  const uint16_t* src = (half ? ck : cv) + eb * D + FPL * lane;
+  const unsigned char* src =
+      reinterpret_cast<const unsigned char*>(half ? ck : cv) + eb * (2 * D);
   const int key0 = j * kBucket;
+  // LDS slots. d = 64 (fp16 rows only): slot = staging position, lane l owns position l.
+  // d = 128: feature F = 16w + 4g + j (w < 8, g < 4, j < 4) has the pair index
+  // P = 16g + 2w + j/2, the order of an 8-bit row (lane l loads its bytes 2l, 2l + 1: P = l),
+  // and its slot is 2P' + j%2 with P' = P ^ 8 [P >= 32]. An fp16 row gives lane l the staging
+  // positions 2l, 2l + 1, i.e. P = 16((l/4)%4) + 4(l/16) + 2((l/2)%2) + l%2. The swap of bit 3
+  // in the upper half makes both lane patterns hit 32 distinct bank pairs in each half-wave.
+  auto swz_pair = [](int P) { return P ^ (((P >> 5) & 1) << 3); };
+  const int o16 = 2 * FPL * lane, o8 = 4 * (lane >> 1);
+  const int a16 = kStage8<D> ? 2 * swz_pair(16 * ((lane >> 2) & 3) + 4 * (lane >> 4) +
+                                            2 * ((lane >> 1) & 1) + (lane & 1))
+                             : FPL * lane;
+  const int a8 = 2 * swz_pair(lane);
+  const int sh8 = 16 * (lane & 1);
   // entry -> slot-relative staging row (clamped into the slot)
   auto row_of = [&](uint32_t ent) { return std::min<uint32_t>(ent >> 5, (uint32_t)(nrows - 1)); };
   if (s1 > s0) {
-    // the first block's entries and steps; afterwards each block requests the next block's
-    // entries at its start and their steps after its row loads, so that both have arrived
+    // the first block's entries and factors; afterwards each block requests the next block's
+    // entries at its start and their factors after its row loads, so that both have arrived
     // when the next block starts (all loads unconditional, positions clamped)
     uint32_t ent = pm[std::min<long long>(s0 + lane, s1 - 1)];
-    float2 st = bstep[(eb + row_of(ent)) >> 4];
+    float2 st = bfac[(eb + row_of(ent)) >> 4];
     for (long long r0 = s0; r0 < s1; r0 += 64) {
       const int n = (int)std::min<long long>(64, s1 - r0);
-      // lanes past the end repeat the last entry and add it with step 0
+      // lanes past the end repeat the last entry and add it with a zero factor of its format
       const uint32_t e = row_of(ent);
       const int kk = (int)(ent & 31u);
-      const float sc = lane < n ? (half ? st.y : st.x) : 0.f;
+      const float f0 = half ? st.y : st.x;
+      const float sc = lane < n ? f0 : copysignf(0.f, f0);
       const uint32_t ent_n = pm[std::min<long long>(r0 + 64 + lane, s1 - 1)];
+      // the step's formats: all fp16 (0), all 8-bit (1) or mixed (2), the same in every lane
+      const uint64_t m8 = __builtin_amdgcn_ballot_w64(__float_as_int(sc) < 0);
+      const int mode = !kStage8<D> || m8 == 0 ? 0 : m8 == ~0ull ? 1 : 2;
       uint32_t x[64];
+      auto load_rows = [&](auto mc) {
+        constexpr int MODE = decltype(mc)::value;
 #pragma unroll
-      for (int u = 0; u < 64; ++u) {
-        const uint32_t eu = __builtin_amdgcn_readlane(e, u);
-        // staging rows are read once: non-temporal, so they do not displace other lines
-        if constexpr (FPL == 2)
-          x[u] = __builtin_nontemporal_load(
-              reinterpret_cast<const uint32_t*>(src + (long long)eu * D));
-        else
-          x[u] = (uint16_t)__builtin_nontemporal_load(src + (long long)eu * D);
-      }
-      const float2 st_n = bstep[(eb + row_of(ent_n)) >> 4];
-#pragma unroll
-      for (int u = 0; u < 64; ++u) {
-        const int ku = __builtin_amdgcn_readlane(kk, u);
-        const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), u));
-        float* a = acc + ku * D + FPL * lane;
-        if constexpr (FPL == 2) {
-          float2 w = *reinterpret_cast<float2*>(a);
-          w.x += su * f16_lo(x[u]);
-          w.y += su * f16_hi(x[u]);
-          *reinterpret_cast<float2*>(a) = w;
-        } else {
-          a[0] += su * f16_lo(x[u]);
+        for (int u = 0; u < 64; ++u) {
+          const uint32_t eu = __builtin_amdgcn_readlane(e, u);
+          // staging rows are read once: non-temporal, so they do not displace other lines
+          const unsigned char* rp = src + (long long)eu * (2 * D);
+          if constexpr (FPL == 1) {
+            x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(rp + o16));
+          } else {
+            if constexpr (MODE == 1) {   // the lane's two codes
+              x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(rp + 2 * lane));
+            } else {
+              int ob = o16;
+              if constexpr (MODE == 2)   // word lane/2 of an 8-bit row, word lane of an fp16 row
+                ob = 4 * (lane >> ((__builtin_amdgcn_readlane(__float_as_int(sc), u) >> 31) & 1));
+              x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(rp + ob));
+            }
+          }
         }
-      }
+      };
+      auto add_rows = [&](auto mc) {
+        constexpr int MODE = decltype(mc)::value;
+#pragma unroll
+        for (int u = 0; u < 64; ++u) {
+          const int ku = __builtin_amdgcn_readlane(kk, u);
+          const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), u));
+          if constexpr (FPL == 1) {
+            acc[ku * D + a16] += su * f16_lo(x[u]);
+          } else if (MODE == 1 || (MODE == 2 && __float_as_int(su) < 0)) {
+            const uint32_t w = MODE == 1 ? x[u] : x[u] >> sh8;
+            float* a = acc + ku * D + a8;
+            float2 v = *reinterpret_cast<float2*>(a);
+            const float c = 128.f * su;   // f = su < 0: (code - 128) * |f| = c - code * f
+            v.x += fmaf((float)(w & 0xffu), -su, c);
+            v.y += fmaf((float)((w >> 8) & 0xffu), -su, c);
+            *reinterpret_cast<float2*>(a) = v;
+          } else {
+            float* a = acc + ku * D + a16;
+            float2 v = *reinterpret_cast<float2*>(a);
+            v.x += su * f16_lo(x[u]);
+            v.y += su * f16_hi(x[u]);
+            *reinterpret_cast<float2*>(a) = v;
+          }
+        }
+      };
+      using M0 = std::integral_constant<int, 0>;
+      using M1 = std::integral_constant<int, 1>;
+      using M2 = std::integral_constant<int, 2>;
+      if (mode == 1) load_rows(M1{});
+      else if (mode == 0) load_rows(M0{});
+      else load_rows(M2{});
+      const float2 st_n = bfac[(eb + row_of(ent_n)) >> 4];
+      if (mode == 1) add_rows(M1{});
+      else if (mode == 0) add_rows(M0{});
+      else add_rows(M2{});
       ent = ent_n;
       st = st_n;
     }
   }
   __syncthreads();
   const int nk = min(kBucket, geo.S - key0);
-  // staging position FPL*lane holds feature 32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4
-  // (position 32fp + 8lg + t); FPL consecutive positions stay consecutive features
-  const int pos = FPL * lane;
-  const int t8 = pos & 7;
-  const int feat = (pos & ~31) + 4 * ((pos >> 3) & 3) + (t8 < 4 ? t8 : 12 + t8);
+  // slots FPL*lane.. back to features. d = 128: pair P = swz_pair(lane) is feature
+  // 16((P/2)%8) + 4(P/16) + 2(P%2) and the next one. d = 64: staging position l holds feature
+  // 32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4 (position 32fp + 8lg + t).
+  int feat;
+  if constexpr (kStage8<D>) {
+    const int P = swz_pair(lane);
+    feat = 16 * ((P >> 1) & 7) + 4 * (P >> 4) + 2 * (P & 1);
+  } else {
+    const int pos = FPL * lane;
+    const int t8 = pos & 7;
+    feat = (pos & ~31) + 4 * ((pos >> 3) & 3) + (t8 < 4 ? t8 : 12 + t8);
+  }
   float* out = (half ? dk : dv) + bh * geo.S * D + (long long)key0 * D + feat;
   for (int l = 0; l < nk; ++l) {
     if constexpr (FPL == 2)
@@ -390,7 +461,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     const uint16_t* v, const uint16_t* __restrict__ o,   // prefetch stays ordered (see below)
     const uint16_t* __restrict__ d_o, const float* __restrict__ lse,
     const int32_t* __restrict__ idx, float scale, float* __restrict__ dq, Chunk ch,
-    uint16_t* __restrict__ cv, uint16_t* __restrict__ ck, float2* __restrict__ bstep, Geom geo) {
+    uint16_t* __restrict__ cv, uint16_t* __restrict__ ck, float2* __restrict__ bfac, Geom geo) {
   constexpr int QBP = (QB + 1) & ~1;   // query blocks padded to whole 32-query k-steps
   constexpr int NM = QBP / 2;
   constexpr int KS = D / 32;
@@ -518,6 +589,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     };
     u32x4 pa[2][NM], dsa[2][NM];
     float2 step[2];
+    bool ok8[2];   // block kb may be staged in 8 bits (both bounds within kStage8Bound)
     // ---- P, dS of block kb, their fp16 staging scales, the dV / dK operands and the dS tile
     auto softmax = [&](const int kb, const floatx4 (&s)[QB], const floatx4 (&dp)[QB]) {
       const bool kvalid = cb + 16 * kb + li < kh;
@@ -559,6 +631,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         cd = max_in_row16(sum_over_rows(cd));
         const float sv = pow2_scale(cp * max_do);
         const float sk = pow2_scale(cd * max_q);   // dK = scale * (sum dS q): scale in the step
+        ok8[kb] = cp * max_do <= kStage8Bound && cd * max_q * scale <= kStage8Bound;
         // sv, sk are powers of two, so their reciprocals are exact
         step[kb] = make_float2(sv > 0.f ? __builtin_amdgcn_rcpf(sv) : 0.f,
                                sk > 0.f ? __builtin_amdgcn_rcpf(sk) * scale : 0.f);
@@ -612,11 +685,6 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     asm volatile("" ::: "memory");
     softmax(1, s1, dp1);
 
-    // both blocks' steps in one 16-byte store by every lane (one address, unconditional);
-    // (grow + cb) is a multiple of 32, so the pair is 16-byte aligned
-    *reinterpret_cast<float4*>(&bstep[(grow + cb) / 16]) =
-        make_float4(step[0].x, step[0].y, step[1].x, step[1].y);
-
     // ---- dQ^T += K^T dS^T; the B operand dS^T is read from the LDS tile in the key order
     // of the K^T operands
     wave_lds_fence();   // dS tile complete
@@ -639,73 +707,157 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
 
     // ---- dV^T = dO^T P, dK^T = Q^T dS (pre-scaled, see above). A operands by transposed LDS
     // reads: row li <-> feature 16fb + li, slot (lg, e) <-> member 32m + 16(e/4) + 4lg + e%4.
-    // Lane: key 16kb + li, features 16fb + 4lg + j. Feature blocks go in pairs (2fp, 2fp + 1)
-    // so that every lane holds 16-byte granules: staging position 32fp + 8lg + t holds feature
-    // 32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4 (t >= 4); the reduce undoes this order.
-    // The rows are written once and read back by the reduce long after, so the stores are
-    // non-temporal and cover whole 128-byte lines (half-line non-temporal stores are far
-    // slower); they are the bulk of this kernel's HBM traffic.
-    u32x4 xv[2], xk[2];   // granules of the even feature-block pair, held for the line swap
+    // Lane: key 16kb + li, features 16fb + 4lg + j. The rows are written once and read back by
+    // the reduce long after, so the stores are non-temporal and cover whole 128-byte lines
+    // (half-line non-temporal stores are far slower); they are the bulk of this kernel's HBM
+    // traffic. fac[t][kb]: the factor the reduce applies to the staged entries of tensor t
+    // (0 = dV, 1 = dK) in block kb, negative (sign bit set) for 8-bit blocks.
+    float fac[2][2];
+    auto stage_f16 = [&]() {
+      // Feature blocks go in pairs (2fp, 2fp + 1) so that every lane holds 16-byte granules:
+      // staging position 32fp + 8lg + t holds feature 32fp + 4lg + t (t < 4) or
+      // 32fp + 16 + 4lg + t - 4 (t >= 4); the reduce undoes this order.
+      u32x4 xv[2], xk[2];   // granules of the even feature-block pair, held for the line swap
 #pragma unroll
-    for (int fp = 0; fp < NDB / 2; ++fp) {
-      floatx4 av[2][2], ak[2][2];
+      for (int fp = 0; fp < NDB / 2; ++fp) {
+        floatx4 av[2][2], ak[2][2];
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) av[h2][kb] = ak[h2][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+          for (int kb = 0; kb < 2; ++kb) av[h2][kb] = ak[h2][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int fb = 2 * fp + h2;
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int fb = 2 * fp + h2;
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const int r1 = 32 * m + 4 * lg + (li >> 2);
-          const int col = 16 * fb + 4 * (li & 3);
-          const u32x2 d1 = lds_read_tr16(&lds.dn[swz<D>(r1, col)]);
-          const u32x2 d2 = lds_read_tr16(&lds.dn[swz<D>(r1 + 16, col)]);
-          const u32x2 q1 = lds_read_tr16(&lds.qn[swz<D>(r1, col)]);
-          const u32x2 q2 = lds_read_tr16(&lds.qn[swz<D>(r1 + 16, col)]);
-          const u32x4 adoT = {d1[0], d1[1], d2[0], d2[1]};
-          const u32x4 aqT = {q1[0], q1[1], q2[0], q2[1]};
+          for (int m = 0; m < NM; ++m) {
+            const int r1 = 32 * m + 4 * lg + (li >> 2);
+            const int col = 16 * fb + 4 * (li & 3);
+            const u32x2 d1 = lds_read_tr16(&lds.dn[swz<D>(r1, col)]);
+            const u32x2 d2 = lds_read_tr16(&lds.dn[swz<D>(r1 + 16, col)]);
+            const u32x2 q1 = lds_read_tr16(&lds.qn[swz<D>(r1, col)]);
+            const u32x2 q2 = lds_read_tr16(&lds.qn[swz<D>(r1 + 16, col)]);
+            const u32x4 adoT = {d1[0], d1[1], d2[0], d2[1]};
+            const u32x4 aqT = {q1[0], q1[1], q2[0], q2[1]};
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            av[h2][kb] = mfma_bf16(adoT, pa[kb][m], av[h2][kb]);
-            ak[h2][kb] = mfma_bf16(aqT, dsa[kb][m], ak[h2][kb]);
+            for (int kb = 0; kb < 2; ++kb) {
+              av[h2][kb] = mfma_bf16(adoT, pa[kb][m], av[h2][kb]);
+              ak[h2][kb] = mfma_bf16(aqT, dsa[kb][m], ak[h2][kb]);
+            }
+          }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          // row cb + 16kb + li < padded_k: past the row end it is a (zero) padding row
+          const u32x4 wv = {pack_f16(av[0][kb][0], av[0][kb][1]), pack_f16(av[0][kb][2], av[0][kb][3]),
+                            pack_f16(av[1][kb][0], av[1][kb][1]), pack_f16(av[1][kb][2], av[1][kb][3])};
+          const u32x4 wk = {pack_f16(ak[0][kb][0], ak[0][kb][1]), pack_f16(ak[0][kb][2], ak[0][kb][3]),
+                            pack_f16(ak[1][kb][0], ak[1][kb][1]), pack_f16(ak[1][kb][2], ak[1][kb][3])};
+          if ((fp & 1) == 0) {
+            xv[kb] = wv;
+            xk[kb] = wk;
+          } else {
+            // a lane holds granules 8p + lg (even fp) and 8p + 4 + lg (odd fp) of row li; after
+            // swapping with lane li ^ 8 every store writes 8 whole 128-byte lines: rows
+            // 16kb + (li & 7) (first) and 16kb + (li & 7) + 8 (second), granule 8p + 4(li / 8) + lg
+            // DPP row_ror:8 with a bank mask: lanes 8..15 of each row (banks 2, 3) take the
+            // odd granule of lane li - 8, lanes 0..7 (banks 0, 1) the even granule of lane li + 8
+            u32x4 av1, av2, ak1, ak2;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              av1[w] = __builtin_amdgcn_update_dpp(xv[kb][w], wv[w], 0x128, 0xf, 0xc, false);
+              av2[w] = __builtin_amdgcn_update_dpp(wv[w], xv[kb][w], 0x128, 0xf, 0x3, false);
+              ak1[w] = __builtin_amdgcn_update_dpp(xk[kb][w], wk[w], 0x128, 0xf, 0xc, false);
+              ak2[w] = __builtin_amdgcn_update_dpp(wk[w], xk[kb][w], 0x128, 0xf, 0x3, false);
+            }
+            const long long ra = grow + cb + 16 * kb + (li & 7);
+            const int gcol = 8 * (8 * (fp >> 1) + 4 * (li >> 3) + lg);
+            __builtin_nontemporal_store(av1, reinterpret_cast<u32x4*>(cv + ra * D + gcol));
+            __builtin_nontemporal_store(av2, reinterpret_cast<u32x4*>(cv + (ra + 8) * D + gcol));
+            __builtin_nontemporal_store(ak1, reinterpret_cast<u32x4*>(ck + ra * D + gcol));
+            __builtin_nontemporal_store(ak2, reinterpret_cast<u32x4*>(ck + (ra + 8) * D + gcol));
           }
         }
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        // row cb + 16kb + li < padded_k: past the row end it is a (zero) padding row
-        const u32x4 wv = {pack_f16(av[0][kb][0], av[0][kb][1]), pack_f16(av[0][kb][2], av[0][kb][3]),
-                          pack_f16(av[1][kb][0], av[1][kb][1]), pack_f16(av[1][kb][2], av[1][kb][3])};
-        const u32x4 wk = {pack_f16(ak[0][kb][0], ak[0][kb][1]), pack_f16(ak[0][kb][2], ak[0][kb][3]),
-                          pack_f16(ak[1][kb][0], ak[1][kb][1]), pack_f16(ak[1][kb][2], ak[1][kb][3])};
-        if ((fp & 1) == 0) {
-          xv[kb] = wv;
-          xk[kb] = wk;
-        } else {
-          // a lane holds granules 8p + lg (even fp) and 8p + 4 + lg (odd fp) of row li; after
-          // swapping with lane li ^ 8 every store writes 8 whole 128-byte lines: rows
-          // 16kb + (li & 7) (first) and 16kb + (li & 7) + 8 (second), granule 8p + 4(li / 8) + lg
-          // DPP row_ror:8 with a bank mask: lanes 8..15 of each row (banks 2, 3) take the
-          // odd granule of lane li - 8, lanes 0..7 (banks 0, 1) the even granule of lane li + 8
-          u32x4 av1, av2, ak1, ak2;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            av1[w] = __builtin_amdgcn_update_dpp(xv[kb][w], wv[w], 0x128, 0xf, 0xc, false);
-            av2[w] = __builtin_amdgcn_update_dpp(wv[w], xv[kb][w], 0x128, 0xf, 0x3, false);
-            ak1[w] = __builtin_amdgcn_update_dpp(xk[kb][w], wk[w], 0x128, 0xf, 0xc, false);
-            ak2[w] = __builtin_amdgcn_update_dpp(wk[w], xk[kb][w], 0x128, 0xf, 0x3, false);
-          }
-          const long long ra = grow + cb + 16 * kb + (li & 7);
-          const int gcol = 8 * (8 * (fp >> 1) + 4 * (li >> 3) + lg);
-          __builtin_nontemporal_store(av1, reinterpret_cast<u32x4*>(cv + ra * D + gcol));
-          __builtin_nontemporal_store(av2, reinterpret_cast<u32x4*>(cv + (ra + 8) * D + gcol));
-          __builtin_nontemporal_store(ak1, reinterpret_cast<u32x4*>(ck + ra * D + gcol));
-          __builtin_nontemporal_store(ak2, reinterpret_cast<u32x4*>(ck + (ra + 8) * D + gcol));
-        }
+        fac[0][kb] = step[kb].x;
+        fac[1][kb] = step[kb].y;
       }
-    }
+    };
+    // 8-bit rows (d = 128), one 16 x d tile (block kb of one tensor) at a time: its largest
+    // |entry| m (the lane's 32 features, the key's 3 other lanes, the block's 16 keys), then
+    // codes 128 + round(x * 127/m). Lane (li, lg) holds bytes 32lg .. 32lg + 31 of row
+    // 16kb + li: byte 32lg + 4fb + j <-> feature 16fb + 4lg + j. The same lane swap as the fp16
+    // rows makes every store cover 8 whole lines.
+    auto stage_8 = [&]() {
+      if constexpr (kStage8<D>) {
+        const long long r0 = grow + cb + (li & 7);
+        const int col = 32 * lg + 16 * (li >> 3);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            // one 16-key block at a time keeps the tile at 32 registers, as in the fp16 path
+            floatx4 acc[NDB];
+#pragma unroll
+            for (int fb = 0; fb < NDB; ++fb) acc[fb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int fb = 0; fb < NDB; ++fb)
+#pragma unroll
+              for (int m = 0; m < NM; ++m) {
+                const int r1 = 32 * m + 4 * lg + (li >> 2);
+                const int c = 16 * fb + 4 * (li & 3);
+                const uint16_t* a = t == 0 ? lds.dn : lds.qn;
+                const u32x2 a1 = lds_read_tr16(&a[swz<D>(r1, c)]);
+                const u32x2 a2 = lds_read_tr16(&a[swz<D>(r1 + 16, c)]);
+                const u32x4 aT = {a1[0], a1[1], a2[0], a2[1]};
+                acc[fb] = mfma_bf16(aT, t == 0 ? pa[kb][m] : dsa[kb][m], acc[fb]);
+              }
+            float mx = 0.f;
+#pragma unroll
+            for (int fb = 0; fb < NDB; ++fb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(acc[fb][j]));
+            mx = max_in_row16(max_over_rows(mx));
+            // |x| <= m and 127 * rcp(m) exceeds 127/m by at most an ulp: |x * inv| < 127.5
+            const float inv = mx > 0.f ? 127.f * __builtin_amdgcn_rcpf(mx) : 0.f;
+            const float st = t == 0 ? step[kb].x : step[kb].y;
+            fac[t][kb] = -(mx * (1.f / 127.f)) * st;   // sign bit set even when zero
+            u32x4 g0, g1;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              g0[w] = pack_i8(acc[w], inv);
+              g1[w] = pack_i8(acc[w + 4], inv);
+            }
+            // lanes li < 8 keep granule 0 of row li and take granule 0 of row li + 8; lanes
+            // li >= 8 keep granule 1 of row li and take granule 1 of row li - 8
+            u32x4 s1, s2;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              s1[w] = __builtin_amdgcn_update_dpp(g0[w], g1[w], 0x128, 0xf, 0xc, false);
+              s2[w] = __builtin_amdgcn_update_dpp(g1[w], g0[w], 0x128, 0xf, 0x3, false);
+            }
+            uint8_t* dst = reinterpret_cast<uint8_t*>(t == 0 ? cv : ck);
+            const long long ra = r0 + 16 * kb;
+            __builtin_nontemporal_store(s1, reinterpret_cast<u32x4*>(dst + ra * (2 * D) + col));
+            __builtin_nontemporal_store(s2,
+                                        reinterpret_cast<u32x4*>(dst + (ra + 8) * (2 * D) + col));
+          }
+      }
+    };
+    // one format for the whole chunk, the same in every lane. The empty asm makes the block
+    // factors exist before the branch: sunk below it, they would split the if/else into two
+    // ifs, and the compiler's wait for the prefetched keys would then assume a path without
+    // this chunk's stores and drain them all.
+    asm volatile("" ::"v"(step[0].x), "v"(step[0].y), "v"(step[1].x), "v"(step[1].y));
+    if (kStage8<D> && __builtin_amdgcn_readfirstlane((int)(ok8[0] && ok8[1])) != 0)
+      stage_8();
+    else
+      stage_f16();
+    // both blocks' factors in one 16-byte store by every lane (one address, unconditional);
+    // (grow + cb) is a multiple of 32, so the pair is 16-byte aligned
+    *reinterpret_cast<float4*>(&bfac[(grow + cb) / 16]) =
+        make_float4(fac[0][0], fac[1][0], fac[0][1], fac[1][1]);
     wave_lds_fence();   // the next chunk overwrites the dS tile
   };
   chunk(0);
@@ -806,10 +958,10 @@ __global__ __launch_bounds__(64) void attn_bwd_f32(
 
 // Workspace layout for a chunk capacity of `cs` slots and `e` staging rows:
 //   [rs: cs*NG*(nB+1) u32][rsT: cs*NG*(nB+1) u32][tot: cs*(nB+1) u32][off: cs*(nB+1) u32]
-//   [perm: e u32][steps: e/16 float2][dV rows: e*d fp16][dK rows: e*d fp16], every region
-//   256-byte aligned.
+//   [perm: e u32][block factors: e/16 float2][dV rows: e*d fp16][dK rows: e*d fp16], every
+//   region 256-byte aligned (an 8-bit row uses the first d bytes of its fp16 row's place).
 struct WsLayout {
-  size_t rs, rst, tot, off, perm, step, cv, ck, total;
+  size_t rs, rst, tot, off, perm, fac, cv, ck, total;
 };
 static WsLayout ws_layout(const Geom& geo, long long cs, long long e) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
@@ -820,8 +972,8 @@ static WsLayout ws_layout(const Geom& geo, long long cs, long long e) {
   L.tot = L.rst + al(cs * geo.NG * (nb + 1) * 4);
   L.off = L.tot + al(cs * (nb + 1) * 4);
   L.perm = L.off + al(cs * (nb + 1) * 4);
-  L.step = L.perm + al((size_t)e * 4);
-  L.cv = L.step + al((size_t)e / 16 * 8);
+  L.fac = L.perm + al((size_t)e * 4);
+  L.cv = L.fac + al((size_t)e / 16 * 8);
   L.ck = L.cv + al((size_t)e * geo.d * sizeof(uint16_t));
   L.total = L.ck + (size_t)e * geo.d * sizeof(uint16_t);
   return L;
@@ -950,7 +1102,7 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
   uint32_t* tot = reinterpret_cast<uint32_t*>(wsb + L.tot);
   uint32_t* off = reinterpret_cast<uint32_t*>(wsb + L.off);
   uint32_t* perm = reinterpret_cast<uint32_t*>(wsb + L.perm);
-  float2* bstep = reinterpret_cast<float2*>(wsb + L.step);
+  float2* bfac = reinterpret_cast<float2*>(wsb + L.fac);
   uint16_t* cv = reinterpret_cast<uint16_t*>(wsb + L.cv);
   uint16_t* ck = reinterpret_cast<uint16_t*>(wsb + L.ck);
   const int nB = n_buckets(geo.S);
@@ -975,10 +1127,10 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
     hipLaunchKernelGGL((attn_bwd_bf16<DD, QQ>), dim3(rows_waves), dim3(64), 0, st,              \
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,              \
                        (const uint16_t*)o, (const uint16_t*)d_o, lse, idx, scale, dq, ch, cv,   \
-                       ck, bstep, geo);                                                         \
+                       ck, bfac, geo);                                                          \
     mark(4 * c + 2);                                                                            \
     hipLaunchKernelGGL((bucket_reduce<DD>), dim3(ch.n * nB * 2), dim3(64), 0, st, off, perm,    \
-                       bstep, cv, ck, ch, dk, dv, geo);                                         \
+                       bfac, cv, ck, ch, dk, dv, geo);                                          \
     mark(4 * c + 3);                                                                            \
   } else
     DSV_BWD16(64, 1) DSV_BWD16(64, 2) DSV_BWD16(64, 3) DSV_BWD16(64, 4)

@@ -120,6 +120,32 @@ __device__ __forceinline__ float sum_over_rows(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Maximum over the four 16-lane rows: lane l gets max of v(l%16 + 16r), r < 4, by the same
+// row swaps as sum_over_rows.
+__device__ __forceinline__ float max_over_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Four values to biased 8-bit codes in one word (byte j <- x[j]): code = 128 + round-to-
+// nearest-even(x[j] * inv), for |x[j] * inv| < 127.5. Adding 1.5 * 2^23 + 128 in one fused
+// multiply-add leaves exactly that integer in the low mantissa bits (the sum lies in
+// [2^23, 2^24), where the float spacing is 1), so the code is the low byte of the result.
+__device__ __forceinline__ uint32_t pack_i8(const floatx4& x, float inv) {
+  constexpr float kMagic = 12583040.f;   // 0x4b400080
+  const uint32_t y0 = __float_as_uint(fmaf(x[0], inv, kMagic));
+  const uint32_t y1 = __float_as_uint(fmaf(x[1], inv, kMagic));
+  const uint32_t y2 = __float_as_uint(fmaf(x[2], inv, kMagic));
+  const uint32_t y3 = __float_as_uint(fmaf(x[3], inv, kMagic));
+  const uint32_t p01 = __builtin_amdgcn_perm(y1, y0, 0x0c0c0400u);   // bytes: y0.b0, y1.b0
+  const uint32_t p23 = __builtin_amdgcn_perm(y3, y2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+}
+
 // Maximum over each 16-lane row (every lane of the row gets it), by DPP: swaps inside quads,
 // then rotations by 4 and 8 lanes.
 __device__ __forceinline__ float max_in_row16(float v) {

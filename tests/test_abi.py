@@ -124,7 +124,8 @@ def test_workspace_and_idx_layout_agree_with_oracle():
     # backward (bf16), for one (b, h) slot: per-row bucket entry points NG x (nB+1) u32 and
     # their transpose, bucket totals and offsets (nB+1) u32 each, then per staging row of the heaviest slot
     # (NG * max k rounded up to 32): a bucket-list entry (u32), a d-entry fp16 dV row and a
-    # d-entry fp16 dK row, plus two fp32 scales per 16 rows
+    # d-entry fp16 dK row (an 8-bit row uses the first d bytes), plus two fp32 factors per 16
+    # rows
     al = lambda x: -(-x // 256) * 256
     nb = -(-p.seq // 32)
     NG = p.n_groups
