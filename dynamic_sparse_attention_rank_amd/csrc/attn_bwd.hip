@@ -212,17 +212,24 @@ __global__ __launch_bounds__(256) void bucket_offsets(const uint32_t* __restrict
   if (threadIdx.x == 255) o[nB] = part[255];
 }
 
-// Bucket-ordered edge list: perm[off[j] + i], i < tot[j], holds the edges (g, p) whose key
-// lies in bucket j, ordered by group, then by position, each as (slot-relative staging row
-// g*padded_k + p) << 5 | (key - 32 j). One wave per (slot, bucket); 64 groups per step,
-// positions from a wave scan; the keys of a step's runs are read 8 per lane at a time. A
-// 128-byte line of an index row holds the keys of about ten consecutive buckets, so the block
-// index is remapped to give each XCD a contiguous range of buckets (one L2 then serves a line
-// to all of them).
+// Bucket edge list, by key: perm[off[j] + i], i < tot[j], holds the edges (g, p) whose key
+// lies in bucket j, ordered by key, then by group, each as (slot-relative staging row
+// g*padded_k + p) << 5 | (key - 32 j). One wave per (slot, bucket), 64 groups per step. A lane
+// turns its group's run of keys in the bucket into a mask of key offsets (the run ascends, so
+// the run's i-th key sits at staging row e0 + i, i = the number of mask bits below it). A
+// first sweep counts each key's groups (one ballot per key) and keeps each group's mask and
+// first staging row in LDS (dynamic, 8 bytes per group, when the launch provides them), a scan
+// over the 32 counts gives each key's first list position, and a second sweep places every
+// edge after those of the key's earlier groups (ballot and lane-prefix count). A 128-byte line
+// of an index row holds
+// the keys of about ten consecutive buckets, so the block index is remapped to give each XCD a
+// contiguous range of buckets (one L2 then serves a line to all of them).
 __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ rsT,
                                                   const uint32_t* __restrict__ off,
                                                   const int32_t* __restrict__ idx, Chunk ch,
-                                                  uint32_t* __restrict__ perm, Geom geo) {
+                                                  uint32_t* __restrict__ perm, Geom geo,
+                                                  int cached) {
+  extern __shared__ uint2 mcache[];   // [NG] {key mask, first staging row} when cached
   const int nB = n_buckets(geo.S);
   const int nblk = gridDim.x, xcd = blockIdx.x & 7;
   const int logical = xcd * (nblk >> 3) + min(xcd, nblk & 7) + (blockIdx.x >> 3);
@@ -238,41 +245,80 @@ __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ r
   const int32_t* keys = idx + geo.row_offset(b, h, 0);   // row of group g: keys + g*k
   uint32_t* pm = perm + ch.edge_base[sl];
   const int key0 = j * kBucket;
-  uint32_t pos0 = off[(long long)sl * (nB + 1) + j];
-  for (int g0 = 0; g0 < geo.NG; g0 += 64) {
+  // mask of the key offsets of group g0 + lane's run in the bucket; a = the run's first
+  // position. A malformed (not ascending) row may repeat an offset: the mask then holds fewer
+  // edges than the run, and no more than the list has room for are placed.
+  auto run_mask = [&](int g0, uint32_t& a) {
     const int g = g0 + lane;
-    uint32_t a = 0, len = 0;
+    uint32_t len = 0;
+    a = 0;
     if (g < geo.NG) {
       a = r[g];
       len = run_len(a, r[geo.NG + g]);
     }
-    uint32_t incl = len;   // inclusive prefix over lanes
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t y = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += y;
-    }
-    const uint32_t pos = pos0 + incl - len;
-    const uint32_t e0 = (uint32_t)g * kp + a;
     const int32_t* krow = keys + (long long)g * kh + a;
     uint32_t maxlen = len;
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) maxlen = max(maxlen, (uint32_t)__shfl_xor((int)maxlen, m, 64));
+    uint32_t mask = 0;
     for (uint32_t i0 = 0; i0 < maxlen; i0 += 8) {
       int kv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) kv[u] = i0 + u < len ? krow[i0 + u] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t i = i0 + u;
-        // a malformed row is dropped rather than written past the slot's list
-        if (i < len && pos + i < slot_rows) {
-          const int ko = min(max(clamp_key(kv[u], geo.S) - key0, 0), kBucket - 1);
-          pm[pos + i] = ((e0 + i) << 5) | (uint32_t)ko;
-        }
-      }
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u < len)
+          mask |= 1u << min(max(clamp_key(kv[u], geo.S) - key0, 0), kBucket - 1);
     }
-    pos0 += __shfl(incl, 63, 64);
+    return mask;
+  };
+  // first sweep: groups per key offset
+  uint32_t cnt[kBucket];
+#pragma unroll
+  for (int ko = 0; ko < kBucket; ++ko) cnt[ko] = 0;
+  for (int g0 = 0; g0 < geo.NG; g0 += 64) {
+    uint32_t a;
+    const uint32_t mask = run_mask(g0, a);
+    if (cached && g0 + lane < geo.NG)
+      mcache[g0 + lane] = make_uint2(mask, (uint32_t)(g0 + lane) * kp + a);
+#pragma unroll
+    for (int ko = 0; ko < kBucket; ++ko)
+      cnt[ko] += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((mask >> ko) & 1u));
+  }
+  uint32_t base[kBucket];   // next list position of each key offset (uniform)
+  uint32_t run = off[(long long)sl * (nB + 1) + j];
+#pragma unroll
+  for (int ko = 0; ko < kBucket; ++ko) {
+    base[ko] = run;
+    run += cnt[ko];
+  }
+  // second sweep: place the edges
+  for (int g0 = 0; g0 < geo.NG; g0 += 64) {
+    uint32_t mask = 0u, e0 = 0u;
+    if (cached) {   // written by this lane in the first sweep: no barrier needed
+      if (g0 + lane < geo.NG) {
+        const uint2 c = mcache[g0 + lane];
+        mask = c.x;
+        e0 = c.y;
+      }
+    } else {
+      uint32_t a;
+      mask = run_mask(g0, a);
+      e0 = (uint32_t)(g0 + lane) * kp + a;
+    }
+#pragma unroll
+    for (int ko = 0; ko < kBucket; ++ko) {
+      const bool has = (mask >> ko) & 1u;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(has);
+      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      const uint32_t pos = base[ko] + below;
+      // a malformed row is dropped rather than written past the slot's list
+      if (has && pos < slot_rows)
+        pm[pos] = ((e0 + (uint32_t)__builtin_popcount(mask & ((1u << ko) - 1u))) << 5) |
+                  (uint32_t)ko;
+      base[ko] += (uint32_t)__builtin_popcountll(m);
+    }
   }
 }
 
@@ -283,16 +329,16 @@ __global__ void fill_zero(float4* __restrict__ p, long long n4) {
 }
 
 // Sum each bucket's staging rows: one wave per (slot, bucket, half), half 0 = dV, 1 = dK.
-// Lane l owns features (D/64)*l .. of the half; the bucket's key rows accumulate in LDS.
-// Each step takes 64 entries of the bucket's edge list (edge row, key, row factor: one per
-// lane), then walks them one row per instruction, so no two lanes ever touch the same LDS word
-// and rows with equal keys are added in list order. The step's 64 row loads are issued at
-// once, and the next step's entries and factors are requested during this one. Every key row
-// of the bucket is then written once (zero where no group selected the key).
-// A row's factor f (one per 16-row block) says its format: sign bit clear, fp16 entries times
-// f; set (d = 128 only), 8-bit codes c with entry (c - 128) * |f|. Both kinds sit at the start of the row's 2d-byte
-// slot; each lane loads one 32-bit word of it, at byte 4l (fp16) or 4(l/2) (8-bit: the lane
-// takes half of the word), and adds its two entries into the LDS slots of their features.
+// The bucket's list is ordered by key, so each key's rows are consecutive: the lanes add them
+// in registers (lane l owns D/64 features) and write the key's row once when the key changes,
+// and zero rows for the keys nobody selected. Each step takes 64 list entries (edge row, key,
+// block factor: one per lane), issues their 64 row loads at once and requests the next step's
+// entries and factors during this one. No LDS, no atomics: each key's rows are added in group
+// order, so dK/dV are bitwise reproducible.
+// A block factor f says its rows' format: sign bit clear, fp16 entries times f; set (d = 128
+// only), 8-bit codes c meaning (c - 128) * |f|. The lane adds c * |f| and, once per row, |f|;
+// the key's row is then sum(c * |f|) - 128 * sum(|f|). Both kinds of row sit at the start of
+// the row's 2d-byte slot.
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 template <int D>
 __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__ off,
@@ -303,7 +349,6 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
                                                    float* __restrict__ dk, float* __restrict__ dv,
                                                    Geom geo) {
   constexpr int FPL = D / 64;   // features per lane
-  __shared__ __attribute__((aligned(16))) float acc[kBucket * D];
   const int nB = n_buckets(geo.S);
   const int half = blockIdx.x & 1;
   const int bj = blockIdx.x >> 1;
@@ -313,9 +358,6 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
   int b, h;
   chunk_slot(geo, ch.s0 + sl, b, h);
   const long long bh = (long long)b * geo.H + h;
-  for (int i = lane; i < kBucket * D / 4; i += 64)
-    reinterpret_cast<float4*>(acc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  __syncthreads();
   const long long eb = ch.edge_base[sl];
   const long long nrows = ch.edge_base[sl + 1] - eb;
   const uint32_t* o = off + (long long)sl * (nB + 1);
@@ -325,19 +367,45 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
   const unsigned char* src =
       reinterpret_cast<const unsigned char*>(half ? ck : cv) + eb * (2 * D);
   const int key0 = j * kBucket;
-  // LDS slots. d = 64 (fp16 rows only): slot = staging position, lane l owns position l.
-  // d = 128: feature F = 16w + 4g + j (w < 8, g < 4, j < 4) has the pair index
-  // P = 16g + 2w + j/2, the order of an 8-bit row (lane l loads its bytes 2l, 2l + 1: P = l),
-  // and its slot is 2P' + j%2 with P' = P ^ 8 [P >= 32]. An fp16 row gives lane l the staging
-  // positions 2l, 2l + 1, i.e. P = 16((l/4)%4) + 4(l/16) + 2((l/2)%2) + l%2. The swap of bit 3
-  // in the upper half makes both lane patterns hit 32 distinct bank pairs in each half-wave.
-  auto swz_pair = [](int P) { return P ^ (((P >> 5) & 1) << 3); };
-  const int o16 = 2 * FPL * lane, o8 = 4 * (lane >> 1);
-  const int a16 = kStage8<D> ? 2 * swz_pair(16 * ((lane >> 2) & 3) + 4 * (lane >> 4) +
-                                            2 * ((lane >> 1) & 1) + (lane & 1))
-                             : FPL * lane;
-  const int a8 = 2 * swz_pair(lane);
-  const int sh8 = 16 * (lane & 1);
+  const int nk = min(kBucket, geo.S - key0);
+  // The lane's features and where a row keeps them. d = 128: features 16w + 4g + 2(l%2) + {0,1}
+  // with g = l/16, w = (l/2)%8, i.e. bytes 2l, 2l + 1 of an 8-bit row (byte 32g + 4w + j <->
+  // feature 16w + 4g + j) and fp16 positions 32(w/2) + 8g + 4(w%2) + 2(l%2) + {0,1}. d = 64
+  // (fp16 only): position l, holding feature 32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4
+  // of position 32fp + 8lg + t.
+  int feat, o16;
+  if constexpr (kStage8<D>) {
+    const int g = lane >> 4, w = (lane >> 1) & 7, j0 = 2 * (lane & 1);
+    feat = 16 * w + 4 * g + j0;
+    o16 = 2 * (32 * (w >> 1) + 8 * g + 4 * (w & 1) + j0);
+  } else {
+    const int t8 = lane & 7;
+    feat = (lane & ~31) + 4 * ((lane >> 3) & 3) + (t8 < 4 ? t8 : 12 + t8);
+    o16 = 2 * lane;
+  }
+  const int o8 = 4 * (lane >> 1), sh8 = 16 * (lane & 1);
+  float* out = (half ? dk : dv) + bh * geo.S * D + (long long)key0 * D + feat;
+  float a0 = 0.f, a1 = 0.f, corr = 0.f;
+  int cur = -1;          // key being summed (uniform)
+  uint32_t done = 0u;    // keys whose row is written (uniform)
+  auto put = [&](int key, float v0, float v1) {
+    if constexpr (FPL == 2)
+      __builtin_nontemporal_store(floatx2{v0, v1}, reinterpret_cast<floatx2*>(out + key * D));
+    else
+      out[key * D] = v0;
+  };
+  // close key `cur` (if any) and zero the keys up to `next`
+  auto close_to = [&](int next) {
+    if (cur >= 0 && cur < nk) {
+      put(cur, fmaf(-128.f, corr, a0), fmaf(-128.f, corr, a1));
+      done |= 1u << cur;
+    }
+    for (int key = cur + 1; key < min(next, nk); ++key) {
+      put(key, 0.f, 0.f);
+      done |= 1u << key;
+    }
+    a0 = a1 = corr = 0.f;
+  };
   // entry -> slot-relative staging row (clamped into the slot)
   auto row_of = [&](uint32_t ent) { return std::min<uint32_t>(ent >> 5, (uint32_t)(nrows - 1)); };
   if (s1 > s0) {
@@ -348,7 +416,8 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
     float2 st = bfac[(eb + row_of(ent)) >> 4];
     for (long long r0 = s0; r0 < s1; r0 += 64) {
       const int n = (int)std::min<long long>(64, s1 - r0);
-      // lanes past the end repeat the last entry and add it with a zero factor of its format
+      // lanes past the end repeat the last entry (same key) and add it with a zero factor of
+      // its format
       const uint32_t e = row_of(ent);
       const int kk = (int)(ent & 31u);
       const float f0 = half ? st.y : st.x;
@@ -367,15 +436,13 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
           const unsigned char* rp = src + (long long)eu * (2 * D);
           if constexpr (FPL == 1) {
             x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(rp + o16));
+          } else if constexpr (MODE == 1) {   // the lane's two codes
+            x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(rp + 2 * lane));
           } else {
-            if constexpr (MODE == 1) {   // the lane's two codes
-              x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(rp + 2 * lane));
-            } else {
-              int ob = o16;
-              if constexpr (MODE == 2)   // word lane/2 of an 8-bit row, word lane of an fp16 row
-                ob = 4 * (lane >> ((__builtin_amdgcn_readlane(__float_as_int(sc), u) >> 31) & 1));
-              x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(rp + ob));
-            }
+            int ob = o16;
+            if constexpr (MODE == 2)   // word lane/2 of an 8-bit row
+              if (__builtin_amdgcn_readlane(__float_as_int(sc), u) < 0) ob = o8;
+            x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(rp + ob));
           }
         }
       };
@@ -385,22 +452,20 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
         for (int u = 0; u < 64; ++u) {
           const int ku = __builtin_amdgcn_readlane(kk, u);
           const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), u));
+          if (ku != cur) {
+            close_to(ku);
+            cur = ku;
+          }
           if constexpr (FPL == 1) {
-            acc[ku * D + a16] += su * f16_lo(x[u]);
+            a0 = fmaf(su, f16_lo(x[u]), a0);
           } else if (MODE == 1 || (MODE == 2 && __float_as_int(su) < 0)) {
             const uint32_t w = MODE == 1 ? x[u] : x[u] >> sh8;
-            float* a = acc + ku * D + a8;
-            float2 v = *reinterpret_cast<float2*>(a);
-            const float c = 128.f * su;   // f = su < 0: (code - 128) * |f| = c - code * f
-            v.x += fmaf((float)(w & 0xffu), -su, c);
-            v.y += fmaf((float)((w >> 8) & 0xffu), -su, c);
-            *reinterpret_cast<float2*>(a) = v;
+            a0 = fmaf((float)(w & 0xffu), -su, a0);
+            a1 = fmaf((float)((w >> 8) & 0xffu), -su, a1);
+            corr -= su;
           } else {
-            float* a = acc + ku * D + a16;
-            float2 v = *reinterpret_cast<float2*>(a);
-            v.x += su * f16_lo(x[u]);
-            v.y += su * f16_hi(x[u]);
-            *reinterpret_cast<float2*>(a) = v;
+            a0 = fmaf(su, f16_lo(x[u]), a0);
+            a1 = fmaf(su, f16_hi(x[u]), a1);
           }
         }
       };
@@ -418,28 +483,10 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
       st = st_n;
     }
   }
-  __syncthreads();
-  const int nk = min(kBucket, geo.S - key0);
-  // slots FPL*lane.. back to features. d = 128: pair P = swz_pair(lane) is feature
-  // 16((P/2)%8) + 4(P/16) + 2(P%2) and the next one. d = 64: staging position l holds feature
-  // 32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4 (position 32fp + 8lg + t).
-  int feat;
-  if constexpr (kStage8<D>) {
-    const int P = swz_pair(lane);
-    feat = 16 * ((P >> 1) & 7) + 4 * (P >> 4) + 2 * (P & 1);
-  } else {
-    const int pos = FPL * lane;
-    const int t8 = pos & 7;
-    feat = (pos & ~31) + 4 * ((pos >> 3) & 3) + (t8 < 4 ? t8 : 12 + t8);
-  }
-  float* out = (half ? dk : dv) + bh * geo.S * D + (long long)key0 * D + feat;
-  for (int l = 0; l < nk; ++l) {
-    if constexpr (FPL == 2)
-      __builtin_nontemporal_store(*reinterpret_cast<const floatx2*>(acc + l * D + FPL * lane),
-                                  reinterpret_cast<floatx2*>(out + (long long)l * D));
-    else
-      out[(long long)l * D] = acc[l * D + lane];
-  }
+  close_to(nk);
+  // a malformed list may skip keys: every row of the bucket is written
+  for (int key = 0; key < nk; ++key)
+    if (!((done >> key) & 1u)) put(key, 0.f, 0.f);
 }
 
 // LDS copy of the group's Q and dO rows (bf16, [member][feature]). Chunk c (8 features,
@@ -589,6 +636,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     };
     u32x4 pa[2][NM], dsa[2][NM];
     float2 step[2];
+    float sv_[2], sk_[2];   // fp16 staging scales of blocks kb
     bool ok8[2];   // block kb may be staged in 8 bits (both bounds within kStage8Bound)
     // ---- P, dS of block kb, their fp16 staging scales, the dV / dK operands and the dS tile
     auto softmax = [&](const int kb, const floatx4 (&s)[QB], const floatx4 (&dp)[QB]) {
@@ -614,9 +662,9 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       // The dV and dK rows of this chunk's edges are staged in fp16 with one power-of-two
       // scale per 16-key block (kb). |dV[d]| <= sum_n P * max|dO| and |dK[d]| <= scale *
       // sum_n |dS| * max|Q| bound every entry of a key's rows; the block's largest bound sets
-      // sv, sk (pow2_scale). P and dS are multiplied by them before they become bf16 MFMA
-      // operands (a power of two commutes with the bf16 rounding, so the operands are
-      // exactly the rounded P and dS, scaled), and the products go to fp16 as they are.
+      // sv, sk (pow2_scale). The fp16 path multiplies the dV / dK products by them before the
+      // fp16 conversion (a power of two commutes with the roundings of the bf16 operands and
+      // of the fp32 sums); the 8-bit path needs no such scaling.
       {
         float cp = 0.f, cd = 0.f;
 #pragma unroll
@@ -632,6 +680,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         const float sv = pow2_scale(cp * max_do);
         const float sk = pow2_scale(cd * max_q);   // dK = scale * (sum dS q): scale in the step
         ok8[kb] = cp * max_do <= kStage8Bound && cd * max_q * scale <= kStage8Bound;
+        sv_[kb] = sv;
+        sk_[kb] = sk;
         // sv, sk are powers of two, so their reciprocals are exact
         step[kb] = make_float2(sv > 0.f ? __builtin_amdgcn_rcpf(sv) : 0.f,
                                sk > 0.f ? __builtin_amdgcn_rcpf(sk) * scale : 0.f);
@@ -639,14 +689,14 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         // 16(2m + e/4) + 4lg + e%4
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          pa[kb][m][0] = pack_bf16(pv[2 * m][0] * sv, pv[2 * m][1] * sv);
-          pa[kb][m][1] = pack_bf16(pv[2 * m][2] * sv, pv[2 * m][3] * sv);
-          pa[kb][m][2] = pack_bf16(pv[2 * m + 1][0] * sv, pv[2 * m + 1][1] * sv);
-          pa[kb][m][3] = pack_bf16(pv[2 * m + 1][2] * sv, pv[2 * m + 1][3] * sv);
-          dsa[kb][m][0] = pack_bf16(dsv_[2 * m][0] * sk, dsv_[2 * m][1] * sk);
-          dsa[kb][m][1] = pack_bf16(dsv_[2 * m][2] * sk, dsv_[2 * m][3] * sk);
-          dsa[kb][m][2] = pack_bf16(dsv_[2 * m + 1][0] * sk, dsv_[2 * m + 1][1] * sk);
-          dsa[kb][m][3] = pack_bf16(dsv_[2 * m + 1][2] * sk, dsv_[2 * m + 1][3] * sk);
+          pa[kb][m][0] = pack_bf16(pv[2 * m][0], pv[2 * m][1]);
+          pa[kb][m][1] = pack_bf16(pv[2 * m][2], pv[2 * m][3]);
+          pa[kb][m][2] = pack_bf16(pv[2 * m + 1][0], pv[2 * m + 1][1]);
+          pa[kb][m][3] = pack_bf16(pv[2 * m + 1][2], pv[2 * m + 1][3]);
+          dsa[kb][m][0] = pack_bf16(dsv_[2 * m][0], dsv_[2 * m][1]);
+          dsa[kb][m][1] = pack_bf16(dsv_[2 * m][2], dsv_[2 * m][3]);
+          dsa[kb][m][2] = pack_bf16(dsv_[2 * m + 1][0], dsv_[2 * m + 1][1]);
+          dsa[kb][m][3] = pack_bf16(dsv_[2 * m + 1][2], dsv_[2 * m + 1][3]);
         }
       }
       // dS tile (unscaled) -> LDS as [key][member]: the lane's 4 members are adjacent
@@ -748,10 +798,15 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           // row cb + 16kb + li < padded_k: past the row end it is a (zero) padding row
-          const u32x4 wv = {pack_f16(av[0][kb][0], av[0][kb][1]), pack_f16(av[0][kb][2], av[0][kb][3]),
-                            pack_f16(av[1][kb][0], av[1][kb][1]), pack_f16(av[1][kb][2], av[1][kb][3])};
-          const u32x4 wk = {pack_f16(ak[0][kb][0], ak[0][kb][1]), pack_f16(ak[0][kb][2], ak[0][kb][3]),
-                            pack_f16(ak[1][kb][0], ak[1][kb][1]), pack_f16(ak[1][kb][2], ak[1][kb][3])};
+          const float v = sv_[kb], q = sk_[kb];
+          const u32x4 wv = {pack_f16(av[0][kb][0] * v, av[0][kb][1] * v),
+                            pack_f16(av[0][kb][2] * v, av[0][kb][3] * v),
+                            pack_f16(av[1][kb][0] * v, av[1][kb][1] * v),
+                            pack_f16(av[1][kb][2] * v, av[1][kb][3] * v)};
+          const u32x4 wk = {pack_f16(ak[0][kb][0] * q, ak[0][kb][1] * q),
+                            pack_f16(ak[0][kb][2] * q, ak[0][kb][3] * q),
+                            pack_f16(ak[1][kb][0] * q, ak[1][kb][1] * q),
+                            pack_f16(ak[1][kb][2] * q, ak[1][kb][3] * q)};
           if ((fp & 1) == 0) {
             xv[kb] = wv;
             xk[kb] = wk;
@@ -821,8 +876,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
             mx = max_in_row16(max_over_rows(mx));
             // |x| <= m and 127 * rcp(m) exceeds 127/m by at most an ulp: |x * inv| < 127.5
             const float inv = mx > 0.f ? 127.f * __builtin_amdgcn_rcpf(mx) : 0.f;
-            const float st = t == 0 ? step[kb].x : step[kb].y;
-            fac[t][kb] = -(mx * (1.f / 127.f)) * st;   // sign bit set even when zero
+            // dK = scale * (sum dS q): the scale goes into the factor
+            fac[t][kb] = -(mx * (1.f / 127.f)) * (t == 0 ? 1.f : scale);   // sign bit set
             u32x4 g0, g1;
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
@@ -1119,8 +1174,10 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
     hipLaunchKernelGGL(transpose_rs, dim3(ttiles), dim3(256), 0, st, rs, rsT, geo);
     hipLaunchKernelGGL(bucket_totals, dim3(ch.n * nB), dim3(64), 0, st, rsT, tot, geo);
     hipLaunchKernelGGL(bucket_offsets, dim3(ch.n), dim3(256), 0, st, tot, off, geo);
-    hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64), 0, st, rsT, off, idx, ch, perm,
-                       geo);
+    // the first sweep's masks stay in LDS up to 6144 groups (48 KB)
+    const int cached = geo.NG <= 6144 ? 1 : 0;
+    hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64), cached ? geo.NG * sizeof(uint2) : 0,
+                       st, rsT, off, idx, ch, perm, geo, cached);
     mark(4 * c + 1);
 #define DSV_BWD16(DD, QQ)                                                                       \
   if (geo.d == DD && QBn == QQ) {                                                               \

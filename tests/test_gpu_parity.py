@@ -293,6 +293,44 @@ def test_bwd_edge_cases(label, over, ks):
         assert float(dk[0, 0].abs().max()) <= TOL[cfg.dtype]
 
 
+def test_bwd_mixed_staging_formats():
+    """d = 128: chunks whose a-priori dV/dK bounds are small are staged in 8 bits, the others
+    in fp16. At k = 2048 and 1400 of 4096 keys about 86% and 58% of the chunks take 8 bits, so
+    one launch holds both kinds (read back from the block factor table of the workspace: sign
+    bit set = 8-bit) and the reduce runs its mixed steps; every output still meets the bf16
+    bar against the oracle."""
+    cfg = workload("small", heads=2, frames=4, height=32, width=32, head_dim=128, rank=32)
+    say("[bwd] mixed staging formats")
+    x = gpu_inputs(cfg, backward=True, k_per_head=[2048, 1400])
+    idx = run_topk(cfg, x)
+    p = dsv.problem_for(cfg)
+    o, lse = dsv.sparse_attn_fwd(p, x["q"], x["k"], x["v"], idx, x["k_per_head"], x["scale"])
+    need = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, x["k_per_head"])
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")   # one slot per chunk
+    dq, dk, dv = dsv.sparse_attn_bwd(p, x["q"], x["k"], x["v"], o, x["do"], lse, idx,
+                                     x["k_per_head"], x["scale"], ws=ws)
+    torch.cuda.synchronize()
+    # the last chunk's block factors (layout pinned in test_abi): heads run heaviest k first,
+    # so the last chunk is head 1 (k = 1400, 44 chunks = 88 blocks per group)
+    al = lambda v: -(-v // 256) * 256
+    NG, nb = p.n_groups, -(-p.seq // 32)
+    e = NG * (-(-max(x["k_per_head"]) // 32) * 32)
+    off = 2 * al(NG * (nb + 1) * 4) + 2 * al((nb + 1) * 4) + al(e * 4)
+    fac = ws[off:off + e // 16 * 8].view(torch.float32).view(-1, 2).cpu()
+    neg = torch.signbit(fac[:NG * 88, 0])
+    say(f"   8-bit blocks of head 1: {float(neg.float().mean()):.2f}")
+    assert bool(neg.any()) and bool((~neg).any()), float(neg.float().mean())
+    tol = TOL[cfg.dtype]
+    mem = members(cfg)
+    for h in range(cfg.heads):
+        rows = gpu_rows(cfg, x, idx, 0, h)
+        rdq, rdk, rdv = oracle_bwd(cfg, x, rows, 0, h, mem=mem)
+        e3 = (maxerr(dq[0, h].cpu().numpy(), rdq), maxerr(dk[0, h].cpu().numpy(), rdk),
+              maxerr(dv[0, h].cpu().numpy(), rdv))
+        say(f"   head {h}: max-abs-err dQ {e3[0]:.2e} dK {e3[1]:.2e} dV {e3[2]:.2e}")
+        assert max(e3) <= tol, (h, e3)
+
+
 def test_bwd_profiled_matches_plain_bitwise():
     """dsv_sparse_attn_bwd_profiled does the same work: bitwise-equal dQ/dK/dV, and its stage
     events are ordered on the stream."""
