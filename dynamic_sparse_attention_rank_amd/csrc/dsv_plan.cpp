@@ -90,8 +90,8 @@ int dsv_plan_heads(const int32_t* k_per_head, int32_t heads, int32_t n_parts, do
 }
 
 // Measured on one MI355X at S = 64K (B=1, H=24, d=128, r=32, G=64, k = 10 % of S):
-// top-k 2.44 ms over 24 * 1024 * 65536 scores; forward 7.31 ms and backward 42.1 ms over
-// 1.611e8 edges. The estimator's work per score scales with r (two bf16 MFMA terms per 16
+// top-k 1.44 ms over 24 * 1024 * 65536 scores; forward 6.50 ms and backward 38.2 ms over
+// 1.611e8 edges (kernel trace of one step, all of the backward's kernels). The estimator's work per score scales with r (two bf16 MFMA terms per 16
 // features and a fixed per-score selection cost, taken here as proportional), the
 // attention's per edge with G * d.
 int dsv_default_cost_model(const dsv_problem* p, int with_backward, dsv_cost_model* cm) {
@@ -104,8 +104,8 @@ int dsv_default_cost_model(const dsv_problem* p, int with_backward, dsv_cost_mod
   std::vector<int32_t> k1(p ? std::max(p->heads, 1) : 1, one);
   const int st = validate_problem(p, k1.data(), &geo);
   if (st != DSV_OK) return st;
-  const double topk_ns = 2.44e6 / (24.0 * 1024.0 * 65536.0);
-  const double fwd_ns = 7.31e6 / 1.611e8, bwd_ns = 42.1e6 / 1.611e8;
+  const double topk_ns = 1.44e6 / (24.0 * 1024.0 * 65536.0);
+  const double fwd_ns = 6.50e6 / 1.611e8, bwd_ns = 38.2e6 / 1.611e8;
   cm->topk_ns_per_score = topk_ns * (double)geo.r / 32.0;
   cm->attn_ns_per_edge =
       (with_backward ? fwd_ns + bwd_ns : fwd_ns) * (double)geo.G * geo.d / (64.0 * 128.0);
