@@ -328,18 +328,77 @@ __global__ void fill_zero(float4* __restrict__ p, long long n4) {
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
-// Sum each bucket's staging rows: one wave per (slot, bucket, half), half 0 = dV, 1 = dK.
-// The bucket's list is ordered by key, so each key's rows are consecutive: the lanes add them
-// in registers (lane l owns D/64 features) and write the key's row once when the key changes,
-// and zero rows for the keys nobody selected. Each step takes 64 list entries (edge row, key,
-// block factor: one per lane), issues their 64 row loads at once and requests the next step's
-// entries and factors during this one. No LDS, no atomics: each key's rows are added in group
-// order, so dK/dV are bitwise reproducible.
+// Sum each bucket's staging rows. The bucket's list is ordered by key, so each key's rows are
+// consecutive: the lanes add them in registers and write the key's row once when the key
+// changes; at the end, zero rows for the keys nobody selected. Each block takes 64 list entries (edge
+// row, key, block factors: one per lane) in two halves of 32 rows, whose loads are requested
+// half a block before they are added (entries two blocks ahead, factors one block ahead). No
+// LDS, no atomics: each key's rows are added in group order, so dK/dV are bitwise reproducible.
 // A block factor f says its rows' format: sign bit clear, fp16 entries times f; set (d = 128
-// only), 8-bit codes c meaning (c - 128) * |f|. The lane adds c * |f| and, once per row, |f|;
-// the key's row is then sum(c * |f|) - 128 * sum(|f|). Both kinds of row sit at the start of
-// the row's 2d-byte slot.
+// only), 8-bit codes c meaning (c - 128) * |f|. For those the lane adds c * |f| and, once per
+// row, |f|; the key's row is then sum(c * |f|) - 128 * sum(|f|).
 typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// A block of 64 list entries, one per lane: staging row, key offset, the lane's dV and dK
+// factors (lanes past the end of the list: zero, same sign, so that they add nothing) and the
+// format mode of its rows: all fp16 (0), all 8-bit (1), mixed (2); the same in every lane.
+struct RBlk {
+  uint32_t e;
+  int kk, mode;
+  float sv, sk;
+};
+__device__ __forceinline__ RBlk make_rblk(uint32_t ent, float2 st, long long r0, long long s1,
+                                          long long nrows, bool pair) {
+  const int lane = threadIdx.x;
+  RBlk k;
+  const int n = (int)std::min<long long>(64, s1 - r0);   // <= 0 past the list: no row counts
+  k.e = std::min<uint32_t>(ent >> 5, (uint32_t)(nrows - 1));
+  k.kk = (int)(ent & 31u);
+  k.sv = lane < n ? st.x : copysignf(0.f, st.x);
+  k.sk = lane < n ? st.y : copysignf(0.f, st.y);
+  const uint64_t m8 = __builtin_amdgcn_ballot_w64(__float_as_int(k.sv) < 0);
+  k.mode = !pair || m8 == 0 ? 0 : m8 == ~0ull ? 1 : 2;
+  return k;
+}
+
+// The reduce's list walk, pipelined in half blocks: the next block's first half
+// is requested before this block's second half is added, its second half before the following
+// block's first half; entries two blocks ahead, factors one block ahead. Every load is
+// unconditional (positions clamped; after the last block the "next" block rereads its last
+// rows, unused), and the second block's entries go out before the first block's rows, as in
+// the loop: the compiler's waits for each half then leave the later requests in flight.
+// A macro over the kernel's lambdas load_half, add_half (passed to a function, the row words
+// would leave registers).
+#define DSV_WALK_BUCKET(PAIR)                                                                 \
+  if (s1 > s0) {                                                                              \
+    auto row_of = [&](uint32_t ent) {                                                         \
+      return std::min<uint32_t>(ent >> 5, (uint32_t)(nrows - 1));                             \
+    };                                                                                        \
+    const uint32_t ent0 = pm[std::min<long long>(s0 + lane, s1 - 1)];                         \
+    const float2 st0 = bfac[(eb + row_of(ent0)) >> 4];                                        \
+    uint32_t ent1 = pm[std::min<long long>(s0 + 64 + lane, s1 - 1)];                          \
+    RBlk cur_b = make_rblk(ent0, st0, s0, s1, nrows, PAIR);                                   \
+    load_half(cur_b, 0);                                                                      \
+    load_half(cur_b, 1);                                                                      \
+    for (long long r0 = s0; r0 < s1; r0 += 64) {                                              \
+      const float2 st1 = bfac[(eb + row_of(ent1)) >> 4];                                      \
+      const uint32_t ent2 = pm[std::min<long long>(r0 + 128 + lane, s1 - 1)];                 \
+      add_half(cur_b, 0);                                                                     \
+      const RBlk nxt = make_rblk(ent1, st1, r0 + 64, s1, nrows, PAIR);                        \
+      load_half(nxt, 0);                                                                      \
+      add_half(cur_b, 1);                                                                     \
+      load_half(nxt, 1);                                                                      \
+      cur_b = nxt;                                                                            \
+      ent1 = ent2;                                                                            \
+    }                                                                                         \
+  }
+
+// One wave per (slot, bucket, half), half 0 = dV, 1 = dK. Lane l owns FPL = d/64 features of
+// the half and loads them from each row: d = 128: features 16w + 4g + 2(l%2) + {0,1} with
+// g = l/16, w = (l/2)%8, i.e. bytes 2l, 2l + 1 of an 8-bit row (byte 32g + 4w + j <-> feature
+// 16w + 4g + j) and fp16 positions 32(w/2) + 8g + 4(w%2) + 2(l%2) + {0,1}. d = 64 (fp16 rows
+// only): position l, holding feature 32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4 of
+// position 32fp + 8lg + t. Both kinds of row sit at the start of the row's 2d-byte place.
 template <int D>
 __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__ off,
                                                    const uint32_t* __restrict__ perm,
@@ -363,16 +422,10 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
   const uint32_t* o = off + (long long)sl * (nB + 1);
   const long long s0 = std::min<long long>(o[j], nrows);
   const long long s1 = std::min<long long>(std::max<long long>(o[j + 1], o[j]), nrows);
-  const uint32_t* pm = perm + eb;
   const unsigned char* src =
       reinterpret_cast<const unsigned char*>(half ? ck : cv) + eb * (2 * D);
   const int key0 = j * kBucket;
   const int nk = min(kBucket, geo.S - key0);
-  // The lane's features and where a row keeps them. d = 128: features 16w + 4g + 2(l%2) + {0,1}
-  // with g = l/16, w = (l/2)%8, i.e. bytes 2l, 2l + 1 of an 8-bit row (byte 32g + 4w + j <->
-  // feature 16w + 4g + j) and fp16 positions 32(w/2) + 8g + 4(w%2) + 2(l%2) + {0,1}. d = 64
-  // (fp16 only): position l, holding feature 32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4
-  // of position 32fp + 8lg + t.
   int feat, o16;
   if constexpr (kStage8<D>) {
     const int g = lane >> 4, w = (lane >> 1) & 7, j0 = 2 * (lane & 1);
@@ -394,100 +447,83 @@ __global__ __launch_bounds__(64) void bucket_reduce(const uint32_t* __restrict__
     else
       out[key * D] = v0;
   };
-  // close key `cur` (if any) and zero the keys up to `next`
-  auto close_to = [&](int next) {
+  // write the finished key (keys nobody selected are zeroed at the end)
+  auto close_key = [&]() {
     if (cur >= 0 && cur < nk) {
       put(cur, fmaf(-128.f, corr, a0), fmaf(-128.f, corr, a1));
       done |= 1u << cur;
     }
-    for (int key = cur + 1; key < min(next, nk); ++key) {
-      put(key, 0.f, 0.f);
-      done |= 1u << key;
-    }
     a0 = a1 = corr = 0.f;
   };
-  // entry -> slot-relative staging row (clamped into the slot)
-  auto row_of = [&](uint32_t ent) { return std::min<uint32_t>(ent >> 5, (uint32_t)(nrows - 1)); };
-  if (s1 > s0) {
-    // the first block's entries and factors; afterwards each block requests the next block's
-    // entries at its start and their factors after its row loads, so that both have arrived
-    // when the next block starts (all loads unconditional, positions clamped)
-    uint32_t ent = pm[std::min<long long>(s0 + lane, s1 - 1)];
-    float2 st = bfac[(eb + row_of(ent)) >> 4];
-    for (long long r0 = s0; r0 < s1; r0 += 64) {
-      const int n = (int)std::min<long long>(64, s1 - r0);
-      // lanes past the end repeat the last entry (same key) and add it with a zero factor of
-      // its format
-      const uint32_t e = row_of(ent);
-      const int kk = (int)(ent & 31u);
-      const float f0 = half ? st.y : st.x;
-      const float sc = lane < n ? f0 : copysignf(0.f, f0);
-      const uint32_t ent_n = pm[std::min<long long>(r0 + 64 + lane, s1 - 1)];
-      // the step's formats: all fp16 (0), all 8-bit (1) or mixed (2), the same in every lane
-      const uint64_t m8 = __builtin_amdgcn_ballot_w64(__float_as_int(sc) < 0);
-      const int mode = !kStage8<D> || m8 == 0 ? 0 : m8 == ~0ull ? 1 : 2;
-      uint32_t x[64];
-      auto load_rows = [&](auto mc) {
-        constexpr int MODE = decltype(mc)::value;
+  using M0 = std::integral_constant<int, 0>;
+  using M1 = std::integral_constant<int, 1>;
+  using M2 = std::integral_constant<int, 2>;
+  uint32_t x[2][32];   // row words of the two halves of a block
+  auto load_half = [&](const RBlk& k, int hf) {
+    const float sc = half ? k.sk : k.sv;
+    auto go = [&](auto mc) {
+      constexpr int MODE = decltype(mc)::value;
 #pragma unroll
-        for (int u = 0; u < 64; ++u) {
-          const uint32_t eu = __builtin_amdgcn_readlane(e, u);
-          // staging rows are read once: non-temporal, so they do not displace other lines
-          const unsigned char* rp = src + (long long)eu * (2 * D);
-          if constexpr (FPL == 1) {
-            x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(rp + o16));
-          } else if constexpr (MODE == 1) {   // the lane's two codes
-            x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(rp + 2 * lane));
-          } else {
-            int ob = o16;
-            if constexpr (MODE == 2)   // word lane/2 of an 8-bit row
-              if (__builtin_amdgcn_readlane(__float_as_int(sc), u) < 0) ob = o8;
-            x[u] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(rp + ob));
-          }
+      for (int v = 0; v < 32; ++v) {
+        const int u = 32 * hf + v;
+        const unsigned char* rp = src + (long long)__builtin_amdgcn_readlane(k.e, u) * (2 * D);
+        // staging rows are read once: non-temporal, so they do not displace other lines
+        if constexpr (FPL == 1) {
+          x[hf][v] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(rp + o16));
+        } else if constexpr (MODE == 1) {   // the lane's two codes
+          x[hf][v] =
+              __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(rp + 2 * lane));
+        } else {
+          int ob = o16;
+          if constexpr (MODE == 2)   // word lane/2 of an 8-bit row
+            if (__builtin_amdgcn_readlane(__float_as_int(sc), u) < 0) ob = o8;
+          x[hf][v] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(rp + ob));
         }
-      };
-      auto add_rows = [&](auto mc) {
-        constexpr int MODE = decltype(mc)::value;
+      }
+    };
+    if (k.mode == 1) go(M1{});
+    else if (k.mode == 0) go(M0{});
+    else go(M2{});
+  };
+  auto add_half = [&](const RBlk& k, int hf) {
+    const float sc = half ? k.sk : k.sv;
+    auto go = [&](auto mc) {
+      constexpr int MODE = decltype(mc)::value;
 #pragma unroll
-        for (int u = 0; u < 64; ++u) {
-          const int ku = __builtin_amdgcn_readlane(kk, u);
-          const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), u));
-          if (ku != cur) {
-            close_to(ku);
-            cur = ku;
-          }
-          if constexpr (FPL == 1) {
-            a0 = fmaf(su, f16_lo(x[u]), a0);
-          } else if (MODE == 1 || (MODE == 2 && __float_as_int(su) < 0)) {
-            const uint32_t w = MODE == 1 ? x[u] : x[u] >> sh8;
-            a0 = fmaf((float)(w & 0xffu), -su, a0);
-            a1 = fmaf((float)((w >> 8) & 0xffu), -su, a1);
-            corr -= su;
-          } else {
-            a0 = fmaf(su, f16_lo(x[u]), a0);
-            a1 = fmaf(su, f16_hi(x[u]), a1);
-          }
+      for (int v = 0; v < 32; ++v) {
+        const int u = 32 * hf + v;
+        const int ku = __builtin_amdgcn_readlane(k.kk, u);
+        const float su = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sc), u));
+        if (ku != cur) {
+          close_key();
+          cur = ku;
         }
-      };
-      using M0 = std::integral_constant<int, 0>;
-      using M1 = std::integral_constant<int, 1>;
-      using M2 = std::integral_constant<int, 2>;
-      if (mode == 1) load_rows(M1{});
-      else if (mode == 0) load_rows(M0{});
-      else load_rows(M2{});
-      const float2 st_n = bfac[(eb + row_of(ent_n)) >> 4];
-      if (mode == 1) add_rows(M1{});
-      else if (mode == 0) add_rows(M0{});
-      else add_rows(M2{});
-      ent = ent_n;
-      st = st_n;
-    }
-  }
-  close_to(nk);
-  // a malformed list may skip keys: every row of the bucket is written
+        const uint32_t xv = x[hf][v];
+        if constexpr (FPL == 1) {
+          a0 = fmaf(su, f16_lo(xv), a0);
+        } else if (MODE == 1 || (MODE == 2 && __float_as_int(su) < 0)) {
+          const uint32_t w = MODE == 1 ? xv : xv >> sh8;
+          a0 = fmaf((float)(w & 0xffu), -su, a0);
+          a1 = fmaf((float)((w >> 8) & 0xffu), -su, a1);
+          corr -= su;
+        } else {
+          a0 = fmaf(su, f16_lo(xv), a0);
+          a1 = fmaf(su, f16_hi(xv), a1);
+        }
+      }
+    };
+    if (k.mode == 1) go(M1{});
+    else if (k.mode == 0) go(M0{});
+    else go(M2{});
+  };
+  const uint32_t* pm = perm + eb;
+  DSV_WALK_BUCKET(kStage8<D>)
+  close_key();
+  // zero rows for the keys nobody selected
   for (int key = 0; key < nk; ++key)
     if (!((done >> key) & 1u)) put(key, 0.f, 0.f);
 }
+#undef DSV_WALK_BUCKET
 
 // LDS copy of the group's Q and dO rows (bf16, [member][feature]). Chunk c (8 features,
 // 16 bytes) of row r is stored at chunk position c ^ (r mod D/8): the 16-byte reads of the
