@@ -175,7 +175,11 @@ struct Flag {
   static constexpr bool value = B;
 };
 
-__device__ __forceinline__ int clamp_key(int key, int S) { return min(max(key, 0), S - 1); }
+// A key from an index list, clamped into [0, S) as an unsigned value: a negative key reads key
+// S - 1, like one >= S (one instruction; only malformed lists hold such keys).
+__device__ __forceinline__ int clamp_key(int key, int S) {
+  return (int)min((uint32_t)key, (uint32_t)S - 1u);
+}
 
 // Token index of member j of group g (groups are gt x gh x gw boxes of the T x Hh x W grid,
 // numbered row-major; members row-major over (dt, dy, dx)).

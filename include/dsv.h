@@ -24,8 +24,9 @@
  *     row of (b,h,g) starts at NG*(b*sum_h k_h + sum_{h'<h} k_h') + g*k_h and holds k_h
  *     strictly ascending key indices in [0,S). Total length B*NG*sum_h k_h.
  *     A list that breaks this is memory-safe: the attention kernels clamp every key into
- *     [0,S); the forward and dQ then use the clamped keys as listed (repeats counted), and
- *     dK/dV are unspecified (finite) for such a list.
+ *     [0,S) (a key >= S, and a negative one, is read as key S-1); the forward and dQ then
+ *     use the clamped keys as listed (repeats counted), and dK/dV are unspecified (finite)
+ *     for such a list.
  *   k_per_head: HOST array of H int32, 1 <= k_h <= S (k_h = S is dense attention).
  *   Scale: softmax(scale * q.k), no causal mask; the LSE is natural-log and includes the scale.
  *

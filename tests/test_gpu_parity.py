@@ -398,7 +398,9 @@ def test_malformed_index_rows_are_memory_safe():
         assert bool(torch.isfinite(t.float()).all())
     mem = members(cfg)
     for h in range(cfg.heads):
-        rows = np.clip(gpu_rows(cfg, x, bad, 0, h).astype(np.int64), 0, S - 1)
+        # the kernels' clamp: any key outside [0, S), negative ones included, reads S - 1
+        rows = gpu_rows(cfg, x, bad, 0, h).astype(np.int64)
+        rows = np.where((rows < 0) | (rows >= S), S - 1, rows)
         ro, rl = oracle_fwd(cfg, x, rows, 0, h, mem=mem)   # any list: repeats count twice
         e = (maxerr(f64(o[0, h]), ro), maxerr(f64(lse[0, h]), rl))
         assert max(e) <= TOL[cfg.dtype], (h, e)
