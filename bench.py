@@ -55,20 +55,44 @@ def n_edges(cfg, ks):
     return cfg.batch * cfg.n_groups * sum(ks)
 
 
-def bwd_stage_bytes(cfg, ks):
+def bwd_stage_bytes(cfg, ks, share8=0.0):
     """HBM bytes of the staged backward design per step (backward kernel, reduce).
 
-    Backward kernel (per (b,h) slot, E = NG*k edges): staging rows written, 4dE (an fp16 dV
-    row and dK row), their scales, E/2, idx reads, 4E, Q, K, V, O and dO read once, 10*S*d,
-    LSE, 4*S, and dQ written once, 4*S*d. Reduce: staging rows and scales read once,
-    E*(4d + 1/2), its edge list, 4E, dK and dV written once, 8*S*d."""
+    A staged edge writes a dV row and a dK row: d bytes each as 8-bit codes (the share share8
+    of the rows) or 2d bytes each in fp16, plus block factors, E/2 bytes. Backward kernel (per
+    (b,h) slot, E = NG*k edges): the staging rows and factors, idx reads, 4E, Q, K, V, O and dO
+    read once, 10*S*d, LSE, 4*S, and dQ written once, 4*S*d. Reduce: staging rows and factors
+    read once, its edge list, 4E, dK and dV written once, 8*S*d."""
     B, S, d, NG = cfg.batch, cfg.seq, cfg.head_dim, cfg.n_groups
+    row = share8 * 2 * d + (1.0 - share8) * 4 * d + 0.5
     k1 = red = 0
     for kh in ks:
         E = NG * kh
-        k1 += B * (E * (4 * d + 0.5) + 4 * E + 10 * S * d + 4 * S + 4 * S * d)
-        red += B * (E * (4 * d + 0.5) + 4 * E + 8 * S * d)
+        k1 += B * (E * row + 4 * E + 10 * S * d + 4 * S + 4 * S * d)
+        red += B * (E * row + 4 * E + 8 * S * d)
     return k1, red
+
+
+def staged_8bit_share(p, cfg, ks, xi, o, lse, idx):
+    """Share of the backward's staging rows written as 8-bit codes, read from the block factor
+    table (sign bit set: 8-bit) that a backward with a one-slot workspace leaves for its last
+    slot (the last in launch order). Layout as pinned by the ABI tests; None for the fp32 path."""
+    if cfg.dtype != "bf16":
+        return None
+    need = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks)
+    ws = torch.zeros(need, dtype=torch.uint8, device=o.device)
+    dsv.sparse_attn_bwd(p, xi["q"], xi["k"], xi["v"], o, xi["do"], lse, idx, ks, xi["scale"],
+                        ws=ws)
+    torch.cuda.synchronize()
+    al = lambda v: -(-v // 256) * 256  # noqa: E731
+    NG, nb = cfg.n_groups, -(-cfg.seq // 32)
+    pad = lambda k: -(-k // 32) * 32  # noqa: E731
+    e = NG * pad(max(ks))
+    off = 2 * al(NG * (nb + 1) * 4) + 2 * al((nb + 1) * 4) + al(e * 4)
+    last = dsv.plan_order(list(ks))[-1]
+    blocks = NG * pad(ks[last]) // 16
+    fac = ws[off:off + e // 16 * 8].view(torch.float32).view(-1, 2)[:blocks, 0]
+    return float(torch.signbit(fac).float().mean())
 
 
 def topk_roofline(cfg, ks):
@@ -362,14 +386,18 @@ def main():
                 pre.append(hip_elapsed_ms(e[4 * c], e[4 * c + 1]))
                 p1.append(hip_elapsed_ms(e[4 * c + 1], e[4 * c + 2]))
                 red.append(hip_elapsed_ms(e[4 * c + 2], e[4 * c + 3]))
-        _, b2 = bwd_stage_bytes(cfg, ks)
+        # the last step's inputs, which idx, o and lse still hold
+        share8 = staged_8bit_share(p, cfg, ks, xs[(steps - 1) % n_sets], o, lse, idx)
+        _, b2 = bwd_stage_bytes(cfg, ks, share8 or 0.0)
         kernels["attn_bwd_bf16"] = {"op": "dsv_sparse_attn_bwd", "launches_per_step": nch,
                                     "ms_per_launch": mean(p1), "ms_median": med(p1),
                                     "bound": "mfma", "units_per_launch": f_bwd / nch}
         kernels["bucket_reduce"] = {"op": "dsv_sparse_attn_bwd", "launches_per_step": nch,
                                     "ms_per_launch": mean(red), "ms_median": med(red),
                                     "bound": "hbm", "units_per_launch": b2 / nch,
-                                    "note": "bytes of the staged design: fp16 rows read once"}
+                                    "staged_8bit_share": share8,
+                                    "note": "bytes of the staged design: rows (8-bit codes "
+                                            "or fp16) and block factors read once"}
         kernels["bwd_index_prepasses"] = {
             "op": "dsv_sparse_attn_bwd", "launches_per_step": nch, "ms_per_launch": mean(pre),
             "ms_median": med(pre), "bound": None,
