@@ -77,6 +77,9 @@ def staged_8bit_share(p, cfg, ks, xi, o, lse, idx):
     """Share of the backward's staging rows written as 8-bit codes, read from the block factor
     table (sign bit set: 8-bit) that a backward with a one-slot workspace leaves for its last
     slot (the last in launch order). Layout as pinned by the ABI tests; None for the fp32 path."""
+    import torch
+
+    import dynamic_sparse_attention_rank_amd as dsv
     if cfg.dtype != "bf16":
         return None
     need = dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks)

@@ -21,13 +21,11 @@
 //   * dK/dV: each (group, selected key) edge yields one row of dV and one of dK, summed over
 //     all groups that selected the key. fp32 atomics on this chip sustain only ~0.33 T adds/s,
 //     so the rows are not added in place. The edge (g, p) owns staging row g*padded_k + p.
-//     A-priori bounds per 16-key block (|dV| <= sum P * max|dO|, |dK| <= scale * sum|dS| *
-//     max|Q|) choose its format per 32-key chunk: at d = 128, where both bounds of both blocks
-//     are at most kStage8Bound, the rows are 8-bit codes with one scale per block from the
-//     block's largest entry m (absolute error <= m/254 <= kStage8Bound/254 per entry);
-//     elsewhere fp16 entries with one power-of-two scale per block (relative error <= 2^-11).
-//     The rows are written with whole-line non-temporal stores, the block scales to a small
-//     table that the reduce reads through L2.
+//     Per (tensor, 16-key block) the block's largest entry m chooses the format: at d = 128
+//     with m <= kStage8Bound, 8-bit codes scaled by m (absolute error <= m/254 <= 5e-4 per
+//     entry); else fp16 times a power of two (relative error <= 2^-11). The rows are written
+//     with whole-line non-temporal stores, one factor per block to a small table that the
+//     reduce reads through L2.
 //     Small pre-passes list, for every 32-key bucket, its edges in (group, position) order;
 //     a reduce kernel then sums each bucket's rows in LDS (one wave per bucket and half, one
 //     row per instruction, no atomics) and writes every dK/dV row exactly once, so dK/dV are
@@ -63,20 +61,23 @@ __device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, i
 constexpr int kBucketLog2 = 5;
 constexpr int kBucket = 1 << kBucketLog2;
 constexpr int kMaxChunk = 64;    // (b, h) slots per chunk
-// Staged dV|dK partial rows are fp16 times one power-of-two scale per (group, 16-key block):
-// kStageMax / bound rounded down to a power of two keeps every scaled entry within
-// kStageMax (fp16 reaches 65504), and fp16's 11-bit significand gives each entry a relative
-// error <= 2^-11 whatever its size, down to 2^-28 of the bound where fp16 turns subnormal.
+// fp16 staging rows are the entries times one power-of-two scale per (group, 16-key block):
+// kStageMax / m (m the block's largest |entry|) rounded down to a power of two keeps every
+// scaled entry within kStageMax (fp16 reaches 65504), and fp16's 11-bit significand gives each
+// entry a relative error <= 2^-11 whatever its size, down to 2^-28 of m where fp16 turns
+// subnormal.
 constexpr float kStageMax = 16384.f;
-// Chunks whose dV and dK bounds are all within kStage8Bound are staged as 8-bit rows (d = 128):
-// code = 128 + round(x * 127 / m) with m the largest |x| of the 16-key block, so every entry is
-// off by at most m/254 <= kStage8Bound/254 ~ 2e-3, and a row takes half the bytes of fp16.
-constexpr float kStage8Bound = 0.5f;
+// Blocks whose largest |entry| m (in true units) is within kStage8Bound are staged as 8-bit
+// rows (d = 128): code = 128 + round(x * 127 / m), so every entry is off by at most
+// m/254 <= kStage8Bound/254 ~ 5e-4, and a row takes half the bytes of fp16. (At 0.5 the worst
+// dK/dV error over the 20 Training steps reached 82% of the 2e-2 bar: a key's sum carries the
+// errors of some 50 groups' rows.)
+constexpr float kStage8Bound = 0.125f;
 template <int D>
 constexpr bool kStage8 = D == 128;
 
 // kStageMax / bound rounded down to a power of two (clamped to [2^-126, 2^100]); 0 if bound
-// is not positive.
+// is not positive (the block is all zero).
 __device__ __forceinline__ float pow2_scale(float bound) {
   if (!(bound > 0.f)) return 0.f;
   const float x =
@@ -341,14 +342,15 @@ typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 // A block of 64 list entries, one per lane: staging row, key offset, the lane's dV and dK
 // factors (lanes past the end of the list: zero, same sign, so that they add nothing) and the
-// format mode of its rows: all fp16 (0), all 8-bit (1), mixed (2); the same in every lane.
+// format mode of the wave's tensor's rows (dV and dK blocks choose their formats apart): all
+// fp16 (0), all 8-bit (1), mixed (2); the same in every lane.
 struct RBlk {
   uint32_t e;
   int kk, mode;
   float sv, sk;
 };
 __device__ __forceinline__ RBlk make_rblk(uint32_t ent, float2 st, long long r0, long long s1,
-                                          long long nrows, bool pair) {
+                                          long long nrows, bool pair, int half) {
   const int lane = threadIdx.x;
   RBlk k;
   const int n = (int)std::min<long long>(64, s1 - r0);   // <= 0 past the list: no row counts
@@ -356,7 +358,7 @@ __device__ __forceinline__ RBlk make_rblk(uint32_t ent, float2 st, long long r0,
   k.kk = (int)(ent & 31u);
   k.sv = lane < n ? st.x : copysignf(0.f, st.x);
   k.sk = lane < n ? st.y : copysignf(0.f, st.y);
-  const uint64_t m8 = __builtin_amdgcn_ballot_w64(__float_as_int(k.sv) < 0);
+  const uint64_t m8 = __builtin_amdgcn_ballot_w64(__float_as_int(half ? k.sk : k.sv) < 0);
   k.mode = !pair || m8 == 0 ? 0 : m8 == ~0ull ? 1 : 2;
   return k;
 }
@@ -377,14 +379,14 @@ __device__ __forceinline__ RBlk make_rblk(uint32_t ent, float2 st, long long r0,
     const uint32_t ent0 = pm[std::min<long long>(s0 + lane, s1 - 1)];                         \
     const float2 st0 = bfac[(eb + row_of(ent0)) >> 4];                                        \
     uint32_t ent1 = pm[std::min<long long>(s0 + 64 + lane, s1 - 1)];                          \
-    RBlk cur_b = make_rblk(ent0, st0, s0, s1, nrows, PAIR);                                   \
+    RBlk cur_b = make_rblk(ent0, st0, s0, s1, nrows, PAIR, half);                             \
     load_half(cur_b, 0);                                                                      \
     load_half(cur_b, 1);                                                                      \
     for (long long r0 = s0; r0 < s1; r0 += 64) {                                              \
       const float2 st1 = bfac[(eb + row_of(ent1)) >> 4];                                      \
       const uint32_t ent2 = pm[std::min<long long>(r0 + 128 + lane, s1 - 1)];                 \
       add_half(cur_b, 0);                                                                     \
-      const RBlk nxt = make_rblk(ent1, st1, r0 + 64, s1, nrows, PAIR);                        \
+      const RBlk nxt = make_rblk(ent1, st1, r0 + 64, s1, nrows, PAIR, half);                  \
       load_half(nxt, 0);                                                                      \
       add_half(cur_b, 1);                                                                     \
       load_half(nxt, 1);                                                                      \
@@ -572,9 +574,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
   // staging row of edge (g, p): the slot's first row + g*padded_k + p (index order)
   const long long grow = ch.edge_base[sl] + (long long)g * padded_k(kh);
 
-  // ---- per-group set-up: Q and dO rows into LDS, Delta = dO.O, LSE, max |dO| and max |Q|
-  // (the bounds of the 16-bit dV|dK staging rows). CPR lanes per row, one chunk each.
-  float max_do = 0.f, max_q = 0.f;
+  // ---- per-group set-up: Q and dO rows into LDS, Delta = dO.O and LSE. CPR lanes per row,
+  // one chunk each.
   {
     const int rr = lane / CPR, c = lane % CPR;
     for (int r0 = 0; r0 < 16 * QBP; r0 += 64 / CPR) {
@@ -591,8 +592,6 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         for (int w = 0; w < 4; ++w) {
           dacc = fmaf(bf16_lo(dv4[w]), bf16_lo(ov[w]), dacc);
           dacc = fmaf(bf16_hi(dv4[w]), bf16_hi(ov[w]), dacc);
-          max_do = fmaxf(max_do, fmaxf(fabsf(bf16_lo(dv4[w])), fabsf(bf16_hi(dv4[w]))));
-          max_q = fmaxf(max_q, fmaxf(fabsf(bf16_lo(qv[w])), fabsf(bf16_hi(qv[w]))));
         }
       }
       *reinterpret_cast<u32x4*>(&lds.qn[swz<D>(r, 8 * c)]) = qv;
@@ -604,11 +603,6 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         lds.lse2[r] = r < G ? lse[bh * geo.S + n] * kLog2e : INFINITY;
       }
     }
-  }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    max_do = wave_xor_max(max_do, m);
-    max_q = wave_xor_max(max_q, m);
   }
   __syncthreads();
 
@@ -671,10 +665,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       }
     };
     u32x4 pa[2][NM], dsa[2][NM];
-    float2 step[2];
-    float sv_[2], sk_[2];   // fp16 staging scales of blocks kb
-    bool ok8[2];   // block kb may be staged in 8 bits (both bounds within kStage8Bound)
-    // ---- P, dS of block kb, their fp16 staging scales, the dV / dK operands and the dS tile
+    // ---- P, dS of block kb, the dV / dK operands and the dS tile
     auto softmax = [&](const int kb, const floatx4 (&s)[QB], const floatx4 (&dp)[QB]) {
       const bool kvalid = cb + 16 * kb + li < kh;
       float pv[QBP][4], dsv_[QBP][4];
@@ -695,32 +686,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       for (int qb = QB; qb < QBP; ++qb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) pv[qb][j] = dsv_[qb][j] = 0.f;
-      // The dV and dK rows of this chunk's edges are staged in fp16 with one power-of-two
-      // scale per 16-key block (kb). |dV[d]| <= sum_n P * max|dO| and |dK[d]| <= scale *
-      // sum_n |dS| * max|Q| bound every entry of a key's rows; the block's largest bound sets
-      // sv, sk (pow2_scale). The fp16 path multiplies the dV / dK products by them before the
-      // fp16 conversion (a power of two commutes with the roundings of the bf16 operands and
-      // of the fp32 sums); the 8-bit path needs no such scaling.
       {
-        float cp = 0.f, cd = 0.f;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            cp += pv[qb][j];
-            cd += fabsf(dsv_[qb][j]);
-          }
-        // column sums over the members, then the largest column bound of the 16 keys
-        cp = max_in_row16(sum_over_rows(cp));
-        cd = max_in_row16(sum_over_rows(cd));
-        const float sv = pow2_scale(cp * max_do);
-        const float sk = pow2_scale(cd * max_q);   // dK = scale * (sum dS q): scale in the step
-        ok8[kb] = cp * max_do <= kStage8Bound && cd * max_q * scale <= kStage8Bound;
-        sv_[kb] = sv;
-        sk_[kb] = sk;
-        // sv, sk are powers of two, so their reciprocals are exact
-        step[kb] = make_float2(sv > 0.f ? __builtin_amdgcn_rcpf(sv) : 0.f,
-                               sk > 0.f ? __builtin_amdgcn_rcpf(sk) * scale : 0.f);
         // B operands of dO^T P / Q^T dS: column li <-> key, slot (lg, e) <-> member
         // 16(2m + e/4) + 4lg + e%4
 #pragma unroll
@@ -791,160 +757,96 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         for (int qb = 0; qb < QB; ++qb) dqacc[qb][fb] = mfma_bf16(kT[fb], bds[qb], dqacc[qb][fb]);
     }
 
-    // ---- dV^T = dO^T P, dK^T = Q^T dS (pre-scaled, see above). A operands by transposed LDS
-    // reads: row li <-> feature 16fb + li, slot (lg, e) <-> member 32m + 16(e/4) + 4lg + e%4.
-    // Lane: key 16kb + li, features 16fb + 4lg + j. The rows are written once and read back by
-    // the reduce long after, so the stores are non-temporal and cover whole 128-byte lines
-    // (half-line non-temporal stores are far slower); they are the bulk of this kernel's HBM
-    // traffic. fac[t][kb]: the factor the reduce applies to the staged entries of tensor t
-    // (0 = dV, 1 = dK) in block kb, negative (sign bit set) for 8-bit blocks.
-    float fac[2][2];
-    auto stage_f16 = [&]() {
-      // Feature blocks go in pairs (2fp, 2fp + 1) so that every lane holds 16-byte granules:
-      // staging position 32fp + 8lg + t holds feature 32fp + 4lg + t (t < 4) or
-      // 32fp + 16 + 4lg + t - 4 (t >= 4); the reduce undoes this order.
-      u32x4 xv[2], xk[2];   // granules of the even feature-block pair, held for the line swap
+    // ---- dV^T = dO^T P (t = 0), dK^T = Q^T dS (t = 1, dK = scale times it), one tensor's
+    // 32 x d tile at a time: A operands by transposed LDS reads (row li <-> feature 16fb + li,
+    // slot (lg, e) <-> member 32m + 16(e/4) + 4lg + e%4), each read once for both 16-key
+    // blocks; lane: key 16kb + li, features 16fb + 4lg + j. Then per block kb its largest
+    // |entry| m (the lane's features, the key's 3 other lanes, the block's 16 keys) sets the
+    // block's format, the same in every lane:
+    //   * true-unit m <= kStage8Bound (d = 128): 8-bit codes 128 + round(x * 127/m); lane
+    //     (li, lg) holds bytes 32lg .. 32lg + 31 of row 16kb + li (byte 32lg + 4fb + j <->
+    //     feature 16fb + 4lg + j); factor -m/127 (sign bit set, even when m = 0);
+    //   * else fp16 times the power of two kStageMax/m rounded down (pow2_scale); feature
+    //     blocks in pairs (2fp, 2fp + 1), staging position 32fp + 8lg + t holding feature
+    //     32fp + 4lg + t (t < 4) or 32fp + 16 + 4lg + t - 4; factor its reciprocal.
+    // Both kinds of row start the row's 2d-byte place. Lanes li and li ^ 8 swap 16-byte
+    // granules (DPP row_ror:8 with a bank mask: lanes 8..15 of each row take the other half
+    // of lane li - 8, lanes 0..7 of lane li + 8), so every store writes 8 whole 128-byte
+    // lines. The rows are written once and read back by the reduce long after, so the stores
+    // are non-temporal; they are the bulk of this kernel's HBM traffic.
+    float fac[2][2];   // [t][kb]: what the reduce multiplies the staged entries by
+    const long long r0 = grow + cb + (li & 7);
+    auto swap_store = [&](const u32x4& lo, const u32x4& hi, uint16_t* dst, long long ra,
+                          int col16) {
+      u32x4 s1, s2;
 #pragma unroll
-      for (int fp = 0; fp < NDB / 2; ++fp) {
-        floatx4 av[2][2], ak[2][2];
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb) av[h2][kb] = ak[h2][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int fb = 2 * fp + h2;
-#pragma unroll
-          for (int m = 0; m < NM; ++m) {
-            const int r1 = 32 * m + 4 * lg + (li >> 2);
-            const int col = 16 * fb + 4 * (li & 3);
-            const u32x2 d1 = lds_read_tr16(&lds.dn[swz<D>(r1, col)]);
-            const u32x2 d2 = lds_read_tr16(&lds.dn[swz<D>(r1 + 16, col)]);
-            const u32x2 q1 = lds_read_tr16(&lds.qn[swz<D>(r1, col)]);
-            const u32x2 q2 = lds_read_tr16(&lds.qn[swz<D>(r1 + 16, col)]);
-            const u32x4 adoT = {d1[0], d1[1], d2[0], d2[1]};
-            const u32x4 aqT = {q1[0], q1[1], q2[0], q2[1]};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-              av[h2][kb] = mfma_bf16(adoT, pa[kb][m], av[h2][kb]);
-              ak[h2][kb] = mfma_bf16(aqT, dsa[kb][m], ak[h2][kb]);
-            }
-          }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          // row cb + 16kb + li < padded_k: past the row end it is a (zero) padding row
-          const float v = sv_[kb], q = sk_[kb];
-          const u32x4 wv = {pack_f16(av[0][kb][0] * v, av[0][kb][1] * v),
-                            pack_f16(av[0][kb][2] * v, av[0][kb][3] * v),
-                            pack_f16(av[1][kb][0] * v, av[1][kb][1] * v),
-                            pack_f16(av[1][kb][2] * v, av[1][kb][3] * v)};
-          const u32x4 wk = {pack_f16(ak[0][kb][0] * q, ak[0][kb][1] * q),
-                            pack_f16(ak[0][kb][2] * q, ak[0][kb][3] * q),
-                            pack_f16(ak[1][kb][0] * q, ak[1][kb][1] * q),
-                            pack_f16(ak[1][kb][2] * q, ak[1][kb][3] * q)};
-          if ((fp & 1) == 0) {
-            xv[kb] = wv;
-            xk[kb] = wk;
-          } else {
-            // a lane holds granules 8p + lg (even fp) and 8p + 4 + lg (odd fp) of row li; after
-            // swapping with lane li ^ 8 every store writes 8 whole 128-byte lines: rows
-            // 16kb + (li & 7) (first) and 16kb + (li & 7) + 8 (second), granule 8p + 4(li / 8) + lg
-            // DPP row_ror:8 with a bank mask: lanes 8..15 of each row (banks 2, 3) take the
-            // odd granule of lane li - 8, lanes 0..7 (banks 0, 1) the even granule of lane li + 8
-            u32x4 av1, av2, ak1, ak2;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              av1[w] = __builtin_amdgcn_update_dpp(xv[kb][w], wv[w], 0x128, 0xf, 0xc, false);
-              av2[w] = __builtin_amdgcn_update_dpp(wv[w], xv[kb][w], 0x128, 0xf, 0x3, false);
-              ak1[w] = __builtin_amdgcn_update_dpp(xk[kb][w], wk[w], 0x128, 0xf, 0xc, false);
-              ak2[w] = __builtin_amdgcn_update_dpp(wk[w], xk[kb][w], 0x128, 0xf, 0x3, false);
-            }
-            const long long ra = grow + cb + 16 * kb + (li & 7);
-            const int gcol = 8 * (8 * (fp >> 1) + 4 * (li >> 3) + lg);
-            __builtin_nontemporal_store(av1, reinterpret_cast<u32x4*>(cv + ra * D + gcol));
-            __builtin_nontemporal_store(av2, reinterpret_cast<u32x4*>(cv + (ra + 8) * D + gcol));
-            __builtin_nontemporal_store(ak1, reinterpret_cast<u32x4*>(ck + ra * D + gcol));
-            __builtin_nontemporal_store(ak2, reinterpret_cast<u32x4*>(ck + (ra + 8) * D + gcol));
-          }
-        }
+      for (int w = 0; w < 4; ++w) {
+        s1[w] = __builtin_amdgcn_update_dpp(lo[w], hi[w], 0x128, 0xf, 0xc, false);
+        s2[w] = __builtin_amdgcn_update_dpp(hi[w], lo[w], 0x128, 0xf, 0x3, false);
       }
+      __builtin_nontemporal_store(s1, reinterpret_cast<u32x4*>(dst + ra * D + col16));
+      __builtin_nontemporal_store(s2, reinterpret_cast<u32x4*>(dst + (ra + 8) * D + col16));
+    };
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      floatx4 acc[NDB][2];
+#pragma unroll
+      for (int fb = 0; fb < NDB; ++fb) acc[fb][0] = acc[fb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int fb = 0; fb < NDB; ++fb)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          const int r1 = 32 * m + 4 * lg + (li >> 2);
+          const int c = 16 * fb + 4 * (li & 3);
+          const uint16_t* a = t == 0 ? lds.dn : lds.qn;
+          const u32x2 a1 = lds_read_tr16(&a[swz<D>(r1, c)]);
+          const u32x2 a2 = lds_read_tr16(&a[swz<D>(r1 + 16, c)]);
+          const u32x4 aT = {a1[0], a1[1], a2[0], a2[1]};
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            acc[fb][kb] = mfma_bf16(aT, t == 0 ? pa[kb][m] : dsa[kb][m], acc[fb][kb]);
+        }
+      uint16_t* dst = t == 0 ? cv : ck;
+      const float tsc = t == 0 ? 1.f : scale;   // tile units -> true units
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        fac[0][kb] = step[kb].x;
-        fac[1][kb] = step[kb].y;
-      }
-    };
-    // 8-bit rows (d = 128), one 16 x d tile (block kb of one tensor) at a time: its largest
-    // |entry| m (the lane's 32 features, the key's 3 other lanes, the block's 16 keys), then
-    // codes 128 + round(x * 127/m). Lane (li, lg) holds bytes 32lg .. 32lg + 31 of row
-    // 16kb + li: byte 32lg + 4fb + j <-> feature 16fb + 4lg + j. The same lane swap as the fp16
-    // rows makes every store cover 8 whole lines.
-    auto stage_8 = [&]() {
-      if constexpr (kStage8<D>) {
-        const long long r0 = grow + cb + (li & 7);
-        const int col = 32 * lg + 16 * (li >> 3);
+        float mx = 0.f;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int fb = 0; fb < NDB; ++fb)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            // one 16-key block at a time keeps the tile at 32 registers, as in the fp16 path
-            floatx4 acc[NDB];
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(acc[fb][kb][j]));
+        mx = max_in_row16(max_over_rows(mx));
+        const long long ra = r0 + 16 * kb;
+        if (kStage8<D> && __builtin_amdgcn_readfirstlane((int)(mx * tsc <= kStage8Bound))) {
+          // |x| <= m and 127 * rcp(m) exceeds 127/m by at most an ulp: |x * inv| < 127.5
+          const float inv = mx > 0.f ? 127.f * __builtin_amdgcn_rcpf(mx) : 0.f;
+          fac[t][kb] = -(mx * (1.f / 127.f)) * tsc;
+          u32x4 g0, g1;
 #pragma unroll
-            for (int fb = 0; fb < NDB; ++fb) acc[fb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int fb = 0; fb < NDB; ++fb)
-#pragma unroll
-              for (int m = 0; m < NM; ++m) {
-                const int r1 = 32 * m + 4 * lg + (li >> 2);
-                const int c = 16 * fb + 4 * (li & 3);
-                const uint16_t* a = t == 0 ? lds.dn : lds.qn;
-                const u32x2 a1 = lds_read_tr16(&a[swz<D>(r1, c)]);
-                const u32x2 a2 = lds_read_tr16(&a[swz<D>(r1 + 16, c)]);
-                const u32x4 aT = {a1[0], a1[1], a2[0], a2[1]};
-                acc[fb] = mfma_bf16(aT, t == 0 ? pa[kb][m] : dsa[kb][m], acc[fb]);
-              }
-            float mx = 0.f;
-#pragma unroll
-            for (int fb = 0; fb < NDB; ++fb)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(acc[fb][j]));
-            mx = max_in_row16(max_over_rows(mx));
-            // |x| <= m and 127 * rcp(m) exceeds 127/m by at most an ulp: |x * inv| < 127.5
-            const float inv = mx > 0.f ? 127.f * __builtin_amdgcn_rcpf(mx) : 0.f;
-            // dK = scale * (sum dS q): the scale goes into the factor
-            fac[t][kb] = -(mx * (1.f / 127.f)) * (t == 0 ? 1.f : scale);   // sign bit set
-            u32x4 g0, g1;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              g0[w] = pack_i8(acc[w], inv);
-              g1[w] = pack_i8(acc[w + 4], inv);
-            }
-            // lanes li < 8 keep granule 0 of row li and take granule 0 of row li + 8; lanes
-            // li >= 8 keep granule 1 of row li and take granule 1 of row li - 8
-            u32x4 s1, s2;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              s1[w] = __builtin_amdgcn_update_dpp(g0[w], g1[w], 0x128, 0xf, 0xc, false);
-              s2[w] = __builtin_amdgcn_update_dpp(g1[w], g0[w], 0x128, 0xf, 0x3, false);
-            }
-            uint8_t* dst = reinterpret_cast<uint8_t*>(t == 0 ? cv : ck);
-            const long long ra = r0 + 16 * kb;
-            __builtin_nontemporal_store(s1, reinterpret_cast<u32x4*>(dst + ra * (2 * D) + col));
-            __builtin_nontemporal_store(s2,
-                                        reinterpret_cast<u32x4*>(dst + (ra + 8) * (2 * D) + col));
+          for (int w = 0; w < 4; ++w) {
+            g0[w] = pack_i8(acc[w][kb], inv);
+            g1[w] = pack_i8(acc[(w + 4) % NDB][kb], inv);
           }
+          swap_store(g0, g1, dst, ra, 16 * lg + 8 * (li >> 3));   // bytes 32lg + 16(li/8)
+        } else {
+          const float sc = pow2_scale(mx);   // a power of two: its reciprocal is exact
+          fac[t][kb] = sc > 0.f ? __builtin_amdgcn_rcpf(sc) * tsc : 0.f;
+#pragma unroll
+          for (int fp = 0; fp < NDB / 2; fp += 2) {
+            u32x4 x[2];   // granules of feature-block pairs fp (even) and fp + 1 (odd)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const floatx4& e0 = acc[2 * (fp + h2)][kb];
+              const floatx4& e1 = acc[2 * (fp + h2) + 1][kb];
+              x[h2] = u32x4{pack_f16(e0[0] * sc, e0[1] * sc), pack_f16(e0[2] * sc, e0[3] * sc),
+                            pack_f16(e1[0] * sc, e1[1] * sc), pack_f16(e1[2] * sc, e1[3] * sc)};
+            }
+            // lane: granules 8p + lg (even pair) and 8p + 4 + lg (odd) of row li, p = fp/2
+            swap_store(x[0], x[1], dst, ra, 8 * (8 * (fp >> 1) + 4 * (li >> 3) + lg));
+          }
+        }
       }
-    };
-    // one format for the whole chunk, the same in every lane. The empty asm makes the block
-    // factors exist before the branch: sunk below it, they would split the if/else into two
-    // ifs, and the compiler's wait for the prefetched keys would then assume a path without
-    // this chunk's stores and drain them all.
-    asm volatile("" ::"v"(step[0].x), "v"(step[0].y), "v"(step[1].x), "v"(step[1].y));
-    if (kStage8<D> && __builtin_amdgcn_readfirstlane((int)(ok8[0] && ok8[1])) != 0)
-      stage_8();
-    else
-      stage_f16();
+    }
     // both blocks' factors in one 16-byte store by every lane (one address, unconditional);
     // (grow + cb) is a multiple of 32, so the pair is 16-byte aligned
     *reinterpret_cast<float4*>(&bfac[(grow + cb) / 16]) =
