@@ -389,8 +389,10 @@ def main():
                 pre.append(hip_elapsed_ms(e[4 * c], e[4 * c + 1]))
                 p1.append(hip_elapsed_ms(e[4 * c + 1], e[4 * c + 2]))
                 red.append(hip_elapsed_ms(e[4 * c + 2], e[4 * c + 3]))
-        # the last step's inputs, which idx, o and lse still hold
-        share8 = staged_8bit_share(p, cfg, ks, xs[(steps - 1) % n_sets], o, lse, idx)
+        # the last step's inputs, which idx, o and lse still hold (an extra backward: skipped
+        # with --no-extras, as in the profiling runs; the reduce is then priced as fp16 rows)
+        share8 = (None if args.no_extras else
+                  staged_8bit_share(p, cfg, ks, xs[(steps - 1) % n_sets], o, lse, idx))
         _, b2 = bwd_stage_bytes(cfg, ks, share8 or 0.0)
         kernels["attn_bwd_bf16"] = {"op": "dsv_sparse_attn_bwd", "launches_per_step": nch,
                                     "ms_per_launch": mean(p1), "ms_median": med(p1),

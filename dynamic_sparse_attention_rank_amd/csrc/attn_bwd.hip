@@ -757,8 +757,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         for (int qb = 0; qb < QB; ++qb) dqacc[qb][fb] = mfma_bf16(kT[fb], bds[qb], dqacc[qb][fb]);
     }
 
-    // ---- dV^T = dO^T P (t = 0), dK^T = Q^T dS (t = 1, dK = scale times it), one tensor's
-    // 32 x d tile at a time: A operands by transposed LDS reads (row li <-> feature 16fb + li,
+    // ---- dV^T = dO^T P (t = 0), dK^T = Q^T dS (t = 1, dK = scale times it), the 32 x d tiles
+    // of both: A operands by transposed LDS reads (row li <-> feature 16fb + li,
     // slot (lg, e) <-> member 32m + 16(e/4) + 4lg + e%4), each read once for both 16-key
     // blocks; lane: key 16kb + li, features 16fb + 4lg + j. Then per block kb its largest
     // |entry| m (the lane's features, the key's 3 other lanes, the block's 16 keys) sets the
@@ -787,25 +787,32 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
       __builtin_nontemporal_store(s1, reinterpret_cast<u32x4*>(dst + ra * D + col16));
       __builtin_nontemporal_store(s2, reinterpret_cast<u32x4*>(dst + (ra + 8) * D + col16));
     };
+    // both tensors' tiles first (their MFMAs overlap the other tile's encoding)
+    floatx4 acc2[2][NDB][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      floatx4 acc[NDB][2];
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int fb = 0; fb < NDB; ++fb) acc[fb][0] = acc[fb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int fb = 0; fb < NDB; ++fb) acc2[t][fb][0] = acc2[t][fb][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int fb = 0; fb < NDB; ++fb)
+    for (int fb = 0; fb < NDB; ++fb)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) {
-          const int r1 = 32 * m + 4 * lg + (li >> 2);
-          const int c = 16 * fb + 4 * (li & 3);
+      for (int m = 0; m < NM; ++m) {
+        const int r1 = 32 * m + 4 * lg + (li >> 2);
+        const int c = 16 * fb + 4 * (li & 3);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
           const uint16_t* a = t == 0 ? lds.dn : lds.qn;
           const u32x2 a1 = lds_read_tr16(&a[swz<D>(r1, c)]);
           const u32x2 a2 = lds_read_tr16(&a[swz<D>(r1 + 16, c)]);
           const u32x4 aT = {a1[0], a1[1], a2[0], a2[1]};
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
-            acc[fb][kb] = mfma_bf16(aT, t == 0 ? pa[kb][m] : dsa[kb][m], acc[fb][kb]);
+            acc2[t][fb][kb] = mfma_bf16(aT, t == 0 ? pa[kb][m] : dsa[kb][m], acc2[t][fb][kb]);
         }
+      }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      auto& acc = acc2[t];
       uint16_t* dst = t == 0 ? cv : ck;
       const float tsc = t == 0 ? 1.f : scale;   // tile units -> true units
 #pragma unroll
