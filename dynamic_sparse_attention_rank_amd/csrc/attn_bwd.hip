@@ -647,7 +647,8 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
   // the loop end with the same prefetch-then-store sequence: the compiler's wait for the
   // prefetched K/V rows at the top of the loop then leaves the previous chunk's stores in
   // flight instead of draining them.
-  auto chunk = [&](const int cb) {
+  auto chunk = [&](const int cb, auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;   // keys past the row end in it
     // ---- S = Q K^T, dP = dO V^T of 16-key block kb; lane: key 16kb + li, members 16qb +
     // 4lg + j. The A operands (member 16qb + li, features 32ks + 8lg ..) are 16-byte LDS row
     // reads.
@@ -667,7 +668,7 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
     u32x4 pa[2][NM], dsa[2][NM];
     // ---- P, dS of block kb, the dV / dK operands and the dS tile
     auto softmax = [&](const int kb, const floatx4 (&s)[QB], const floatx4 (&dp)[QB]) {
-      const bool kvalid = cb + 16 * kb + li < kh;
+      const bool kvalid = !kTail || cb + 16 * kb + li < kh;
       float pv[QBP][4], dsv_[QBP][4];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -810,49 +811,70 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
             acc2[t][fb][kb] = mfma_bf16(aT, t == 0 ? pa[kb][m] : dsa[kb][m], acc2[t][fb][kb]);
         }
       }
+    // the four blocks' largest |entries| (tile units), then their formats
+    float mx4[2][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      auto& acc = acc2[t];
-      uint16_t* dst = t == 0 ? cv : ck;
-      const float tsc = t == 0 ? 1.f : scale;   // tile units -> true units
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         float mx = 0.f;
 #pragma unroll
         for (int fb = 0; fb < NDB; ++fb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(acc[fb][kb][j]));
-        mx = max_in_row16(max_over_rows(mx));
-        const long long ra = r0 + 16 * kb;
-        if (kStage8<D> && __builtin_amdgcn_readfirstlane((int)(mx * tsc <= kStage8Bound))) {
-          // |x| <= m and 127 * rcp(m) exceeds 127/m by at most an ulp: |x * inv| < 127.5
-          const float inv = mx > 0.f ? 127.f * __builtin_amdgcn_rcpf(mx) : 0.f;
-          fac[t][kb] = -(mx * (1.f / 127.f)) * tsc;
-          u32x4 g0, g1;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            g0[w] = pack_i8(acc[w][kb], inv);
-            g1[w] = pack_i8(acc[(w + 4) % NDB][kb], inv);
-          }
-          swap_store(g0, g1, dst, ra, 16 * lg + 8 * (li >> 3));   // bytes 32lg + 16(li/8)
-        } else {
-          const float sc = pow2_scale(mx);   // a power of two: its reciprocal is exact
-          fac[t][kb] = sc > 0.f ? __builtin_amdgcn_rcpf(sc) * tsc : 0.f;
-#pragma unroll
-          for (int fp = 0; fp < NDB / 2; fp += 2) {
-            u32x4 x[2];   // granules of feature-block pairs fp (even) and fp + 1 (odd)
-#pragma unroll
-            for (int h2 = 0; h2 < 2; ++h2) {
-              const floatx4& e0 = acc[2 * (fp + h2)][kb];
-              const floatx4& e1 = acc[2 * (fp + h2) + 1][kb];
-              x[h2] = u32x4{pack_f16(e0[0] * sc, e0[1] * sc), pack_f16(e0[2] * sc, e0[3] * sc),
-                            pack_f16(e1[0] * sc, e1[1] * sc), pack_f16(e1[2] * sc, e1[3] * sc)};
-            }
-            // lane: granules 8p + lg (even pair) and 8p + 4 + lg (odd) of row li, p = fp/2
-            swap_store(x[0], x[1], dst, ra, 8 * (8 * (fp >> 1) + 4 * (li >> 3) + lg));
-          }
-        }
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, fabsf(acc2[t][fb][kb][j]));
+        mx4[t][kb] = max_in_row16(max_over_rows(mx));
       }
+    auto is8 = [&](int t, int kb) {
+      return kStage8<D> && mx4[t][kb] * (t == 0 ? 1.f : scale) <= kStage8Bound;
+    };
+    auto enc8 = [&](int t, int kb) {
+      const float mx = mx4[t][kb];
+      // |x| <= m and 127 * rcp(m) exceeds 127/m by at most an ulp: |x * inv| < 127.5
+      const float inv = mx > 0.f ? 127.f * __builtin_amdgcn_rcpf(mx) : 0.f;
+      fac[t][kb] = -(mx * (1.f / 127.f)) * (t == 0 ? 1.f : scale);
+      u32x4 g0, g1;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        g0[w] = pack_i8(acc2[t][w][kb], inv);
+        g1[w] = pack_i8(acc2[t][(w + 4) % NDB][kb], inv);
+      }
+      swap_store(g0, g1, t == 0 ? cv : ck, r0 + 16 * kb, 16 * lg + 8 * (li >> 3));
+    };
+    auto enc16 = [&](int t, int kb) {
+      const float sc = pow2_scale(mx4[t][kb]);   // a power of two: its reciprocal is exact
+      fac[t][kb] = sc > 0.f ? __builtin_amdgcn_rcpf(sc) * (t == 0 ? 1.f : scale) : 0.f;
+#pragma unroll
+      for (int fp = 0; fp < NDB / 2; fp += 2) {
+        u32x4 x[2];   // granules of feature-block pairs fp (even) and fp + 1 (odd)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const floatx4& e0 = acc2[t][2 * (fp + h2)][kb];
+          const floatx4& e1 = acc2[t][2 * (fp + h2) + 1][kb];
+          x[h2] = u32x4{pack_f16(e0[0] * sc, e0[1] * sc), pack_f16(e0[2] * sc, e0[3] * sc),
+                        pack_f16(e1[0] * sc, e1[1] * sc), pack_f16(e1[2] * sc, e1[3] * sc)};
+        }
+        // lane: granules 8p + lg (even pair) and 8p + 4 + lg (odd) of row li, p = fp/2
+        swap_store(x[0], x[1], t == 0 ? cv : ck, r0 + 16 * kb,
+                   8 * (8 * (fp >> 1) + 4 * (li >> 3) + lg));
+      }
+    };
+    // all four blocks 8-bit (nearly every chunk on the workloads here): one straight run;
+    // otherwise block by block (each branch the same in every lane)
+    if (__builtin_amdgcn_readfirstlane((int)(is8(0, 0) && is8(0, 1) && is8(1, 0) && is8(1, 1)))) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) enc8(t, kb);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (__builtin_amdgcn_readfirstlane((int)is8(t, kb)))
+            enc8(t, kb);
+          else
+            enc16(t, kb);
+        }
     }
     // both blocks' factors in one 16-byte store by every lane (one address, unconditional);
     // (grow + cb) is a multiple of 32, so the pair is 16-byte aligned
@@ -860,8 +882,15 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
         make_float4(fac[0][0], fac[1][0], fac[0][1], fac[1][1]);
     wave_lds_fence();   // the next chunk overwrites the dS tile
   };
-  chunk(0);
-  for (int cb = 32; cb < kh; cb += 32) chunk(cb);
+  // full chunks carry no key masks; the partial last chunk is its own instantiation
+  const int kfull = kh & ~31;
+  if (kfull == 0) {
+    chunk(0, Flag<true>{});
+  } else {
+    chunk(0, Flag<false>{});
+    for (int cb = 32; cb < kfull; cb += 32) chunk(cb, Flag<false>{});
+    if (kfull < kh) chunk(kfull, Flag<true>{});
+  }
 
   // ---- store dQ (fp32): lane holds member 16qb + li, features 16fb + 4lg + j
 #pragma unroll
