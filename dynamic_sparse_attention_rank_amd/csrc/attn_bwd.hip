@@ -61,6 +61,7 @@ __device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, i
 constexpr int kBucketLog2 = 5;
 constexpr int kBucket = 1 << kBucketLog2;
 constexpr int kMaxChunk = 64;    // (b, h) slots per chunk
+constexpr int kPermWaves = 4;    // waves per bucket in the edge-list placement
 // fp16 staging rows are the entries times one power-of-two scale per (group, 16-key block):
 // kStageMax / m (m the block's largest |entry|) rounded down to a power of two keeps every
 // scaled entry within kStageMax (fp16 reaches 65504), and fp16's 11-bit significand gives each
@@ -119,6 +120,9 @@ __device__ __forceinline__ void chunk_slot(const Geom& geo, int s, int& b, int& 
 
 // Row entry points: rs[g][j] = first position of row g whose key lies in bucket >= j
 // (rs[g][nB] = k). One wave per row; rows are ascending, so each bucket's keys form one run.
+// Position p writes the buckets after its predecessor's, up to its own; the lanes load eight
+// 64-key steps of the row at once, and a step's predecessor buckets come from the lane below
+// (lane 0: the previous step's lane 63).
 __global__ __launch_bounds__(256) void row_bucket_starts(const int32_t* __restrict__ idx, Chunk ch,
                                                          uint32_t* __restrict__ rs, Geom geo) {
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
@@ -132,10 +136,21 @@ __global__ __launch_bounds__(256) void row_bucket_starts(const int32_t* __restri
   const int nB = n_buckets(geo.S);
   const int32_t* row = idx + geo.row_offset(b, h, g);
   uint32_t* r = rs + (long long)wave * (nB + 1);
-  for (int p = lane; p < kh; p += 64) {
-    const int jp = clamp_key(row[p], geo.S) >> kBucketLog2;
-    const int jq = p == 0 ? -1 : (clamp_key(row[p - 1], geo.S) >> kBucketLog2);
-    for (int j = jq + 1; j <= jp; ++j) r[j] = (uint32_t)p;
+  int prev = -1;   // bucket of the key before the step's first
+  for (int p0 = 0; p0 < kh; p0 += 8 * 64) {
+    int kv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) kv[u] = row[min(p0 + 64 * u + lane, kh - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int p = p0 + 64 * u + lane;
+      const int jp = clamp_key(kv[u], geo.S) >> kBucketLog2;
+      const int below = __shfl_up(jp, 1, 64);
+      const int jq = lane == 0 ? prev : below;
+      prev = __shfl(jp, 63, 64);
+      if (p < kh)
+        for (int j = jq + 1; j <= jp; ++j) r[j] = (uint32_t)p;
+    }
   }
   const int jl = clamp_key(row[kh - 1], geo.S) >> kBucketLog2;
   for (int j = jl + 1 + lane; j <= nB; j += 64) r[j] = (uint32_t)kh;
@@ -215,28 +230,28 @@ __global__ __launch_bounds__(256) void bucket_offsets(const uint32_t* __restrict
 
 // Bucket edge list, by key: perm[off[j] + i], i < tot[j], holds the edges (g, p) whose key
 // lies in bucket j, ordered by key, then by group, each as (slot-relative staging row
-// g*padded_k + p) << 5 | (key - 32 j). One wave per (slot, bucket), 64 groups per step. A lane
-// turns its group's run of keys in the bucket into a mask of key offsets (the run ascends, so
-// the run's i-th key sits at staging row e0 + i, i = the number of mask bits below it). A
-// first sweep counts each key's groups (one ballot per key) and keeps each group's mask and
-// first staging row in LDS (dynamic, 8 bytes per group, when the launch provides them), a scan
-// over the 32 counts gives each key's first list position, and a second sweep places every
-// edge after those of the key's earlier groups (ballot and lane-prefix count). A 128-byte line
-// of an index row holds
-// the keys of about ten consecutive buckets, so the block index is remapped to give each XCD a
-// contiguous range of buckets (one L2 then serves a line to all of them).
-__global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ rsT,
-                                                  const uint32_t* __restrict__ off,
-                                                  const int32_t* __restrict__ idx, Chunk ch,
-                                                  uint32_t* __restrict__ perm, Geom geo,
-                                                  int cached) {
+// g*padded_k + p) << 5 | (key - 32 j). kPermWaves waves per (slot, bucket), each over its own
+// run of 64-group steps. A lane turns its group's run of keys in the bucket into a mask of key
+// offsets (the run ascends, so the run's i-th key sits at staging row e0 + i, i = the number of
+// mask bits below it). A first sweep counts each key's groups (one ballot per key) and keeps
+// each group's mask and first staging row in LDS (dynamic, 8 bytes per group, when the launch
+// provides them); the waves' counts give each key's first list position per wave, and a
+// second sweep places every edge after those of the key's earlier groups (ballot and
+// lane-prefix count). A 128-byte line of an index row holds the keys of about ten consecutive
+// buckets, so the block index is remapped to give each XCD a contiguous range of buckets (one
+// L2 then serves a line to all of them).
+__global__ __launch_bounds__(64 * kPermWaves) void bucket_perm(
+    const uint32_t* __restrict__ rsT, const uint32_t* __restrict__ off,
+    const int32_t* __restrict__ idx, Chunk ch, uint32_t* __restrict__ perm, Geom geo, int cached) {
   extern __shared__ uint2 mcache[];   // [NG] {key mask, first staging row} when cached
+  __shared__ uint32_t wcnt[kPermWaves][kBucket];   // each wave's edges per key offset
   const int nB = n_buckets(geo.S);
   const int nblk = gridDim.x, xcd = blockIdx.x & 7;
   const int logical = xcd * (nblk >> 3) + min(xcd, nblk & 7) + (blockIdx.x >> 3);
   const int sl = logical / nB;
   const int j = logical - sl * nB;
-  const int lane = threadIdx.x;
+  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   int b, h;
   chunk_slot(geo, ch.s0 + sl, b, h);
   const uint32_t kh = (uint32_t)geo.k[h];
@@ -246,6 +261,10 @@ __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ r
   const int32_t* keys = idx + geo.row_offset(b, h, 0);   // row of group g: keys + g*k
   uint32_t* pm = perm + ch.edge_base[sl];
   const int key0 = j * kBucket;
+  // the wave's groups: a run of whole 64-group steps, in group order across the waves
+  const int nsteps = (geo.NG + 63) / 64;
+  const int spw = (nsteps + kPermWaves - 1) / kPermWaves;
+  const int gbeg = min(wv * spw, nsteps) * 64, gend = min((wv + 1) * spw, nsteps) * 64;
   // mask of the key offsets of group g0 + lane's run in the bucket; a = the run's first
   // position. A malformed (not ascending) row may repeat an offset: the mask then holds fewer
   // edges than the run, and no more than the list has room for are placed.
@@ -277,7 +296,7 @@ __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ r
   uint32_t cnt[kBucket];
 #pragma unroll
   for (int ko = 0; ko < kBucket; ++ko) cnt[ko] = 0;
-  for (int g0 = 0; g0 < geo.NG; g0 += 64) {
+  for (int g0 = gbeg; g0 < gend; g0 += 64) {
     uint32_t a;
     const uint32_t mask = run_mask(g0, a);
     if (cached && g0 + lane < geo.NG)
@@ -286,38 +305,56 @@ __global__ __launch_bounds__(64) void bucket_perm(const uint32_t* __restrict__ r
     for (int ko = 0; ko < kBucket; ++ko)
       cnt[ko] += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64((mask >> ko) & 1u));
   }
-  uint32_t base[kBucket];   // next list position of each key offset (uniform)
-  uint32_t run = off[(long long)sl * (nB + 1) + j];
+  // first list position of each key offset for this wave: the bucket's offset, the edges of
+  // the lower key offsets (all waves), then those of the earlier waves at the same offset
+  uint32_t mine = 0;
 #pragma unroll
-  for (int ko = 0; ko < kBucket; ++ko) {
-    base[ko] = run;
-    run += cnt[ko];
+  for (int ko = 0; ko < kBucket; ++ko) mine = lane == ko ? cnt[ko] : mine;
+  if (lane < kBucket) wcnt[wv][lane] = mine;
+  __syncthreads();
+  uint32_t tk = 0, before = 0;
+  if (lane < kBucket) {
+#pragma unroll
+    for (int w = 0; w < kPermWaves; ++w) {
+      const uint32_t c = wcnt[w][lane];
+      tk += c;
+      before += w < wv ? c : 0u;
+    }
   }
-  // second sweep: place the edges
-  for (int g0 = 0; g0 < geo.NG; g0 += 64) {
-    uint32_t mask = 0u, e0 = 0u;
+  uint32_t incl = tk;
+#pragma unroll
+  for (int o = 1; o < kBucket; o <<= 1) {
+    const uint32_t x = (uint32_t)__shfl_up((int)incl, o, 64);
+    if (lane >= o) incl += x;
+  }
+  const uint32_t first = off[(long long)sl * (nB + 1) + j] + incl - tk + before;
+  uint32_t base[kBucket];   // next list position of each key offset (uniform)
+#pragma unroll
+  for (int ko = 0; ko < kBucket; ++ko) base[ko] = (uint32_t)__builtin_amdgcn_readlane((int)first, ko);
+  // second sweep: place the edges; an edge's staging row is the run's first row plus the
+  // number of the run's keys below it
+  for (int g0 = gbeg; g0 < gend; g0 += 64) {
+    uint32_t mask = 0u, e = 0u;
     if (cached) {   // written by this lane in the first sweep: no barrier needed
       if (g0 + lane < geo.NG) {
         const uint2 c = mcache[g0 + lane];
         mask = c.x;
-        e0 = c.y;
+        e = c.y;
       }
     } else {
       uint32_t a;
       mask = run_mask(g0, a);
-      e0 = (uint32_t)(g0 + lane) * kp + a;
+      e = (uint32_t)(g0 + lane) * kp + a;
     }
 #pragma unroll
     for (int ko = 0; ko < kBucket; ++ko) {
-      const bool has = (mask >> ko) & 1u;
-      const uint64_t m = __builtin_amdgcn_ballot_w64(has);
-      const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      const uint32_t pos = base[ko] + below;
+      const uint32_t bit = (mask >> ko) & 1u;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(bit != 0u);
+      const uint32_t pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, base[ko]));
       // a malformed row is dropped rather than written past the slot's list
-      if (has && pos < slot_rows)
-        pm[pos] = ((e0 + (uint32_t)__builtin_popcount(mask & ((1u << ko) - 1u))) << 5) |
-                  (uint32_t)ko;
+      if (bit != 0u && pos < slot_rows) pm[pos] = (e << 5) | (uint32_t)ko;
+      e += bit;
       base[ko] += (uint32_t)__builtin_popcountll(m);
     }
   }
@@ -1150,7 +1187,8 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
     hipLaunchKernelGGL(bucket_offsets, dim3(ch.n), dim3(256), 0, st, tot, off, geo);
     // the first sweep's masks stay in LDS up to 6144 groups (48 KB)
     const int cached = geo.NG <= 6144 ? 1 : 0;
-    hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64), cached ? geo.NG * sizeof(uint2) : 0,
+    hipLaunchKernelGGL(bucket_perm, dim3(ch.n * nB), dim3(64 * kPermWaves),
+                       cached ? geo.NG * sizeof(uint2) : 0,
                        st, rsT, off, idx, ch, perm, geo, cached);
     mark(4 * c + 1);
 #define DSV_BWD16(DD, QQ)                                                                       \
