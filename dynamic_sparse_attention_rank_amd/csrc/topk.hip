@@ -411,11 +411,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
       const int mb = t * TK_TILE + 32 * kw + 4 * hh;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        // keys below the window are not counted (only the count from the top matters)
-        int bin = min(__float2int_rd(acc[e]), TK_W) + 1;
+        // keys below the window land in bin 0, which is never read (only the count from the
+        // top matters); counting them costs no more than masking them out
+        int bin = min(max(__float2int_rd(acc[e]), -1), TK_W) + 1;
         if constexpr (kTail) bin = mb + 8 * (e >> 2) + (e & 3) < S ? bin : 0;
-        if (bin > 0)
-          __hip_atomic_fetch_add(&wrow[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&wrow[bin], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     });
     ss.c0 = 0.0f;
@@ -613,8 +613,24 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
       const int pre_gt = (int)(pre & 0xffffu), pre_eq = (int)(pre >> 16);
       const int lft = max(left, 0);
       const int base = cnt + pre_gt + min(lft, pre_eq);
-      // the lane's selected keys, one at a time (about 10 % of them); eqm is zero in most tiles
+      // the lane's selected keys, one at a time (about 10 % of them)
       const int lr = max(lft - pre_eq, 0);   // equal keys this slice may still take
+      if (lr == 0 || (eqm | peqm) == 0u) {
+        // No equal key is taken before any of the pair's keys above the threshold: the lane's
+        // j-th such key goes to base + j + the partner's keys in the blocks before its own
+        // (blocks up to its own for the upper lane). `pw` holds those partner bits shifted so
+        // that, for either lane, they are the low (e | 3) + 1 bits.
+        const uint32_t pw = hh ? pgtm : (pgtm << 4);
+        uint32_t todo = writes ? gtm : 0u;
+        int p = base;
+        while (todo != 0u) {
+          const int e = __builtin_ctz(todo);
+          todo &= todo - 1u;
+          const int pos = p + __popc(__builtin_amdgcn_ubfe(pw, 0u, (uint32_t)((e | 3) + 1)));
+          if (pos < kh) orow[pos] = mb + e + (e & 12);
+          ++p;
+        }
+      } else {
       uint32_t todo = writes ? (gtm | eqm) : 0u;
       while (todo != 0u) {
         const int e = __builtin_ctz(todo);
@@ -627,6 +643,7 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
         const bool sel = ((gtm >> e) & 1u) || eqb < lr;
         const int pos = base + gtb + min(lr, eqb);
         if (sel && pos < kh) orow[pos] = mb + 8 * i + (e & 3);
+      }
       }
       cnt += (int)(tot & 0xffffu) + min(lft, (int)(tot >> 16));
       left -= (int)(tot >> 16);
