@@ -225,15 +225,13 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
     for (int qb = 0; qb < QB; ++qb) {
       const float nm = -mrun[qb] * c2;
       float p[2][4];
-      float psum = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          p[kb][j] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][j], c2, nm));
-          psum += p[kb][j];
-        }
-      lrun[qb] += psum;
+        for (int j = 0; j < 4; ++j) p[kb][j] = __builtin_amdgcn_exp2f(fmaf(s[kb][qb][j], c2, nm));
+      // pairwise: seven adds in a tree of depth three
+      lrun[qb] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                  ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
       // P^T operand: element e <-> key (e < 4 ? 4lg + e : 16 + 4lg + e - 4), matching vT
       const u32x4 pb = {pack_bf16(p[0][0], p[0][1]), pack_bf16(p[0][2], p[0][3]),
                         pack_bf16(p[1][0], p[1][1]), pack_bf16(p[1][2], p[1][3])};
