@@ -587,12 +587,21 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
       constexpr bool kTail = decltype(tail_tag)::value;
       const int mb = t * TK_TILE + 32 * kw + 4 * hh;
       uint32_t gtm = 0, eqm = 0;   // bit e: element e above / equal
+      uint64_t anyeq = 0;          // lanes with an element equal to the threshold
 #pragma unroll
-      for (int e = 15; e >= 0; --e) {
+      for (int e = 0; e < 16; ++e) {
         bool valid = true;
         if constexpr (kTail) valid = mb + 8 * (e >> 2) + (e & 3) < S;
-        gtm = (gtm << 1) | (uint32_t)(valid & (acc[e] >= f_hi));
-        eqm = (eqm << 1) | (uint32_t)(valid & (acc[e] == f_eq));
+        gtm |= valid && acc[e] >= f_hi ? 1u << e : 0u;
+        anyeq |= __builtin_amdgcn_ballot_w64(valid && acc[e] == f_eq);
+      }
+      if (anyeq != 0) {   // the same in every lane; most tiles have no key at the threshold
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          bool valid = true;
+          if constexpr (kTail) valid = mb + 8 * (e >> 2) + (e & 3) < S;
+          eqm |= valid && acc[e] == f_eq ? 1u << e : 0u;
+        }
       }
       const uint32_t both = gtm | (eqm << 16);
       const uint32_t pboth = (uint32_t)__shfl_xor((int)both, 32, 64);
