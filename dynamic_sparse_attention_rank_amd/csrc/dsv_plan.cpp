@@ -104,8 +104,8 @@ int dsv_default_cost_model(const dsv_problem* p, int with_backward, dsv_cost_mod
   std::vector<int32_t> k1(p ? std::max(p->heads, 1) : 1, one);
   const int st = validate_problem(p, k1.data(), &geo);
   if (st != DSV_OK) return st;
-  const double topk_ns = 1.44e6 / (24.0 * 1024.0 * 65536.0);
-  const double fwd_ns = 6.50e6 / 1.611e8, bwd_ns = 38.2e6 / 1.611e8;
+  const double topk_ns = 1.30e6 / (24.0 * 1024.0 * 65536.0);
+  const double fwd_ns = 6.30e6 / 1.611e8, bwd_ns = 31.3e6 / 1.611e8;
   cm->topk_ns_per_score = topk_ns * (double)geo.r / 32.0;
   cm->attn_ns_per_edge =
       (with_backward ? fwd_ns + bwd_ns : fwd_ns) * (double)geo.G * geo.d / (64.0 * 128.0);
