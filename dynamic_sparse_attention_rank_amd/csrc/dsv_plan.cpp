@@ -90,10 +90,11 @@ int dsv_plan_heads(const int32_t* k_per_head, int32_t heads, int32_t n_parts, do
 }
 
 // Measured on one MI355X at S = 64K (B=1, H=24, d=128, r=32, G=64, k = 10 % of S):
-// top-k 1.44 ms over 24 * 1024 * 65536 scores; forward 6.50 ms and backward 38.2 ms over
-// 1.611e8 edges (kernel trace of one step, all of the backward's kernels). The estimator's work per score scales with r (two bf16 MFMA terms per 16
-// features and a fixed per-score selection cost, taken here as proportional), the
-// attention's per edge with G * d.
+// top-k 1.30 ms over 24 * 1024 * 65536 scores; forward 6.30 ms and backward 31.3 ms over
+// 1.611e8 edges (one step, every slot of the backward in one launch, all of its kernels).
+// The estimator's work per score scales with r (two bf16 MFMA terms per 16 features and a
+// fixed per-score selection cost, taken here as proportional), the attention's per edge
+// with G * d.
 int dsv_default_cost_model(const dsv_problem* p, int with_backward, dsv_cost_model* cm) {
   if (!cm) {
     set_error("cm is NULL");
