@@ -402,10 +402,11 @@ __device__ __forceinline__ RBlk make_rblk(uint32_t ent, float2 st, long long r0,
 
 // The reduce's list walk, pipelined in half blocks: the next block's first half
 // is requested before this block's second half is added, its second half before the following
-// block's first half; entries two blocks ahead, factors one block ahead. Every load is
-// unconditional (positions clamped; after the last block the "next" block rereads its last
-// rows, unused), and the second block's entries go out before the first block's rows, as in
-// the loop: the compiler's waits for each half then leave the later requests in flight.
+// block's first half; entries three blocks ahead, factors two blocks ahead (a factor is a
+// scattered 8-byte read whose address comes from its entry). Every load is unconditional
+// (positions clamped; after the last block the "next" blocks reread the last rows, unused),
+// and the later blocks' entries and factors go out before the first block's rows, as in the
+// loop: the compiler's waits for each half then leave the later requests in flight.
 // A macro over the kernel's lambdas load_half, add_half (passed to a function, the row words
 // would leave registers).
 #define DSV_WALK_BUCKET(PAIR)                                                                 \
@@ -414,14 +415,16 @@ __device__ __forceinline__ RBlk make_rblk(uint32_t ent, float2 st, long long r0,
       return std::min<uint32_t>(ent >> 5, (uint32_t)(nrows - 1));                             \
     };                                                                                        \
     const uint32_t ent0 = pm[std::min<long long>(s0 + lane, s1 - 1)];                         \
-    const float2 st0 = bfac[(eb + row_of(ent0)) >> 4];                                        \
     uint32_t ent1 = pm[std::min<long long>(s0 + 64 + lane, s1 - 1)];                          \
+    const float2 st0 = bfac[(eb + row_of(ent0)) >> 4];                                        \
+    uint32_t ent2 = pm[std::min<long long>(s0 + 128 + lane, s1 - 1)];                         \
+    float2 st1 = bfac[(eb + row_of(ent1)) >> 4];                                              \
     RBlk cur_b = make_rblk(ent0, st0, s0, s1, nrows, PAIR, half);                             \
     load_half(cur_b, 0);                                                                      \
     load_half(cur_b, 1);                                                                      \
     for (long long r0 = s0; r0 < s1; r0 += 64) {                                              \
-      const float2 st1 = bfac[(eb + row_of(ent1)) >> 4];                                      \
-      const uint32_t ent2 = pm[std::min<long long>(r0 + 128 + lane, s1 - 1)];                 \
+      const float2 st2 = bfac[(eb + row_of(ent2)) >> 4];                                      \
+      const uint32_t ent3 = pm[std::min<long long>(r0 + 192 + lane, s1 - 1)];                 \
       add_half(cur_b, 0);                                                                     \
       const RBlk nxt = make_rblk(ent1, st1, r0 + 64, s1, nrows, PAIR, half);                  \
       load_half(nxt, 0);                                                                      \
@@ -429,6 +432,8 @@ __device__ __forceinline__ RBlk make_rblk(uint32_t ent, float2 st, long long r0,
       load_half(nxt, 1);                                                                      \
       cur_b = nxt;                                                                            \
       ent1 = ent2;                                                                            \
+      st1 = st2;                                                                              \
+      ent2 = ent3;                                                                            \
     }                                                                                         \
   }
 
