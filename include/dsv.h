@@ -176,9 +176,11 @@ int dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, cons
  * With P = exp(scale*q.k - LSE), Delta_n = dO_n.O_n, dS = P*(dO.v - Delta):
  *   dQ_n = scale*sum_m dS[n,m] k_m,  dK_m = scale*sum_n dS[n,m] q_n,  dV_m = sum_n P[n,m] dO_n.
  * bf16 path: each (group, selected key) edge writes its partial dV and dK rows to its own
- * staging row in ws, in fp16 scaled by a power of two per (group, 16-key block) chosen from an
- * a-priori bound (relative error <= 2^-11 per entry); a second kernel sums each 32-key
- * bucket's rows in a fixed order. dK/dV are therefore bitwise reproducible from run to run.
+ * staging row in ws, with one scale per (tensor, group, 16-key block) taken from the block's
+ * largest entry m (for dK after the softmax scale): 8-bit codes when d = 128 and m <= 0.125
+ * (absolute error <= m/254 per entry), else fp16 scaled by a power of two (relative error
+ * <= 2^-11 per entry); a second kernel sums each 32-key bucket's rows in a fixed order.
+ * dK/dV are therefore bitwise reproducible from run to run.
  * The stream is used for several launches per call (heads are processed in chunks that fit
  * ws). Unsupported (DSV_ERR_UNSUPPORTED) when NG * k32 >= 2^27 staging rows per head. */
 int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,

@@ -294,11 +294,11 @@ def test_bwd_edge_cases(label, over, ks):
 
 
 def test_bwd_mixed_staging_formats():
-    """d = 128: chunks whose a-priori dV/dK bounds are small are staged in 8 bits, the others
-    in fp16. At k = 2048 and 1400 of 4096 keys about 86% and 58% of the chunks take 8 bits, so
-    one launch holds both kinds (read back from the block factor table of the workspace: sign
-    bit set = 8-bit) and the reduce runs its mixed steps; every output still meets the bf16
-    bar against the oracle."""
+    """d = 128: 16-key blocks whose largest dV (dK: after the softmax scale) entry is at most
+    0.125 are staged in 8 bits, the others in fp16. At k = 1400 of 4096 keys about 95% of
+    head 1's dV blocks take 8 bits, so one launch holds both kinds (read back from the block
+    factor table of the workspace: sign bit set = 8-bit) and the reduce runs its mixed steps;
+    every output still meets the bf16 bar against the oracle."""
     cfg = workload("small", heads=2, frames=4, height=32, width=32, head_dim=128, rank=32)
     say("[bwd] mixed staging formats")
     x = gpu_inputs(cfg, backward=True, k_per_head=[2048, 1400])
