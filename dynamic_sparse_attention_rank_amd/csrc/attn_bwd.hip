@@ -26,10 +26,11 @@
 //     entry); else fp16 times a power of two (relative error <= 2^-11). The rows are written
 //     with whole-line non-temporal stores, one factor per block to a small table that the
 //     reduce reads through L2.
-//     Small pre-passes list, for every 32-key bucket, its edges in (group, position) order;
-//     a reduce kernel then sums each bucket's rows in LDS (one wave per bucket and half, one
-//     row per instruction, no atomics) and writes every dK/dV row exactly once, so dK/dV are
-//     bitwise reproducible. Heads are processed in chunks sized to the caller's workspace.
+//     Small pre-passes list, for every 32-key bucket, its edges ordered by key, then by
+//     group; a reduce kernel then sums each key's rows in registers (one wave per bucket and
+//     tensor, one row per load instruction, no atomics, no LDS) and writes every dK/dV row
+//     exactly once, so dK/dV are bitwise reproducible. Heads are processed in chunks sized to
+//     the caller's workspace.
 // fp32 path: plain fp32 FMA (one lane per query, then one lane per feature for dK/dV); it
 // exists for fp32 inputs and is not tuned.
 #include <math.h>
@@ -56,8 +57,8 @@ __device__ __forceinline__ void decode_unit(const Geom& geo, int unit, int& b, i
 }
 
 
-// 32 keys per dK/dV bucket: the reduce keeps a bucket's rows in LDS (32 x d fp32 per wave),
-// so smaller buckets let more reduce waves share a CU
+// 32 keys per dK/dV bucket: a bucket's key offset fits the 5 low bits of a list entry, and
+// its keys' rows form one list that one reduce wave per tensor walks
 constexpr int kBucketLog2 = 5;
 constexpr int kBucket = 1 << kBucketLog2;
 constexpr int kMaxChunk = 64;    // (b, h) slots per chunk
