@@ -949,12 +949,26 @@ __global__ __launch_bounds__(64) void attn_bwd_bf16(
 }
 
 // fp32 inputs: lane = group member for P/dS/dQ, then lane = feature for dK/dV.
+// fp32 dK/dV: each group's partial sum is rounded to a multiple of 2^-32 and added as a 64-bit
+// integer. Integer sums do not depend on the order of the atomics, so dK/dV repeat bit for bit
+// whatever the scheduling; each contribution is off by at most 2^-33 (sums must stay below
+// 2^31 in magnitude).
+__device__ __forceinline__ unsigned long long to_fixed(float x) {
+  return (unsigned long long)__double2ll_rn((double)x * 4294967296.0);
+}
+__global__ void fixed_to_f32(const unsigned long long* __restrict__ acc, float* __restrict__ out,
+                             long long n) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    out[i] = (float)((double)(long long)acc[i] * (1.0 / 4294967296.0));
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void attn_bwd_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ o, const float* __restrict__ d_o, const float* __restrict__ lse,
     const int32_t* __restrict__ idx, float scale, float* __restrict__ dq,
-    float* __restrict__ dk, float* __restrict__ dv, Geom geo) {
+    unsigned long long* __restrict__ acck, unsigned long long* __restrict__ accv, Geom geo) {
   constexpr int CH = 16;   // keys per chunk
   extern __shared__ float smem[];
   const int G = geo.G;
@@ -1014,8 +1028,8 @@ __global__ __launch_bounds__(64) void attn_bwd_f32(
           av = fmaf(sp[mem * CH + t], sdo[mem * D + c], av);
           ak = fmaf(sds[mem * CH + t], sq[mem * D + c], ak);
         }
-        unsafeAtomicAdd(dv + kr + c, av);
-        unsafeAtomicAdd(dk + kr + c, ak * scale);
+        atomicAdd(accv + kr + c, to_fixed(av));
+        atomicAdd(acck + kr + c, to_fixed(ak * scale));
       }
     }
     __syncthreads();
@@ -1058,7 +1072,8 @@ static long long max_slot_rows(const Geom& geo) {
 }
 
 size_t bwd_workspace_bytes(const Geom& geo) {
-  if (geo.dtype == DSV_FP32) return 0;
+  // fp32 path: the dV and dK fixed-point accumulators, 8 bytes per element each
+  if (geo.dtype == DSV_FP32) return (size_t)geo.B * geo.H * geo.S * geo.d * 2 * sizeof(uint64_t);
   return ws_layout(geo, 1, max_slot_rows(geo)).total;
 }
 
@@ -1141,10 +1156,14 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
     if (events) (void)hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
   };
   if (geo.dtype == DSV_FP32) {
-    const long long n4 = (long long)geo.B * geo.H * geo.S * geo.d / 4;
+    // fixed-point accumulators in the workspace (dK, then dV), zeroed, then converted
+    const long long n = (long long)geo.B * geo.H * geo.S * geo.d;
+    unsigned long long* acck = static_cast<unsigned long long*>(ws);
+    unsigned long long* accv = acck + n;
+    const long long n4 = n * 2 * (long long)sizeof(uint64_t) / 16;   // float4 units of both
     const int fill_blocks = (int)std::min<long long>((n4 + 255) / 256, 4096);
-    hipLaunchKernelGGL(fill_zero, dim3(fill_blocks), dim3(256), 0, st, (float4*)dk, n4);
-    hipLaunchKernelGGL(fill_zero, dim3(fill_blocks), dim3(256), 0, st, (float4*)dv, n4);
+    hipLaunchKernelGGL(fill_zero, dim3(fill_blocks), dim3(256), 0, st, (float4*)ws, n4);
+    const int conv_blocks = (int)std::min<long long>((n + 255) / 256, 4096);
     const dim3 grid(geo.B * geo.H * geo.NG);
     const size_t shm = (size_t)geo.G * (2 * geo.d + 2 * 16) * sizeof(float);
 #define DSV_BWD32(DD)                                                                         \
@@ -1154,7 +1173,9 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);        \
     hipLaunchKernelGGL((attn_bwd_f32<DD>), grid, dim3(64), shm, st, (const float*)q,          \
                        (const float*)k, (const float*)v, (const float*)o, (const float*)d_o,  \
-                       lse, idx, scale, dq, dk, dv, geo);                                     \
+                       lse, idx, scale, dq, acck, accv, geo);                                 \
+    hipLaunchKernelGGL(fixed_to_f32, dim3(conv_blocks), dim3(256), 0, st, acck, dk, n);      \
+    hipLaunchKernelGGL(fixed_to_f32, dim3(conv_blocks), dim3(256), 0, st, accv, dv, n);      \
     return (int)hipGetLastError();                                                            \
   }
     DSV_BWD32(64)

@@ -88,8 +88,8 @@ typedef struct {
  * need none (their ws may be NULL). DSV_OP_BWD on the bf16 path needs the per-edge dV|dK
  * staging rows of one (b,h) head (about NG*k32*(4*d + 4.5) bytes, k32 = max k rounded up
  * to a multiple of 32, plus small per-bucket tables); a
- * larger workspace lets one launch cover several heads. The fp32 path needs none.
- * Returns (size_t)-1 if the problem is invalid. */
+ * larger workspace lets one launch cover several heads. The fp32 path needs 16*B*H*S*d bytes
+ * (fixed-point dV and dK accumulators). Returns (size_t)-1 if the problem is invalid. */
 size_t dsv_workspace_bytes(int op, const dsv_problem* p, const int32_t* k_per_head);
 
 /* Total int32 elements of the packed idx array: B * NG * sum_h k_h (0 if invalid). */
@@ -180,7 +180,9 @@ int dsv_sparse_attn_fwd(const dsv_problem* p, const void* q, const void* k, cons
  * largest entry m (for dK after the softmax scale): 8-bit codes when d = 128 and m <= 0.125
  * (absolute error <= m/254 per entry), else fp16 scaled by a power of two (relative error
  * <= 2^-11 per entry); a second kernel sums each 32-key bucket's rows in a fixed order.
- * dK/dV are therefore bitwise reproducible from run to run.
+ * dK/dV are therefore bitwise reproducible from run to run. fp32 path: each group's partial
+ * dV and dK sums are rounded to multiples of 2^-32 and added as 64-bit integers in ws, then
+ * converted (error <= 2^-33 per group's contribution; reproducible bit for bit; |sums| < 2^31).
  * The stream is used for several launches per call (heads are processed in chunks that fit
  * ws). Unsupported (DSV_ERR_UNSUPPORTED) when NG * k32 >= 2^27 staging rows per head. */
 int dsv_sparse_attn_bwd(const dsv_problem* p, const void* q, const void* k, const void* v,

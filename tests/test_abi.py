@@ -134,7 +134,8 @@ def test_workspace_and_idx_layout_agree_with_oracle():
             + al(e * 64 * 2) + e * 64 * 2)
     assert dsv.workspace_bytes(dsv.DSV_OP_BWD, p, ks) == need
     pf = dsv.problem(2, 3, 4, 8, 8, 64, 16, (2, 2, 4), "fp32")
-    assert dsv.workspace_bytes(dsv.DSV_OP_BWD, pf, ks) == 0
+    # fp32: fixed-point dV and dK accumulators, 8 bytes per element each (S = 4 * 8 * 8)
+    assert dsv.workspace_bytes(dsv.DSV_OP_BWD, pf, ks) == 2 * 3 * 256 * 64 * 2 * 8
     assert dsv.validate(dsv.DSV_OP_BWD, p, ks, [FAKE] * 10, ws_bytes=need) == 0
     assert dsv.STATUS[dsv.validate(dsv.DSV_OP_BWD, p, ks, [FAKE] * 10, ws_bytes=need - 1)] \
         == "DSV_ERR_WORKSPACE"
@@ -175,8 +176,9 @@ def test_bwd_chunks_and_profiled_entry_point_validation():
     assert dsv.STATUS[st] == "DSV_ERR_NULL"
     pf = dsv.problem(1, 2, 4, 16, 16, 64, 16, (2, 2, 4), "fp32")
     kf = (ctypes.c_int32 * 2)(128, 128)
+    need_f = dsv.workspace_bytes(dsv.DSV_OP_BWD, pf, [128, 128])   # fixed-point accumulators
     st = L.dsv_sparse_attn_bwd_profiled(ctypes.byref(pf), *([FAKE] * 7), kf, 0.1, FAKE, FAKE,
-                                        FAKE, None, 0, None, ev, 4)
+                                        FAKE, FAKE, need_f, None, ev, 4)
     assert dsv.STATUS[st] == "DSV_ERR_UNSUPPORTED"
 
 

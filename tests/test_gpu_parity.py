@@ -248,6 +248,20 @@ def test_bwd_tiny_shape_fp32():
     _bwd_check(cfg, x, idx)
 
 
+def test_bwd_fp32_repeatable_bitwise():
+    """fp32 dK/dV are summed as fixed-point integers: the same bits on every run, although
+    the groups' atomics land in whatever order the scheduling gives."""
+    cfg = workload("tiny", heads=2, head_dim=128, rank=32, k_fixed=256)
+    say("[bwd] fp32 repeatable")
+    x = gpu_inputs(cfg, backward=True)
+    idx = run_topk(cfg, x)
+    o, lse = run_fwd(cfg, x, idx)
+    first = [t.clone() for t in run_bwd(cfg, x, idx, o, lse)]
+    for _ in range(3):
+        again = run_bwd(cfg, x, idx, o, lse)
+        assert all(torch.equal(a, b) for a, b in zip(first, again))
+
+
 def test_bwd_small_bf16_all_heads():
     cfg = workload("small")
     say("[bwd] small bf16")
