@@ -23,8 +23,8 @@
 //     compiler wait early. The tile is read after all of the wave's loads have retired.
 //   * Built with MFMA results in VGPRs: the rare rescale multiplies the O accumulators with
 //     VALU ops, and AGPR accumulators would be copied to VGPRs on every chunk.
-// fp32 path: plain fp32 FMA per lane (one lane per query); it exists for fp32 inputs and is
-// not tuned.
+// fp32 path: v_mfma_f32_16x16x4_f32 tiles, one wave per group, keys in chunks of 16 through
+// LDS; it exists for fp32 inputs and is not tuned for speed.
 #include <math.h>
 
 #include "device_common.h"
@@ -265,47 +265,112 @@ __global__ __launch_bounds__(64) void attn_fwd_bf16(const uint16_t* __restrict__
   }
 }
 
-// fp32 inputs: one lane per query, exact online softmax, fp32 FMA.
-template <int D>
+// fp32 inputs: v_mfma_f32_16x16x4_f32 tiles, one wave per group, keys in chunks of 16. The
+// group's Q rows and each chunk's K and V rows sit in LDS (rows padded by one word so that the
+// operand reads of 16 rows spread over the banks). S^T = K Q^T gives a lane 4 keys of one
+// query; the online softmax runs per chunk in the natural-log domain with the scale applied
+// to the scores; P^T goes through an LDS tile [key][query] to become the B operand of
+// O^T += V^T P^T. Exact up to fp32 rounding; kept simple (it serves fp32 inputs).
+template <int D, int QB>
 __global__ __launch_bounds__(64) void attn_fwd_f32(const float* __restrict__ q,
                                                    const float* __restrict__ k,
                                                    const float* __restrict__ v,
                                                    const int32_t* __restrict__ idx, float scale,
                                                    float* __restrict__ o, float* __restrict__ lse,
                                                    Geom geo) {
+  constexpr int G = 16 * QB;
+  constexpr int DP = D + 1;   // LDS row stride of Q, K, V (words)
+  constexpr int GP = G + 1;   // LDS row stride of the P tile
+  constexpr int NDB = D / 16;
+  __shared__ float sq[G * DP];
+  __shared__ float sk[16 * DP];
+  __shared__ float sv[16 * DP];
+  __shared__ float sp[16 * GP];
   const int lane = threadIdx.x;
+  const int lg = lane >> 4;
+  const int li = lane & 15;
   int b, h, g;
   decode_unit(geo, blockIdx.x, b, h, g);
-  if (lane >= geo.G) return;
   const int kh = geo.k[h];
   const long long base = ((long long)b * geo.H + h) * geo.S * D;
   const int32_t* row = idx + geo.row_offset(b, h, g);
   const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
-  const int n = gg.token(g, lane);
-  float qv[D], acc[D];
-#pragma unroll
-  for (int c = 0; c < D; ++c) {
-    qv[c] = q[base + (long long)n * D + c] * scale;
-    acc[c] = 0.f;
+  for (int i = lane; i < G * D; i += 64) {
+    const int r = i / D, c = i - r * D;
+    sq[r * DP + c] = q[base + (long long)gg.token(g, r) * D + c];
   }
-  float m = -INFINITY, l = 0.f;
-  for (int p = 0; p < kh; ++p) {
-    const long long kr = base + (long long)clamp_key(row[p], geo.S) * D;
-    float s = 0.f;
+  floatx4 oacc[QB][NDB];
+  float mrun[QB], lrun[QB];
 #pragma unroll
-    for (int c = 0; c < D; ++c) s = fmaf(qv[c], k[kr + c], s);
-    const float mn = fmaxf(m, s);
-    const float alpha = expf(m - mn);
-    const float e = expf(s - mn);
-    l = l * alpha + e;
+  for (int qb = 0; qb < QB; ++qb) {
+    mrun[qb] = -INFINITY;
+    lrun[qb] = 0.f;
 #pragma unroll
-    for (int c = 0; c < D; ++c) acc[c] = fmaf(e, v[kr + c], acc[c] * alpha);
-    m = mn;
+    for (int f = 0; f < NDB; ++f) oacc[qb][f] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
-  const float inv = 1.0f / l;
+  for (int cb = 0; cb < kh; cb += 16) {
+    // lane li's key (positions past the row end read its last key; their scores are masked)
+    const int key = clamp_key(row[min(cb + li, kh - 1)], geo.S);
+    for (int r = 0; r < 16; ++r) {
+      const long long kr = base + (long long)__shfl(key, r, 64) * D;
+      for (int c = lane; c < D; c += 64) {
+        sk[r * DP + c] = k[kr + c];
+        sv[r * DP + c] = v[kr + c];
+      }
+    }
+    __syncthreads();
 #pragma unroll
-  for (int c = 0; c < D; ++c) o[base + (long long)n * D + c] = acc[c] * inv;
-  lse[((long long)b * geo.H + h) * geo.S + n] = m + logf(l);
+    for (int qb = 0; qb < QB; ++qb) {
+      // S^T: lane holds keys 4lg + j of the chunk for query 16qb + li
+      floatx4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int st = 0; st < D / 4; ++st)
+        s = mfma_f32(sk[li * DP + 4 * st + lg], sq[(16 * qb + li) * DP + 4 * st + lg], s);
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[j] = cb + 4 * lg + j < kh ? s[j] * scale : -INFINITY;
+        tmax = fmaxf(tmax, s[j]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrun[qb], tmax);   // finite: key cb is always in the row
+      const float alpha = expf(mrun[qb] - mnew);   // 0 on the first chunk
+      float psum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = expf(s[j] - mnew);
+        psum += p;
+        sp[(4 * lg + j) * GP + 16 * qb + li] = p;
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      lrun[qb] = fmaf(lrun[qb], alpha, psum);
+      mrun[qb] = mnew;
+#pragma unroll
+      for (int f = 0; f < NDB; ++f) oacc[qb][f] *= alpha;
+    }
+    // O^T += V^T P^T (the P tile is this wave's own LDS writes, read back in order)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int f = 0; f < NDB; ++f)
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          oacc[qb][f] = mfma_f32(sv[(4 * st + lg) * DP + 16 * f + li],
+                                 sp[(4 * st + lg) * GP + 16 * qb + li], oacc[qb][f]);
+    __syncthreads();   // the next chunk's rows overwrite the tiles
+  }
+  // lane: query 16qb + li, features 16f + 4lg + j
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float inv = 1.0f / lrun[qb];
+    const long long n = gg.token(g, 16 * qb + li);
+#pragma unroll
+    for (int f = 0; f < NDB; ++f)
+      *reinterpret_cast<floatx4*>(o + base + n * D + 16 * f + 4 * lg) = oacc[qb][f] * inv;
+    if (lg == 0) lse[((long long)b * geo.H + h) * geo.S + n] = mrun[qb] + logf(lrun[qb]);
+  }
 }
 
 }  // namespace
@@ -316,14 +381,15 @@ int launch_attn_fwd(const Geom& geo, const void* q, const void* k, const void* v
   const dim3 block(64);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (geo.dtype == DSV_FP32) {
-#define DSV_FWD32(DD)                                                                        \
-  if (geo.d == DD) {                                                                         \
-    hipLaunchKernelGGL((attn_fwd_f32<DD>), grid, block, 0, st, (const float*)q,              \
+    const int QB32 = geo.G / 16;
+#define DSV_FWD32(DD, QQ)                                                                    \
+  if (geo.d == DD && QB32 == QQ) {                                                           \
+    hipLaunchKernelGGL((attn_fwd_f32<DD, QQ>), grid, block, 0, st, (const float*)q,          \
                        (const float*)k, (const float*)v, idx, scale, (float*)o, lse, geo);   \
     return (int)hipGetLastError();                                                           \
   }
-    DSV_FWD32(64)
-    DSV_FWD32(128)
+    DSV_FWD32(64, 1) DSV_FWD32(64, 2) DSV_FWD32(64, 3) DSV_FWD32(64, 4)
+    DSV_FWD32(128, 1) DSV_FWD32(128, 2) DSV_FWD32(128, 3) DSV_FWD32(128, 4)
 #undef DSV_FWD32
     return (int)hipErrorInvalidValue;
   }
