@@ -963,20 +963,32 @@ __global__ void fixed_to_f32(const unsigned long long* __restrict__ acc, float* 
     out[i] = (float)((double)(long long)acc[i] * (1.0 / 4294967296.0));
 }
 
-template <int D>
+// fp32 inputs: v_mfma_f32_16x16x4_f32 tiles, one wave per group, keys in chunks of 16. The
+// group's Q and dO rows and each chunk's K and V rows sit in LDS (rows padded by one word);
+// S^T = K Q^T and dP^T = V dO^T give a lane 4 keys of one query, P and dS go to LDS tiles
+// [key][query], and dQ^T += K^T dS^T, dV^T = dO^T P, dK^T = Q^T dS (the last two over the
+// group's queries) come out of more tiles. Each chunk's dV/dK rows are added to the
+// fixed-point accumulators; dQ is written once. Kept simple (it serves fp32 inputs).
+template <int D, int QB>
 __global__ __launch_bounds__(64) void attn_bwd_f32(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ o, const float* __restrict__ d_o, const float* __restrict__ lse,
     const int32_t* __restrict__ idx, float scale, float* __restrict__ dq,
     unsigned long long* __restrict__ acck, unsigned long long* __restrict__ accv, Geom geo) {
-  constexpr int CH = 16;   // keys per chunk
+  constexpr int G = 16 * QB;
+  constexpr int DP = D + 1;   // LDS row stride of Q, dO, K, V (words)
+  constexpr int GP = G + 1;   // LDS row stride of the P and dS tiles
+  constexpr int NDB = D / 16;
   extern __shared__ float smem[];
-  const int G = geo.G;
-  float* sq = smem;                 // [G][D]
-  float* sdo = sq + G * D;          // [G][D]
-  float* sp = sdo + G * D;          // [G][CH]
-  float* sds = sp + G * CH;         // [G][CH]
+  float* const sq = smem;            // [G][DP]
+  float* const sdo = sq + G * DP;    // [G][DP]
+  float* const sk = sdo + G * DP;    // [16][DP]
+  float* const sv = sk + 16 * DP;    // [16][DP]
+  float* const sp = sv + 16 * DP;    // [16][GP]: P[key][query]
+  float* const sds = sp + 16 * GP;   // [16][GP]: dS[key][query]
   const int lane = threadIdx.x;
+  const int lg = lane >> 4;
+  const int li = lane & 15;
   int b, h, g;
   decode_unit(geo, blockIdx.x, b, h, g);
   const int kh = geo.k[h];
@@ -985,58 +997,96 @@ __global__ __launch_bounds__(64) void attn_bwd_f32(
   const int32_t* row = idx + geo.row_offset(b, h, g);
   const GroupGeom gg{geo.Hh, geo.W, geo.gt, geo.gh, geo.gw, geo.nbh, geo.nbw};
   for (int i = lane; i < G * D; i += 64) {
-    const int mem = i / D, c = i - mem * D;
-    const long long n = gg.token(g, mem);
-    sq[i] = q[base + n * D + c];
-    sdo[i] = d_o[base + n * D + c];
+    const int r = i / D, c = i - r * D;
+    const long long n = gg.token(g, r);
+    sq[r * DP + c] = q[base + n * D + c];
+    sdo[r * DP + c] = d_o[base + n * D + c];
   }
   __syncthreads();
-  const bool member = lane < G;
-  const int n = member ? gg.token(g, lane) : 0;
-  float delta = 0.f, l = 0.f;
-  if (member) {
-    for (int c = 0; c < D; ++c) delta = fmaf(sdo[lane * D + c], o[base + (long long)n * D + c], delta);
-    l = lse[bh * geo.S + n];
+  // LSE and Delta = dO . O of the lane's query 16qb + li (features lg, lg + 4, .. summed over
+  // the 4 lanes of the query)
+  float lq[QB], dl[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const long long n = gg.token(g, 16 * qb + li);
+    lq[qb] = lse[bh * geo.S + n];
+    float acc = 0.f;
+    for (int c = lg; c < D; c += 4) acc = fmaf(sdo[(16 * qb + li) * DP + c], o[base + n * D + c], acc);
+    acc += __shfl_xor(acc, 16, 64);
+    acc += __shfl_xor(acc, 32, 64);
+    dl[qb] = acc;
   }
-  float dqa[D];
+  floatx4 dqacc[QB][NDB];
 #pragma unroll
-  for (int c = 0; c < D; ++c) dqa[c] = 0.f;
-  for (int cb = 0; cb < kh; cb += CH) {
-    const int nk = min(CH, kh - cb);
-    if (member) {
-      for (int t = 0; t < nk; ++t) {
-        const long long kr = base + (long long)clamp_key(row[cb + t], geo.S) * D;
-        float s = 0.f, dp = 0.f;
-        for (int c = 0; c < D; ++c) {
-          s = fmaf(sq[lane * D + c], k[kr + c], s);
-          dp = fmaf(sdo[lane * D + c], v[kr + c], dp);
-        }
-        const float p = expf(s * scale - l);
-        const float ds = p * (dp - delta);
-        sp[lane * CH + t] = p;
-        sds[lane * CH + t] = ds;
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int c = 0; c < D; ++c) dqa[c] = fmaf(ds * scale, k[kr + c], dqa[c]);
-      }
-    }
-    __syncthreads();
-    for (int t = 0; t < nk; ++t) {
-      const long long kr = base + (long long)clamp_key(row[cb + t], geo.S) * D;
+    for (int f = 0; f < NDB; ++f) dqacc[qb][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < kh; cb += 16) {
+    // lane li's key (positions past the row end read its last key; their P and dS are 0)
+    const int key = clamp_key(row[min(cb + li, kh - 1)], geo.S);
+    for (int r = 0; r < 16; ++r) {
+      const long long kr = base + (long long)__shfl(key, r, 64) * D;
       for (int c = lane; c < D; c += 64) {
-        float av = 0.f, ak = 0.f;
-        for (int mem = 0; mem < G; ++mem) {
-          av = fmaf(sp[mem * CH + t], sdo[mem * D + c], av);
-          ak = fmaf(sds[mem * CH + t], sq[mem * D + c], ak);
-        }
-        atomicAdd(accv + kr + c, to_fixed(av));
-        atomicAdd(acck + kr + c, to_fixed(ak * scale));
+        sk[r * DP + c] = k[kr + c];
+        sv[r * DP + c] = v[kr + c];
       }
     }
     __syncthreads();
-  }
-  if (member) {
 #pragma unroll
-    for (int c = 0; c < D; ++c) dq[base + (long long)n * D + c] = dqa[c];
+    for (int qb = 0; qb < QB; ++qb) {
+      // S^T and dP^T: lane holds keys 4lg + j of the chunk for query 16qb + li
+      floatx4 s = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int st = 0; st < D / 4; ++st) {
+        s = mfma_f32(sk[li * DP + 4 * st + lg], sq[(16 * qb + li) * DP + 4 * st + lg], s);
+        dp = mfma_f32(sv[li * DP + 4 * st + lg], sdo[(16 * qb + li) * DP + 4 * st + lg], dp);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool ok = cb + 4 * lg + j < kh;
+        const float p = ok ? expf(fmaf(s[j], scale, -lq[qb])) : 0.f;
+        sp[(4 * lg + j) * GP + 16 * qb + li] = p;
+        sds[(4 * lg + j) * GP + 16 * qb + li] = p * (dp[j] - dl[qb]);
+      }
+    }
+    // (the P and dS tiles are this wave's own LDS writes, read back in order)
+    // dQ^T += K^T dS^T: lane holds features 16f + 4lg + j of query 16qb + li
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int f = 0; f < NDB; ++f)
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          dqacc[qb][f] = mfma_f32(sk[(4 * st + lg) * DP + 16 * f + li],
+                                  sds[(4 * st + lg) * GP + 16 * qb + li], dqacc[qb][f]);
+    // dV^T = dO^T P and dK^T = Q^T dS over the group's queries: lane holds features
+    // 16f + 4lg + j of chunk key li
+    const bool kvalid = cb + li < kh;
+    const long long kr = base + (long long)key * D;
+#pragma unroll 1
+    for (int f = 0; f < NDB; ++f) {
+      floatx4 tv = {0.f, 0.f, 0.f, 0.f}, tk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < G / 4; ++st) {
+        tv = mfma_f32(sdo[(4 * st + lg) * DP + 16 * f + li], sp[li * GP + 4 * st + lg], tv);
+        tk = mfma_f32(sq[(4 * st + lg) * DP + 16 * f + li], sds[li * GP + 4 * st + lg], tk);
+      }
+      if (kvalid) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          atomicAdd(accv + kr + 16 * f + 4 * lg + j, to_fixed(tv[j]));
+          atomicAdd(acck + kr + 16 * f + 4 * lg + j, to_fixed(tk[j] * scale));
+        }
+      }
+    }
+    __syncthreads();   // the next chunk's rows overwrite the tiles
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const long long n = gg.token(g, 16 * qb + li);
+#pragma unroll
+    for (int f = 0; f < NDB; ++f)
+      *reinterpret_cast<floatx4*>(dq + base + n * D + 16 * f + 4 * lg) = dqacc[qb][f] * scale;
   }
 }
 
@@ -1165,21 +1215,24 @@ int launch_attn_bwd(const Geom& geo, const void* q, const void* k, const void* v
     hipLaunchKernelGGL(fill_zero, dim3(fill_blocks), dim3(256), 0, st, (float4*)ws, n4);
     const int conv_blocks = (int)std::min<long long>((n + 255) / 256, 4096);
     const dim3 grid(geo.B * geo.H * geo.NG);
-    const size_t shm = (size_t)geo.G * (2 * geo.d + 2 * 16) * sizeof(float);
-#define DSV_BWD32(DD)                                                                         \
-  if (geo.d == DD) {                                                                          \
+    const int QB32 = geo.G / 16;
+    // LDS: Q and dO rows, the chunk's K and V rows (rows padded by one word), P and dS tiles
+    const size_t shm =
+        ((size_t)2 * (geo.G + 16) * (geo.d + 1) + (size_t)2 * 16 * (geo.G + 1)) * sizeof(float);
+#define DSV_BWD32(DD, QQ)                                                                     \
+  if (geo.d == DD && QB32 == QQ) {                                                            \
     if (shm > 65536)                                                                          \
-      (void)hipFuncSetAttribute((const void*)attn_bwd_f32<DD>,                                \
+      (void)hipFuncSetAttribute((const void*)attn_bwd_f32<DD, QQ>,                            \
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);        \
-    hipLaunchKernelGGL((attn_bwd_f32<DD>), grid, dim3(64), shm, st, (const float*)q,          \
+    hipLaunchKernelGGL((attn_bwd_f32<DD, QQ>), grid, dim3(64), shm, st, (const float*)q,      \
                        (const float*)k, (const float*)v, (const float*)o, (const float*)d_o,  \
                        lse, idx, scale, dq, acck, accv, geo);                                 \
     hipLaunchKernelGGL(fixed_to_f32, dim3(conv_blocks), dim3(256), 0, st, acck, dk, n);      \
     hipLaunchKernelGGL(fixed_to_f32, dim3(conv_blocks), dim3(256), 0, st, accv, dv, n);      \
     return (int)hipGetLastError();                                                            \
   }
-    DSV_BWD32(64)
-    DSV_BWD32(128)
+    DSV_BWD32(64, 1) DSV_BWD32(64, 2) DSV_BWD32(64, 3) DSV_BWD32(64, 4)
+    DSV_BWD32(128, 1) DSV_BWD32(128, 2) DSV_BWD32(128, 3) DSV_BWD32(128, 4)
 #undef DSV_BWD32
     return (int)hipErrorInvalidValue;
   }

@@ -304,6 +304,18 @@ BWD_CASES = [
     ("bf16-d128-G32", dict(heads=2, frames=4, height=8, width=16, group=(2, 4, 4),
                            head_dim=128, rank=32), [33, 257]),
     ("bf16-d64-G48", dict(heads=1, frames=3, height=8, width=16, group=(3, 4, 4)), [130]),
+    # the remaining (head dim, query blocks) instances of the fp32 MFMA kernel
+    ("fp32-d128-G16", dict(heads=1, frames=4, height=8, width=8, group=(2, 2, 4),
+                           head_dim=128, rank=32, dtype="fp32"), [45]),
+    ("fp32-d128-G32", dict(heads=2, frames=4, height=8, width=8, group=(2, 4, 4),
+                           head_dim=128, rank=32, dtype="fp32"), [100, 31]),
+    ("fp32-d128-G48", dict(heads=1, frames=3, height=8, width=16, group=(3, 4, 4),
+                           head_dim=128, rank=32, dtype="fp32"), [33]),
+    ("fp32-d64-G16", dict(heads=1, frames=4, height=8, width=8, group=(2, 2, 4),
+                          dtype="fp32"), [256]),
+    ("fp32-d64-G48", dict(heads=1, frames=3, height=8, width=16, group=(3, 4, 4),
+                          dtype="fp32"), [200]),
+    ("fp32-d64-G64", dict(heads=1, frames=4, height=8, width=16, dtype="fp32"), [77]),
 ]
 
 
