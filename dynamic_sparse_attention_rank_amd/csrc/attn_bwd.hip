@@ -31,8 +31,9 @@
 //     tensor, one row per load instruction, no atomics, no LDS) and writes every dK/dV row
 //     exactly once, so dK/dV are bitwise reproducible. Heads are processed in chunks sized to
 //     the caller's workspace.
-// fp32 path: plain fp32 FMA (one lane per query, then one lane per feature for dK/dV); it
-// exists for fp32 inputs and is not tuned.
+// fp32 path: v_mfma_f32_16x16x4_f32 tiles, one wave per group, 16-key chunks through LDS;
+// dK/dV are summed as 2^-32 fixed-point 64-bit integers (order-independent, so reproducible
+// bit for bit). It exists for fp32 inputs and is not tuned for speed.
 #include <math.h>
 
 #include <algorithm>
